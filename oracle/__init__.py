@@ -1,0 +1,273 @@
+"""CPU oracle for blockwise FP4 fake quantization -- TEST INFRASTRUCTURE.
+
+Only the tests, the smoke check and the CPU-baseline leg of the benchmark may
+import this package.  The GPU library never does, and this package imports
+nothing from it: the two share no code.
+
+Everything here is numpy on the host.  BF16 tensors are passed as numpy
+uint16 arrays holding the raw BF16 bit patterns.  The arithmetic lives in
+fq_oracle.c (plain scalar C, each step cited there); this module only
+marshals arrays and expresses the transposed-axis variant by its definition:
+quantizing along columns is quantizing the transpose along rows, with codes
+and scales kept in the transposed layout and y transposed back.
+
+Formats (this package's own names):
+  "mx"        MXFP4: 1x32 groups, E8M0 scale
+  "nv_tensor" NVFP4: 1x16 groups, E4M3 scale, FP32 per-tensor outer scale
+  "nv_128"    NVFP4 double block: 1x16 E4M3 inner scale, FP32 scale per 128
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+FORMATS = {"mx": 0, "nv_tensor": 1, "nv_128": 2}
+ROUNDINGS = {"rne": 0, "sr": 1}
+BLOCK = {"mx": 32, "nv_tensor": 16, "nv_128": 16}
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        path = _build.ensure_built()
+        L = ctypes.CDLL(path)
+        u8p = ctypes.POINTER(ctypes.c_uint8)
+        u16p = ctypes.POINTER(ctypes.c_uint16)
+        f32p = ctypes.POINTER(ctypes.c_float)
+        i64 = ctypes.c_int64
+        L.fqo_bf16_to_f32.argtypes = [ctypes.c_uint16]
+        L.fqo_bf16_to_f32.restype = ctypes.c_float
+        L.fqo_f32_to_bf16.argtypes = [ctypes.c_float]
+        L.fqo_f32_to_bf16.restype = ctypes.c_uint16
+        L.fqo_e2m1_decode.argtypes = [ctypes.c_int]
+        L.fqo_e2m1_decode.restype = ctypes.c_double
+        L.fqo_e2m1_rne.argtypes = [ctypes.c_float]
+        L.fqo_e2m1_rne.restype = ctypes.c_int
+        L.fqo_e2m1_sr.argtypes = [ctypes.c_float, ctypes.c_uint16]
+        L.fqo_e2m1_sr.restype = ctypes.c_int
+        L.fqo_e8m0_decode.argtypes = [ctypes.c_uint8]
+        L.fqo_e8m0_decode.restype = ctypes.c_float
+        L.fqo_mx_scale_code.argtypes = [ctypes.c_float]
+        L.fqo_mx_scale_code.restype = ctypes.c_uint8
+        L.fqo_e4m3_decode.argtypes = [ctypes.c_uint8]
+        L.fqo_e4m3_decode.restype = ctypes.c_double
+        L.fqo_e4m3_encode.argtypes = [ctypes.c_float]
+        L.fqo_e4m3_encode.restype = ctypes.c_uint8
+        L.fqo_philox4x32_10.argtypes = [ctypes.POINTER(ctypes.c_uint32),
+                                        ctypes.POINTER(ctypes.c_uint32),
+                                        ctypes.POINTER(ctypes.c_uint32)]
+        L.fqo_philox4x32_10.restype = None
+        L.fqo_r16.argtypes = [ctypes.c_uint64, ctypes.c_uint64]
+        L.fqo_r16.restype = ctypes.c_uint16
+        L.fqo_nv_outer_scale.argtypes = [ctypes.c_float]
+        L.fqo_nv_outer_scale.restype = ctypes.c_float
+        L.fqo_absmax.argtypes = [u16p, i64]
+        L.fqo_absmax.restype = ctypes.c_float
+        L.fqo_quantize_rows.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_uint64,
+                                        u16p, i64, i64, u8p, u8p, f32p, u16p, u8p,
+                                        ctypes.c_int]
+        L.fqo_quantize_rows.restype = ctypes.c_int
+        L.fqo_dequantize_rows.argtypes = [ctypes.c_int, u8p, u8p, f32p, i64, i64,
+                                          u16p, ctypes.c_int]
+        L.fqo_dequantize_rows.restype = ctypes.c_int
+        L.fqo_ste_backward_rows.argtypes = [ctypes.c_int, u16p, u8p, f32p, u16p,
+                                            i64, i64, u16p, ctypes.c_int]
+        L.fqo_ste_backward_rows.restype = ctypes.c_int
+        L.fqo_max_threads.argtypes = []
+        L.fqo_max_threads.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _ptr(a: np.ndarray | None, ctype):
+    if a is None:
+        return None
+    assert a.flags["C_CONTIGUOUS"]
+    return a.ctypes.data_as(ctypes.POINTER(ctype))
+
+
+def default_threads() -> int:
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+# --------------------------------------------------------------------------
+# scalar helpers (exposed for the pins)
+# --------------------------------------------------------------------------
+
+def bf16_to_f32(h: int) -> float:
+    return lib().fqo_bf16_to_f32(h)
+
+
+def f32_to_bf16(f: float) -> int:
+    return lib().fqo_f32_to_bf16(f)
+
+
+def e2m1_decode(code: int) -> float:
+    return lib().fqo_e2m1_decode(code)
+
+
+def e2m1_rne(a: float) -> int:
+    return lib().fqo_e2m1_rne(a)
+
+
+def e2m1_sr(a: float, r: int) -> int:
+    return lib().fqo_e2m1_sr(a, r)
+
+
+def e8m0_decode(code: int) -> float:
+    return lib().fqo_e8m0_decode(code)
+
+
+def mx_scale_code(amax: float) -> int:
+    return lib().fqo_mx_scale_code(amax)
+
+
+def e4m3_decode(code: int) -> float:
+    return lib().fqo_e4m3_decode(code)
+
+
+def e4m3_encode(v: float) -> int:
+    return lib().fqo_e4m3_encode(v)
+
+
+def nv_outer_scale(amax: float) -> float:
+    return lib().fqo_nv_outer_scale(amax)
+
+
+def philox4x32_10(counter, key):
+    c = (ctypes.c_uint32 * 4)(*counter)
+    k = (ctypes.c_uint32 * 2)(*key)
+    o = (ctypes.c_uint32 * 4)()
+    lib().fqo_philox4x32_10(c, k, o)
+    return list(o)
+
+
+def r16(seed: int, n: int) -> int:
+    return lib().fqo_r16(seed, n)
+
+
+# --------------------------------------------------------------------------
+# tensor-level calls
+# --------------------------------------------------------------------------
+
+def _rows_quantize(fmt: str, rounding: str, seed: int, x: np.ndarray,
+                   nthreads: int):
+    R, C = x.shape
+    B = BLOCK[fmt]
+    codes = np.zeros((R, C // 2), np.uint8)
+    scales = np.zeros((R, C // B), np.uint8)
+    if fmt == "nv_tensor":
+        outer = np.zeros((1,), np.float32)
+    elif fmt == "nv_128":
+        outer = np.zeros((R, C // 128), np.float32)
+    else:
+        outer = None
+    y = np.zeros((R, C), np.uint16)
+    clip = np.zeros((R, C), np.uint8)
+    rc = lib().fqo_quantize_rows(FORMATS[fmt], ROUNDINGS[rounding], seed,
+                                 _ptr(x, ctypes.c_uint16), R, C,
+                                 _ptr(codes, ctypes.c_uint8),
+                                 _ptr(scales, ctypes.c_uint8),
+                                 _ptr(outer, ctypes.c_float),
+                                 _ptr(y, ctypes.c_uint16),
+                                 _ptr(clip, ctypes.c_uint8), nthreads)
+    if rc != 0:
+        raise ValueError(f"oracle: shape {x.shape} cannot be blocked for {fmt}")
+    return codes, scales, outer, y, clip
+
+
+def fake_quant(x: np.ndarray, fmt: str, rounding: str = "rne", axis: str = "row",
+               seed: int = 0, nthreads: int | None = None) -> dict:
+    """Quantize and dequantize a [R, C] BF16 tensor (uint16 bit patterns).
+
+    axis="row": 1xB groups along each row.  codes [R, C/2], scales [R, C/B],
+    outer (nv_tensor: [1]; nv_128: [R, C/128]), y [R, C].
+    axis="col": 1xB groups along each column, i.e. the row quantization of
+    x^T.  codes [C, R/2], scales [C, R/B], outer [1] or [C, R/128] (the
+    transposed layout); y [R, C] in the layout of x; the stochastic-rounding
+    index of element (i, j) is j * R + i.
+    Also returns clip (1 where the element was clipped), in the layout of y.
+    """
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    assert x.ndim == 2
+    n = default_threads() if nthreads is None else nthreads
+    src = x if axis == "row" else np.ascontiguousarray(x.T)
+    codes, scales, outer, y, clip = _rows_quantize(fmt, rounding, seed, src, n)
+    if axis == "col":
+        y = np.ascontiguousarray(y.T)
+        clip = np.ascontiguousarray(clip.T)
+    return {"codes": codes, "scales": scales, "outer": outer, "y": y, "clip": clip}
+
+
+def dequantize(codes: np.ndarray, scales: np.ndarray, outer, fmt: str,
+               shape: tuple[int, int], axis: str = "row",
+               nthreads: int | None = None) -> np.ndarray:
+    """Inverse of fake_quant's encode step: y [R, C] for x of shape `shape`."""
+    R, C = shape
+    QR, QC = (R, C) if axis == "row" else (C, R)
+    n = default_threads() if nthreads is None else nthreads
+    y = np.zeros((QR, QC), np.uint16)
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    outer = None if outer is None else np.ascontiguousarray(outer, dtype=np.float32)
+    rc = lib().fqo_dequantize_rows(FORMATS[fmt], _ptr(codes, ctypes.c_uint8),
+                                   _ptr(scales, ctypes.c_uint8),
+                                   _ptr(outer, ctypes.c_float), QR, QC,
+                                   _ptr(y, ctypes.c_uint16), n)
+    if rc != 0:
+        raise ValueError("oracle: bad shape for dequantize")
+    return y if axis == "row" else np.ascontiguousarray(y.T)
+
+
+def ste_backward(x: np.ndarray, scales: np.ndarray, outer, dy: np.ndarray,
+                 fmt: str, axis: str = "row", nthreads: int | None = None) -> np.ndarray:
+    """dx = dy where the forward did not clip x, else +0 (layout of x)."""
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    dy = np.ascontiguousarray(dy, dtype=np.uint16)
+    n = default_threads() if nthreads is None else nthreads
+    if axis == "col":
+        x = np.ascontiguousarray(x.T)
+        dy = np.ascontiguousarray(dy.T)
+    QR, QC = x.shape
+    dx = np.zeros((QR, QC), np.uint16)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    outer = None if outer is None else np.ascontiguousarray(outer, dtype=np.float32)
+    rc = lib().fqo_ste_backward_rows(FORMATS[fmt], _ptr(x, ctypes.c_uint16),
+                                     _ptr(scales, ctypes.c_uint8),
+                                     _ptr(outer, ctypes.c_float),
+                                     _ptr(dy, ctypes.c_uint16), QR, QC,
+                                     _ptr(dx, ctypes.c_uint16), n)
+    if rc != 0:
+        raise ValueError("oracle: bad shape for ste_backward")
+    return dx if axis == "row" else np.ascontiguousarray(dx.T)
+
+
+def bf16_bits_to_f64(a: np.ndarray) -> np.ndarray:
+    """Exact widening of BF16 bit patterns to float64."""
+    a = np.ascontiguousarray(a, dtype=np.uint16)
+    return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def qlinear(x: np.ndarray, w: np.ndarray, fmt_x: str = "nv_tensor",
+            fmt_w: str = "nv_tensor", rounding_x: str = "rne",
+            rounding_w: str = "rne", seed_x: int = 0, seed_w: int = 0,
+            nthreads: int | None = None) -> dict:
+    """QAT linear forward: Y = FQ(X) @ FQ(W).
+
+    X [M, K] is quantized in groups along K (its rows), W [K, N] in groups
+    along K (its columns, the transposed axis).  Y is the float64 product of
+    the two dequantized BF16 tensors (numpy matmul as the contraction step).
+    """
+    fx = fake_quant(x, fmt_x, rounding_x, "row", seed_x, nthreads)
+    fw = fake_quant(w, fmt_w, rounding_w, "col", seed_w, nthreads)
+    Y = bf16_bits_to_f64(fx["y"]) @ bf16_bits_to_f64(fw["y"])
+    return {"xhat": fx["y"], "what": fw["y"], "y": Y}
