@@ -1,0 +1,275 @@
+#!/usr/bin/env python3
+"""Benchmark: blockwise FP4 fake quantization on one MI355X.
+
+One step is one pass of the whole fake-quantization path over one
+16384 x 4096 BF16 activation tensor (N(0,1) with 8 outlier channels x100,
+seed 3) and its upstream gradient (N(0, 1e-3^2), seed 4):
+
+  mx_rne_row      MXFP4 fake quant, round to nearest even, 1x32 row groups
+  nvt_rne_row     NVFP4 (per-tensor FP32 scale) fake quant, RNE, 1x16 rows
+  nv128_rne_row   NVFP4 double block (FP32 scale per 128) fake quant, RNE
+  nv128_sr_row    the same with Philox stochastic rounding (seed 1234)
+  nv128_sr_col    double-block SR fake quant along the transposed axis
+  mx_sr_col       MXFP4 SR fake quant along the transposed axis (seed 1235)
+  ste_nv128       clip-masked straight-through backward
+  dequant_nv128   codes + scales -> BF16
+
+Every op writes all of its outputs (codes, scales, outer scales, BF16).
+`value` is the step's algorithmic bytes (each input read once, each output
+written once) over the step time, in GB/s.  Inputs are resident in HBM; the
+step rotates over three input/output buffer sets (~1.9 GB) so no launch
+finds its operands in the 256 MB Infinity Cache.
+
+The QAT linear forward (X 8192x2880 @ W 2880x5760, both NVFP4 RNE) is timed
+after the step and reported in TFLOP/s under "qlinear".  The CPU oracle is
+timed on a bounded sample (the first rows of the same tensors) for
+"cpu_baseline".
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense BF16 MFMA, TFLOP/s
+METRIC = "FP4 fake-quant GB/s and % of HBM peak (MXFP4/NVFP4, 16384x4096 bf16)"
+ROWS, COLS = 16384, 4096
+NBUF = 3
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def op_bytes(op: str, n: int) -> int:
+    """Algorithmic bytes of one op on n elements (read once + outputs)."""
+    x, y = 2 * n, 2 * n
+    codes = n // 2
+    if op.startswith("mx"):
+        scales, outer = n // 32, 0
+    elif op.startswith("nvt"):
+        scales, outer = n // 16, 4
+    else:
+        scales, outer = n // 16, 4 * (n // 128)
+    if op == "ste_nv128":
+        return x + 2 * n + scales + outer + 2 * n          # x, dy, scales, outer -> dx
+    if op == "dequant_nv128":
+        return codes + scales + outer + y
+    return x + y + codes + scales + outer
+
+
+OPS = ["mx_rne_row", "nvt_rne_row", "nv128_rne_row", "nv128_sr_row", "nv128_sr_col",
+       "mx_sr_col", "ste_nv128", "dequant_nv128"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("fq_device.hpp", "fq_kernels.hip"):
+        with open(os.path.join(ROOT, "fp4_block_quantization_fq_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(op: str):
+    """HBM bytes per launch from committed rocprofv3 counter summaries, if
+    they were taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    if data.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    ent = data.get("ops", {}).get(op)
+    return None if ent is None else ent.get("hbm_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=1024,
+                    help="rows of the workload the CPU oracle is timed on")
+    ap.add_argument("--qlinear-iters", type=int, default=20)
+    ap.add_argument("--only", default="", help="comma-separated subset of ops (profiling)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py: this build measures one GPU only (--gpus 1); the multi-GPU "
+              "sharding of this path is a design note, not a benchmark.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import fp4_block_quantization_fq_amd as fq
+    import workloads as wl
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log("bench: generating inputs")
+    x_bits = wl.nv_activation(ROWS, COLS, seed=3)
+    dy_bits = wl.grad_output(ROWS, COLS, seed=4)
+
+    def to_dev(b):
+        return torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    n = ROWS * COLS
+    xs = [to_dev(x_bits) for _ in range(NBUF)]
+    dys = [to_dev(dy_bits) for _ in range(NBUF)]
+    ys = [torch.empty_like(xs[0]) for _ in range(NBUF)]
+
+    descs = {
+        "mx_rne_row": fq.fq_desc_mxfp4(),
+        "nvt_rne_row": fq.fq_desc_nvfp4(),
+        "nv128_rne_row": fq.fq_desc_nvfp4(outer=fq.FQ_OUTER_BLOCK128),
+        "nv128_sr_row": fq.fq_desc_nvfp4(outer=fq.FQ_OUTER_BLOCK128, rounding=fq.FQ_ROUND_SR,
+                                         seed=1234),
+        "nv128_sr_col": fq.fq_desc_nvfp4(outer=fq.FQ_OUTER_BLOCK128, rounding=fq.FQ_ROUND_SR,
+                                         axis=fq.FQ_AXIS_COL, seed=1234),
+        "mx_sr_col": fq.fq_desc_mxfp4(rounding=fq.FQ_ROUND_SR, axis=fq.FQ_AXIS_COL, seed=1235),
+    }
+    d_nv128 = descs["nv128_rne_row"]
+    outs = {op: [fq.alloc_outputs(d, ROWS, COLS, dev) for _ in range(NBUF)]
+            for op, d in descs.items()}
+    ws = torch.empty((4096,), dtype=torch.uint8, device=dev)
+    dxs = [torch.empty_like(xs[0]) for _ in range(NBUF)]
+    # forward scales for the STE / dequant ops come from the RNE double-block op
+    ops = [o for o in OPS if not args.only or o in args.only.split(",")]
+
+    def run_op(op, i):
+        if op in descs:
+            fq.fq_fake_quant(descs[op], xs[i], y=ys[i], out=outs[op][i], ws=ws)
+        elif op == "ste_nv128":
+            fq.fq_ste_backward(d_nv128, xs[i], outs["nv128_rne_row"][i], dys[i], dx=dxs[i])
+        elif op == "dequant_nv128":
+            fq.fq_dequantize(d_nv128, outs["nv128_rne_row"][i], ROWS, COLS, y=dxs[i])
+
+    # make the forward scales exist before the first STE / dequant
+    for i in range(NBUF):
+        fq.fq_fake_quant(d_nv128, xs[i], y=ys[i], out=outs["nv128_rne_row"][i])
+    torch.cuda.synchronize()
+
+    log(f"bench: warmup {args.warmup} steps")
+    for s in range(args.warmup):
+        for op in ops:
+            run_op(op, s % NBUF)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = {op: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(K)] for op in ops}
+    log(f"bench: timing {K} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(K):
+        i = s % NBUF
+        for op in ops:
+            a, b = ev[op][s]
+            a.record()
+            run_op(op, i)
+            b.record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / K
+
+    kernels = {}
+    step_bytes = 0
+    for op in ops:
+        times = [a.elapsed_time(b) for a, b in ev[op]]
+        avg = float(np.mean(times))
+        by = op_bytes(op, n)
+        step_bytes += by
+        kernels[op] = {"ms": round(avg, 5), "bytes": by,
+                       "GBps": round(by / (avg * 1e-3) / 1e9, 1),
+                       "frac_hbm": round(by / (avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    # dominant single-kernel op: the largest share of the step time
+    single = [o for o in ops if o != "nvt_rne_row"]
+    dom = max(single or ops, key=lambda o: kernels[o]["ms"])
+    achieved = kernels[dom]["GBps"]
+    roofline = {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": load_traffic(dom)}
+
+    # ---------------- QAT linear ----------------
+    qlin = None
+    if not args.only:
+        log("bench: qlinear")
+        M, Kd, N = 8192, 2880, 5760
+        xm, wm = wl.linear_inputs(M, Kd, N)
+        xq, wq = to_dev(xm), to_dev(wm)
+        dxd = fq.fq_desc_nvfp4()
+        dwd = fq.fq_desc_nvfp4(axis=fq.FQ_AXIS_COL)
+        qws = fq.qlinear_workspace(dxd, dwd, M, Kd, N, dev)
+        yq = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        for _ in range(3):
+            fq.fq_qlinear_fwd(dxd, dwd, xq, wq, y=yq, ws=qws)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.qlinear_iters):
+            fq.fq_qlinear_fwd(dxd, dwd, xq, wq, y=yq, ws=qws)
+        e1.record()
+        torch.cuda.synchronize()
+        qms = e0.elapsed_time(e1) / args.qlinear_iters
+        flops = 2.0 * M * Kd * N
+        tf = flops / (qms * 1e-3) / 1e12
+        qlin = {"workload": "X 8192x2880 N(0,1) @ W 2880x5760 N(0,0.02^2), NVFP4 RNE both",
+                "ms": round(qms, 4), "TFLOPs": round(tf, 1),
+                "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": BF16_PEAK_TFLOPS,
+                             "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4)}}
+
+    # ---------------- CPU oracle baseline ----------------
+    cpu = None
+    if not args.no_cpu_baseline and not args.only:
+        import oracle
+        log(f"bench: cpu oracle on {args.cpu_rows} rows")
+        r = args.cpu_rows
+        xs_c = np.ascontiguousarray(x_bits[:r])
+        dy_c = np.ascontiguousarray(dy_bits[:r])
+        nthreads = oracle.default_threads()
+        nc = r * COLS
+        t = time.perf_counter()
+        oracle.fake_quant(xs_c, "mx", "rne")
+        oracle.fake_quant(xs_c, "nv_tensor", "rne")
+        f = oracle.fake_quant(xs_c, "nv_128", "rne")
+        oracle.fake_quant(xs_c, "nv_128", "sr", seed=1234)
+        oracle.fake_quant(xs_c, "nv_128", "sr", "col", seed=1234)
+        oracle.fake_quant(xs_c, "mx", "sr", "col", seed=1235)
+        oracle.ste_backward(xs_c, f["scales"], f["outer"], dy_c, "nv_128")
+        oracle.dequantize(f["codes"], f["scales"], f["outer"], "nv_128", xs_c.shape)
+        dt = time.perf_counter() - t
+        cbytes = sum(op_bytes(o, nc) for o in OPS)
+        cpu = {"value": round(cbytes / dt / 1e9, 4), "unit": "GB/s", "cores": nthreads,
+               "kind": "oracle", "seconds": round(dt, 2),
+               "sample": f"the same 8-op step on the first {r} of {ROWS} rows "
+                         f"({nc} elements per op)"}
+
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": K, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "FP4 fake-quant step over a 16384x4096 bf16 activation "
+                               "(N(0,1), 8 outlier channels x100) and its gradient",
+                   "rows": ROWS, "cols": COLS, "ops": ops, "step_bytes": step_bytes,
+                   "frac_hbm_step": round(value / HBM_PEAK_GBS, 4)},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "kernels": kernels,
+        "qlinear": qlin,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,273 @@
+"""Blockwise FP4 (MXFP4 / NVFP4) fake quantization on AMD MI355X (gfx950).
+
+Thin ctypes binding over libfq.so (C ABI in include/fq.h).  Every function
+here only marshals arguments: shapes, device pointers and the current HIP
+stream go to the library, and all arithmetic runs in its HIP kernels.  PyTorch
+supplies device memory and streams.  There is no fallback: if libfq.so is
+missing or a call fails, an exception is raised.
+
+Tensors: BF16 data is passed as torch.bfloat16 tensors; codes and scales as
+torch.uint8; outer scales as torch.float32.  Layouts are those of fq.h.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfq.so")
+
+FQ_OK, FQ_ERR_NULL, FQ_ERR_DESC, FQ_ERR_SHAPE, FQ_ERR_ALIGN, FQ_ERR_WORKSPACE, FQ_ERR_DEVICE = range(7)
+FQ_SCALE_E8M0, FQ_SCALE_E4M3 = 0, 1
+FQ_OUTER_NONE, FQ_OUTER_TENSOR, FQ_OUTER_BLOCK128 = 0, 1, 2
+FQ_ROUND_RNE, FQ_ROUND_SR = 0, 1
+FQ_AXIS_ROW, FQ_AXIS_COL = 0, 1
+
+# every symbol include/fq.h declares
+EXPORTED = (
+    "fq_desc_mxfp4", "fq_desc_nvfp4", "fq_workspace_size", "fq_quantize",
+    "fq_dequantize", "fq_fake_quant", "fq_ste_backward",
+    "fq_qlinear_workspace_size", "fq_qlinear_fwd", "fq_status_string",
+    "fq_last_error", "fq_version",
+)
+
+
+class FqDesc(ctypes.Structure):
+    _fields_ = [
+        ("block_size", ctypes.c_int32),
+        ("scale_type", ctypes.c_int32),
+        ("outer", ctypes.c_int32),
+        ("rounding", ctypes.c_int32),
+        ("axis", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+        ("seed", ctypes.c_uint64),
+    ]
+
+    def __repr__(self):
+        return (f"FqDesc(block_size={self.block_size}, scale_type={self.scale_type}, "
+                f"outer={self.outer}, rounding={self.rounding}, axis={self.axis}, "
+                f"seed={self.seed})")
+
+
+class FqError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{message} (status {status})")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libfq.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(
+                f"{LIB_PATH} is missing: build it with "
+                "`python -m fp4_block_quantization_fq_amd.build` (or __graft_entry__.build())")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i64, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
+        dp = ctypes.POINTER(FqDesc)
+        L.fq_desc_mxfp4.argtypes = []
+        L.fq_desc_mxfp4.restype = FqDesc
+        L.fq_desc_nvfp4.argtypes = []
+        L.fq_desc_nvfp4.restype = FqDesc
+        L.fq_workspace_size.argtypes = [dp, i64, i64]
+        L.fq_workspace_size.restype = sz
+        L.fq_quantize.argtypes = [dp, vp, i64, i64, vp, vp, vp, vp, sz, vp]
+        L.fq_quantize.restype = ctypes.c_int
+        L.fq_dequantize.argtypes = [dp, vp, vp, vp, i64, i64, vp, vp]
+        L.fq_dequantize.restype = ctypes.c_int
+        L.fq_fake_quant.argtypes = [dp, vp, i64, i64, vp, vp, vp, vp, vp, sz, vp]
+        L.fq_fake_quant.restype = ctypes.c_int
+        L.fq_ste_backward.argtypes = [dp, vp, vp, vp, vp, i64, i64, vp, vp]
+        L.fq_ste_backward.restype = ctypes.c_int
+        L.fq_qlinear_workspace_size.argtypes = [dp, dp, i64, i64, i64]
+        L.fq_qlinear_workspace_size.restype = sz
+        L.fq_qlinear_fwd.argtypes = [dp, dp, vp, vp, i64, i64, i64, vp, vp, sz, vp]
+        L.fq_qlinear_fwd.restype = ctypes.c_int
+        L.fq_status_string.argtypes = [ctypes.c_int]
+        L.fq_status_string.restype = ctypes.c_char_p
+        L.fq_last_error.argtypes = []
+        L.fq_last_error.restype = ctypes.c_char_p
+        L.fq_version.argtypes = []
+        L.fq_version.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != FQ_OK:
+        msg = lib().fq_last_error().decode() or lib().fq_status_string(status).decode()
+        raise FqError(status, msg)
+
+
+# ---------------------------------------------------------------------------
+# descriptors
+# ---------------------------------------------------------------------------
+
+def fq_desc_mxfp4(rounding: int = FQ_ROUND_RNE, axis: int = FQ_AXIS_ROW, seed: int = 0) -> FqDesc:
+    d = lib().fq_desc_mxfp4()
+    d.rounding, d.axis, d.seed = rounding, axis, seed
+    return d
+
+
+def fq_desc_nvfp4(rounding: int = FQ_ROUND_RNE, axis: int = FQ_AXIS_ROW, seed: int = 0,
+                  outer: int = FQ_OUTER_TENSOR) -> FqDesc:
+    d = lib().fq_desc_nvfp4()
+    d.rounding, d.axis, d.seed, d.outer = rounding, axis, seed, outer
+    return d
+
+
+def block_size(desc: FqDesc) -> int:
+    return desc.block_size
+
+
+# ---------------------------------------------------------------------------
+# tensor plumbing
+# ---------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+@dataclass
+class Quantized:
+    codes: "object"
+    scales: "object"
+    outer: "object"
+
+
+def output_shapes(desc: FqDesc, rows: int, cols: int) -> dict:
+    """Shapes of codes, scales and outer for x of shape [rows, cols]."""
+    qr, qc = (rows, cols) if desc.axis == FQ_AXIS_ROW else (cols, rows)
+    B = desc.block_size
+    shapes = {"codes": (qr, qc // 2), "scales": (qr, qc // B)}
+    if desc.outer == FQ_OUTER_TENSOR:
+        shapes["outer"] = (1,)
+    elif desc.outer == FQ_OUTER_BLOCK128:
+        shapes["outer"] = (qr, qc // 128)
+    else:
+        shapes["outer"] = None
+    return shapes
+
+
+def alloc_outputs(desc: FqDesc, rows: int, cols: int, device) -> Quantized:
+    torch = _torch()
+    s = output_shapes(desc, rows, cols)
+    codes = torch.empty(s["codes"], dtype=torch.uint8, device=device)
+    scales = torch.empty(s["scales"], dtype=torch.uint8, device=device)
+    outer = None if s["outer"] is None else torch.empty(s["outer"], dtype=torch.float32, device=device)
+    return Quantized(codes, scales, outer)
+
+
+def workspace(desc: FqDesc, rows: int, cols: int, device):
+    torch = _torch()
+    n = lib().fq_workspace_size(ctypes.byref(desc), rows, cols)
+    return torch.empty((max(n, 16),), dtype=torch.uint8, device=device), n
+
+
+# ---------------------------------------------------------------------------
+# the five operations
+# ---------------------------------------------------------------------------
+
+def fq_quantize(desc: FqDesc, x, out: Quantized | None = None, ws=None, stream=None) -> Quantized:
+    rows, cols = x.shape
+    if out is None:
+        out = alloc_outputs(desc, rows, cols, x.device)
+    if ws is None:
+        ws, nbytes = workspace(desc, rows, cols, x.device)
+    else:
+        nbytes = ws.numel() * ws.element_size()
+    _check(lib().fq_quantize(ctypes.byref(desc), _ptr(x), rows, cols, _ptr(out.codes),
+                             _ptr(out.scales), _ptr(out.outer), _ptr(ws), nbytes,
+                             _stream(stream)))
+    return out
+
+
+def fq_dequantize(desc: FqDesc, q: Quantized, rows: int, cols: int, y=None, stream=None):
+    torch = _torch()
+    if y is None:
+        y = torch.empty((rows, cols), dtype=torch.bfloat16, device=q.codes.device)
+    _check(lib().fq_dequantize(ctypes.byref(desc), _ptr(q.codes), _ptr(q.scales),
+                               _ptr(q.outer), rows, cols, _ptr(y), _stream(stream)))
+    return y
+
+
+def fq_fake_quant(desc: FqDesc, x, y=None, out: Quantized | None = None, ws=None,
+                  stream=None):
+    """y = dequantize(quantize(x)); also fills `out` (codes, scales, outer) if
+    given.  Returns y."""
+    torch = _torch()
+    rows, cols = x.shape
+    if y is None:
+        y = torch.empty_like(x)
+    if ws is None:
+        ws, nbytes = workspace(desc, rows, cols, x.device)
+    else:
+        nbytes = ws.numel() * ws.element_size()
+    codes = scales = outer = None
+    if out is not None:
+        codes, scales, outer = out.codes, out.scales, out.outer
+    _check(lib().fq_fake_quant(ctypes.byref(desc), _ptr(x), rows, cols, _ptr(y), _ptr(codes),
+                               _ptr(scales), _ptr(outer), _ptr(ws), nbytes, _stream(stream)))
+    return y
+
+
+def fq_ste_backward(desc: FqDesc, x, q: Quantized, dy, dx=None, stream=None):
+    torch = _torch()
+    rows, cols = x.shape
+    if dx is None:
+        dx = torch.empty_like(dy)
+    _check(lib().fq_ste_backward(ctypes.byref(desc), _ptr(x), _ptr(q.scales), _ptr(q.outer),
+                                 _ptr(dy), rows, cols, _ptr(dx), _stream(stream)))
+    return dx
+
+
+def qlinear_workspace(desc_x: FqDesc, desc_w: FqDesc, M: int, K: int, N: int, device):
+    torch = _torch()
+    n = lib().fq_qlinear_workspace_size(ctypes.byref(desc_x), ctypes.byref(desc_w), M, K, N)
+    return torch.empty((n,), dtype=torch.uint8, device=device)
+
+
+def qlinear_workspace_views(ws, M: int, K: int, N: int):
+    """(X_hat [M, K], W_hat^T [N, K]) views into a qlinear workspace."""
+    torch = _torch()
+    off = (M * K * 2 + 255) // 256 * 256
+    xhat = ws[: M * K * 2].view(torch.bfloat16).view(M, K)
+    what_t = ws[off: off + N * K * 2].view(torch.bfloat16).view(N, K)
+    return xhat, what_t
+
+
+def fq_qlinear_fwd(desc_x: FqDesc, desc_w: FqDesc, x, w, y=None, ws=None, stream=None):
+    """Y [M, N] = FQ(X) @ FQ(W) (BF16 out, FP32 accumulation)."""
+    torch = _torch()
+    M, K = x.shape
+    K2, N = w.shape
+    if K2 != K:
+        raise ValueError(f"inner dimensions differ: {x.shape} @ {w.shape}")
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    if ws is None:
+        ws = qlinear_workspace(desc_x, desc_w, M, K, N, x.device)
+    _check(lib().fq_qlinear_fwd(ctypes.byref(desc_x), ctypes.byref(desc_w), _ptr(x), _ptr(w),
+                                M, K, N, _ptr(y), _ptr(ws), ws.numel(), _stream(stream)))
+    return y
+
+
+def version() -> str:
+    return lib().fq_version().decode()

@@ -1,0 +1,362 @@
+// fq_api.cpp -- the C ABI of libfq.so (declared in include/fq.h).
+//
+// Every entry point validates its arguments completely before touching the
+// device: a rejected call enqueues nothing and writes nothing.  Accepted calls
+// enqueue kernels on the caller's stream and return; launch failures are
+// reported as FQ_ERR_DEVICE.  No exception crosses the boundary.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+
+#include "fq.h"
+#include "fq_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+fq_status fail(fq_status s, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+fq_status ok()
+{
+    g_err[0] = '\0';
+    return FQ_OK;
+}
+
+constexpr int64_t kMaxElems = int64_t(1) << 34;
+
+struct Fmt {
+    int fmt;   // fqimpl::FMT_*
+    int B;     // block size
+};
+
+fq_status check_desc(const fq_desc *d, Fmt *out, const char *name)
+{
+    if (!d) return fail(FQ_ERR_NULL, "%s is NULL", name);
+    if (d->reserved != 0) return fail(FQ_ERR_DESC, "%s->reserved must be 0", name);
+    if (d->rounding != FQ_ROUND_RNE && d->rounding != FQ_ROUND_SR)
+        return fail(FQ_ERR_DESC, "%s->rounding=%d is not FQ_ROUND_RNE/SR", name, d->rounding);
+    if (d->axis != FQ_AXIS_ROW && d->axis != FQ_AXIS_COL)
+        return fail(FQ_ERR_DESC, "%s->axis=%d is not FQ_AXIS_ROW/COL", name, d->axis);
+    if (d->block_size == 32 && d->scale_type == FQ_SCALE_E8M0 && d->outer == FQ_OUTER_NONE) {
+        *out = {fqimpl::FMT_MX, 32};
+        return FQ_OK;
+    }
+    if (d->block_size == 16 && d->scale_type == FQ_SCALE_E4M3) {
+        if (d->outer == FQ_OUTER_TENSOR) {
+            *out = {fqimpl::FMT_NVT, 16};
+            return FQ_OK;
+        }
+        if (d->outer == FQ_OUTER_BLOCK128) {
+            *out = {fqimpl::FMT_NV128, 16};
+            return FQ_OK;
+        }
+    }
+    return fail(FQ_ERR_DESC,
+                "%s: unsupported format {block_size=%d, scale_type=%d, outer=%d}; valid: "
+                "MXFP4 {32, E8M0, NONE}, NVFP4 {16, E4M3, TENSOR|BLOCK128}",
+                name, d->block_size, d->scale_type, d->outer);
+}
+
+fq_status check_shape(const Fmt &f, int axis, int64_t R, int64_t C)
+{
+    if (R < 1 || C < 1) return fail(FQ_ERR_SHAPE, "rows=%lld cols=%lld must be >= 1",
+                                    (long long)R, (long long)C);
+    if (R > kMaxElems || C > kMaxElems || R * C > kMaxElems)
+        return fail(FQ_ERR_SHAPE, "rows*cols=%lld*%lld exceeds 2^34 elements", (long long)R,
+                    (long long)C);
+    const int64_t q = (axis == FQ_AXIS_ROW) ? C : R;    // quantized axis length
+    const char *qn = (axis == FQ_AXIS_ROW) ? "cols" : "rows";
+    if (q % f.B != 0)
+        return fail(FQ_ERR_SHAPE, "%s=%lld must be a multiple of the block size %d", qn,
+                    (long long)q, f.B);
+    if (f.fmt == fqimpl::FMT_NV128 && q % 128 != 0)
+        return fail(FQ_ERR_SHAPE, "%s=%lld must be a multiple of the 128-element outer block",
+                    qn, (long long)q);
+    if (axis == FQ_AXIS_COL && C % 8 != 0)
+        return fail(FQ_ERR_SHAPE, "cols=%lld must be a multiple of 8 for FQ_AXIS_COL",
+                    (long long)C);
+    return FQ_OK;
+}
+
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+fq_status check_ptr(const void *p, const char *name, bool required, uintptr_t align = 16)
+{
+    if (!p) {
+        if (required) return fail(FQ_ERR_NULL, "%s is NULL", name);
+        return FQ_OK;
+    }
+    if (!aligned(p, align))
+        return fail(FQ_ERR_ALIGN, "%s=%p is not %u-byte aligned", name, p, (unsigned)align);
+    return FQ_OK;
+}
+
+size_t quant_ws(const Fmt &f)
+{
+    return f.fmt == fqimpl::FMT_NVT ? fqimpl::kAbsmaxPartials * sizeof(uint32_t) : 0;
+}
+
+fq_status device_status(hipError_t e, const char *what)
+{
+    if (e != hipSuccess)
+        return fail(FQ_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+#define FQ_TRY(expr)                       \
+    do {                                   \
+        fq_status _s = (expr);             \
+        if (_s != FQ_OK) return _s;        \
+    } while (0)
+
+// Shared body of fq_quantize / fq_fake_quant once arguments are checked.
+fq_status run_quant(const Fmt &f, const fq_desc *d, const void *x, int64_t R, int64_t C,
+                    void *y, void *codes, void *scales, float *outer, void *ws,
+                    hipStream_t st)
+{
+    fqimpl::QuantArgs a;
+    a.fmt = f.fmt;
+    a.sr = d->rounding == FQ_ROUND_SR;
+    a.col = d->axis == FQ_AXIS_COL;
+    a.seed = d->seed;
+    a.x = x;
+    a.R = R;
+    a.C = C;
+    a.y = y;
+    a.codes = codes;
+    a.scales = scales;
+    a.outer = (f.fmt == fqimpl::FMT_MX) ? nullptr : outer;
+    a.yt = nullptr;
+    a.partials = (uint32_t *)ws;
+    uint32_t npart = 0;
+    if (f.fmt == fqimpl::FMT_NVT) {
+        hipError_t e = fqimpl::launch_absmax(x, R * C, a.partials, &npart, st);
+        if (e != hipSuccess) return device_status(e, "tensor absmax launch");
+    }
+    return device_status(fqimpl::launch_quant(a, npart, st), "quantize launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+fq_desc fq_desc_mxfp4(void)
+{
+    fq_desc d;
+    std::memset(&d, 0, sizeof(d));
+    d.block_size = 32;
+    d.scale_type = FQ_SCALE_E8M0;
+    d.outer = FQ_OUTER_NONE;
+    d.rounding = FQ_ROUND_RNE;
+    d.axis = FQ_AXIS_ROW;
+    return d;
+}
+
+fq_desc fq_desc_nvfp4(void)
+{
+    fq_desc d;
+    std::memset(&d, 0, sizeof(d));
+    d.block_size = 16;
+    d.scale_type = FQ_SCALE_E4M3;
+    d.outer = FQ_OUTER_TENSOR;
+    d.rounding = FQ_ROUND_RNE;
+    d.axis = FQ_AXIS_ROW;
+    return d;
+}
+
+size_t fq_workspace_size(const fq_desc *desc, int64_t rows, int64_t cols)
+{
+    (void)rows;
+    (void)cols;
+    Fmt f;
+    if (check_desc(desc, &f, "desc") != FQ_OK) return 0;
+    return quant_ws(f);
+}
+
+fq_status fq_quantize(const fq_desc *desc, const void *x_bf16, int64_t rows, int64_t cols,
+                      void *codes, void *scales, float *outer, void *ws, size_t ws_bytes,
+                      void *stream)
+{
+    Fmt f;
+    FQ_TRY(check_desc(desc, &f, "desc"));
+    FQ_TRY(check_shape(f, desc->axis, rows, cols));
+    FQ_TRY(check_ptr(x_bf16, "x", true));
+    FQ_TRY(check_ptr(codes, "codes", true));
+    FQ_TRY(check_ptr(scales, "scales", true));
+    if (f.fmt != fqimpl::FMT_MX) FQ_TRY(check_ptr(outer, "outer", true, 4));
+    const size_t need = quant_ws(f);
+    if (need) {
+        FQ_TRY(check_ptr(ws, "ws", true));
+        if (ws_bytes < need)
+            return fail(FQ_ERR_WORKSPACE, "workspace %zu bytes < %zu required", ws_bytes, need);
+    }
+    return run_quant(f, desc, x_bf16, rows, cols, nullptr, codes, scales, outer, ws,
+                     (hipStream_t)stream);
+}
+
+fq_status fq_dequantize(const fq_desc *desc, const void *codes, const void *scales,
+                        const float *outer, int64_t rows, int64_t cols, void *y_bf16,
+                        void *stream)
+{
+    Fmt f;
+    FQ_TRY(check_desc(desc, &f, "desc"));
+    FQ_TRY(check_shape(f, desc->axis, rows, cols));
+    FQ_TRY(check_ptr(codes, "codes", true));
+    FQ_TRY(check_ptr(scales, "scales", true));
+    if (f.fmt != fqimpl::FMT_MX) FQ_TRY(check_ptr(outer, "outer", true, 4));
+    FQ_TRY(check_ptr(y_bf16, "y", true));
+    return device_status(
+        fqimpl::launch_dequant(f.fmt, desc->axis == FQ_AXIS_COL, codes, scales,
+                               f.fmt == fqimpl::FMT_MX ? nullptr : outer, rows, cols, y_bf16,
+                               (hipStream_t)stream),
+        "dequantize launch");
+}
+
+fq_status fq_fake_quant(const fq_desc *desc, const void *x_bf16, int64_t rows, int64_t cols,
+                        void *y_bf16, void *codes, void *scales, float *outer, void *ws,
+                        size_t ws_bytes, void *stream)
+{
+    Fmt f;
+    FQ_TRY(check_desc(desc, &f, "desc"));
+    FQ_TRY(check_shape(f, desc->axis, rows, cols));
+    FQ_TRY(check_ptr(x_bf16, "x", true));
+    FQ_TRY(check_ptr(y_bf16, "y", true));
+    FQ_TRY(check_ptr(codes, "codes", false));
+    FQ_TRY(check_ptr(scales, "scales", false));
+    FQ_TRY(check_ptr(outer, "outer", false, 4));
+    const size_t need = quant_ws(f);
+    if (need) {
+        FQ_TRY(check_ptr(ws, "ws", true));
+        if (ws_bytes < need)
+            return fail(FQ_ERR_WORKSPACE, "workspace %zu bytes < %zu required", ws_bytes, need);
+    }
+    return run_quant(f, desc, x_bf16, rows, cols, y_bf16, codes, scales, outer, ws,
+                     (hipStream_t)stream);
+}
+
+fq_status fq_ste_backward(const fq_desc *desc, const void *x_bf16, const void *scales,
+                          const float *outer, const void *dy_bf16, int64_t rows,
+                          int64_t cols, void *dx_bf16, void *stream)
+{
+    Fmt f;
+    FQ_TRY(check_desc(desc, &f, "desc"));
+    FQ_TRY(check_shape(f, desc->axis, rows, cols));
+    FQ_TRY(check_ptr(x_bf16, "x", true));
+    FQ_TRY(check_ptr(scales, "scales", true));
+    if (f.fmt != fqimpl::FMT_MX) FQ_TRY(check_ptr(outer, "outer", true, 4));
+    FQ_TRY(check_ptr(dy_bf16, "dy", true));
+    FQ_TRY(check_ptr(dx_bf16, "dx", true));
+    return device_status(
+        fqimpl::launch_ste(f.fmt, desc->axis == FQ_AXIS_COL, x_bf16, scales,
+                           f.fmt == fqimpl::FMT_MX ? nullptr : outer, dy_bf16, rows, cols,
+                           dx_bf16, (hipStream_t)stream),
+        "ste launch");
+}
+
+// qlinear workspace: X_hat [M, K], W_hat^T [N, K] (BF16), reduction scratch.
+static size_t round256(size_t v) { return (v + 255) & ~size_t(255); }
+
+size_t fq_qlinear_workspace_size(const fq_desc *desc_x, const fq_desc *desc_w, int64_t M,
+                                 int64_t K, int64_t N)
+{
+    (void)desc_x;
+    (void)desc_w;
+    if (M < 1 || K < 1 || N < 1) return 0;
+    return round256((size_t)M * K * 2) + round256((size_t)N * K * 2) +
+           2 * fqimpl::kAbsmaxPartials * sizeof(uint32_t);
+}
+
+fq_status fq_qlinear_fwd(const fq_desc *desc_x, const fq_desc *desc_w, const void *x_bf16,
+                         const void *w_bf16, int64_t M, int64_t K, int64_t N, void *y_bf16,
+                         void *ws, size_t ws_bytes, void *stream)
+{
+    Fmt fx, fw;
+    FQ_TRY(check_desc(desc_x, &fx, "desc_x"));
+    FQ_TRY(check_desc(desc_w, &fw, "desc_w"));
+    if (desc_x->axis != FQ_AXIS_ROW)
+        return fail(FQ_ERR_DESC, "desc_x->axis must be FQ_AXIS_ROW (groups along K)");
+    if (desc_w->axis != FQ_AXIS_COL)
+        return fail(FQ_ERR_DESC, "desc_w->axis must be FQ_AXIS_COL (groups along K)");
+    if (M < 1 || K < 1 || N < 1)
+        return fail(FQ_ERR_SHAPE, "M=%lld K=%lld N=%lld must be >= 1", (long long)M,
+                    (long long)K, (long long)N);
+    FQ_TRY(check_shape(fx, FQ_AXIS_ROW, M, K));
+    FQ_TRY(check_shape(fw, FQ_AXIS_COL, K, N));
+    if (K % 64 != 0)
+        return fail(FQ_ERR_SHAPE, "K=%lld must be a multiple of 64", (long long)K);
+    if (M * N > kMaxElems)
+        return fail(FQ_ERR_SHAPE, "M*N exceeds 2^34 elements");
+    FQ_TRY(check_ptr(x_bf16, "x", true));
+    FQ_TRY(check_ptr(w_bf16, "w", true));
+    FQ_TRY(check_ptr(y_bf16, "y", true));
+    FQ_TRY(check_ptr(ws, "ws", true));
+    const size_t need = fq_qlinear_workspace_size(desc_x, desc_w, M, K, N);
+    if (ws_bytes < need)
+        return fail(FQ_ERR_WORKSPACE, "workspace %zu bytes < %zu required", ws_bytes, need);
+
+    char *base = (char *)ws;
+    void *xhat = base;
+    char *what_t = base + round256((size_t)M * K * 2);
+    uint32_t *parts = (uint32_t *)(what_t + round256((size_t)N * K * 2));
+    hipStream_t st = (hipStream_t)stream;
+
+    // X_hat = FQ(X) along K (rows of X)
+    FQ_TRY(run_quant(fx, desc_x, x_bf16, M, K, xhat, nullptr, nullptr, nullptr, parts, st));
+    // W_hat^T: FQ(W) along K (columns of W), written transposed [N, K]
+    {
+        fqimpl::QuantArgs a;
+        a.fmt = fw.fmt;
+        a.sr = desc_w->rounding == FQ_ROUND_SR;
+        a.col = 1;
+        a.seed = desc_w->seed;
+        a.x = w_bf16;
+        a.R = K;
+        a.C = N;
+        a.y = nullptr;
+        a.codes = nullptr;
+        a.scales = nullptr;
+        a.outer = nullptr;
+        a.partials = parts + fqimpl::kAbsmaxPartials;
+        uint32_t npart = 0;
+        if (fw.fmt == fqimpl::FMT_NVT) {
+            hipError_t e = fqimpl::launch_absmax(w_bf16, K * N, a.partials, &npart, st);
+            if (e != hipSuccess) return device_status(e, "tensor absmax launch");
+        }
+        a.yt = what_t;
+        hipError_t e = fqimpl::launch_quant(a, npart, st);
+        if (e != hipSuccess) return device_status(e, "transposed quantize launch");
+    }
+    return device_status(fqimpl::launch_gemm_bf16_nt(xhat, what_t, y_bf16, M, N, K, st),
+                         "gemm launch");
+}
+
+const char *fq_status_string(fq_status s)
+{
+    switch (s) {
+    case FQ_OK: return "FQ_OK";
+    case FQ_ERR_NULL: return "FQ_ERR_NULL: a required pointer is NULL";
+    case FQ_ERR_DESC: return "FQ_ERR_DESC: unsupported descriptor";
+    case FQ_ERR_SHAPE: return "FQ_ERR_SHAPE: unsupported shape";
+    case FQ_ERR_ALIGN: return "FQ_ERR_ALIGN: misaligned pointer";
+    case FQ_ERR_WORKSPACE: return "FQ_ERR_WORKSPACE: workspace too small";
+    case FQ_ERR_DEVICE: return "FQ_ERR_DEVICE: HIP launch failed";
+    }
+    return "unknown fq_status";
+}
+
+const char *fq_last_error(void) { return g_err; }
+
+const char *fq_version(void) { return "0.1.0"; }
+
+}  // extern "C"

@@ -1,0 +1,44 @@
+// fq_internal.h -- launchers shared between the C-ABI layer and the kernels.
+// Arguments are validated by the caller (fq_api.cpp); launchers only map the
+// problem onto a grid and enqueue on `stream`.  Each returns hipSuccess or
+// the launch error.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fqimpl {
+
+enum { FMT_MX = 0, FMT_NVT = 1, FMT_NV128 = 2 };
+
+// Number of partial maxima the per-tensor reduction writes (4 bytes each).
+constexpr uint32_t kAbsmaxPartials = 1024;
+
+struct QuantArgs {
+    int fmt;              // FMT_*
+    int sr;               // 0 = round to nearest even, 1 = stochastic
+    int col;              // 0 = groups along rows of x, 1 = along columns
+    uint64_t seed;
+    const void *x;        // BF16 [R, C]
+    int64_t R, C;
+    void *y;              // BF16 [R, C] or null
+    void *yt;             // column axis only: BF16 [C, R] (y transposed) or null
+    void *codes;          // or null
+    void *scales;         // or null
+    float *outer;         // or null
+    uint32_t *partials;   // kAbsmaxPartials words (NV per-tensor only)
+};
+
+hipError_t launch_absmax(const void *x, int64_t n_elems, uint32_t *partials,
+                         uint32_t *npart_out, hipStream_t stream);
+hipError_t launch_quant(const QuantArgs &a, uint32_t npart, hipStream_t stream);
+hipError_t launch_dequant(int fmt, int col, const void *codes, const void *scales,
+                          const float *outer, int64_t R, int64_t C, void *y,
+                          hipStream_t stream);
+hipError_t launch_ste(int fmt, int col, const void *x, const void *scales,
+                      const float *outer, const void *dy, int64_t R, int64_t C,
+                      void *dx, hipStream_t stream);
+hipError_t launch_gemm_bf16_nt(const void *a, const void *bt, void *c, int64_t M,
+                               int64_t N, int64_t K, hipStream_t stream);
+
+}  // namespace fqimpl

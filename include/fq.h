@@ -1,0 +1,198 @@
+/*
+ * fq.h -- blockwise FP4 fake quantization on AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libfq.so.  Every call validates its arguments on the host, then
+ * enqueues hand-written HIP kernels on the caller's stream and returns.  The
+ * library allocates no device memory and keeps no state between calls other
+ * than a thread-local error message; scratch memory comes from the caller's
+ * workspace argument.
+ *
+ * Sources for the operations (cited by page title and section):
+ *  - "Como o Treinamento com Quantizacao Detecta e Recupera Precisao em
+ *    Inferencia de Baixa Precisao" (brainai.pro), "Detalhes tecnicos ou
+ *    Implementacao": QAT fake-quantizes weights and activations in the
+ *    forward pass (quantize then dequantize inside a wider type) and passes
+ *    gradients through the quantizer with the straight-through estimator,
+ *    exposing rounding and clipping effects.
+ *  - "Aprimorando gpt-oss para Precisao e Desempenho com Treinamento
+ *    Consciente a Quantizacao" (brainai.pro), "O que ha de novo", and the
+ *    gpt-oss QAT tutorial (thakicloud), "NVFP4: The Next Generation": MXFP4
+ *    and NVFP4 targets, NVFP4's FP8 E4M3 block scale, switching between the
+ *    two formats as a one-line configuration change.
+ *  - "Resumo Tecnico: TetraJet-v2" (gist.science), sec. 2.A: NVFP4 groups of
+ *    16 elements with an 8-bit scale; a 128-element outer block with its own
+ *    scale over 16-element inner blocks instead of a tensor-wide maximum;
+ *    stochastic rounding with E[round(x)] = x in the backward pass; 1x16
+ *    weight groups with the transposed weight aligned accordingly; linear
+ *    layers whose activations and weights are all quantized.
+ *  - Format definitions: OCP Microscaling Formats (MX) v1.0 (FP4 E2M1
+ *    element, E8M0 scale 2^(floor(log2 amax) - 2)); OCP OFP8 v1.0 (E4M3,
+ *    bias 7, max 448, no infinities).  Philox4x32-10: Salmon et al., "Parallel
+ *    Random Numbers: As Easy as 1, 2, 3", SC'11.
+ *
+ * Numerics (identical, bit for bit, on every call):
+ *  - E2M1 codes: bit 3 sign, magnitudes {0, .5, 1, 1.5, 2, 3, 4, 6}; the sign
+ *    of x is kept, so a negative value that rounds to zero is code 8 and
+ *    dequantizes to -0.0.
+ *  - MXFP4 block scale: E8M0 code clamp(floor(log2 amax) - 2, -127, 127) + 127
+ *    (an all-zero block gets code 0).
+ *  - NVFP4 outer scale s = RN(amax_outer / 2688) in FP32 (2688 = 6 * 448),
+ *    amax_outer over the whole tensor (FQ_OUTER_TENSOR) or over each
+ *    128-element outer block (FQ_OUTER_BLOCK128).  Block scale code
+ *    e4 = E4M3_RNE_sat(RN(RN(amax_b / 6) / s)) (0 if s = 0); effective scale
+ *    s_eff = RN(e4m3(e4) * s).
+ *  - Scaled magnitude a = RN(|x| / s_eff), correctly rounded FP32 (0 when
+ *    s_eff = 0).
+ *  - FQ_ROUND_RNE: a rounds to the nearest grid value, ties to the even
+ *    code, saturating at 6.  FQ_ROUND_SR: a >= 6 gives 6; otherwise with
+ *    g_k <= a < g_{k+1}, T = floor((a - g_k) / (g_{k+1} - g_k) * 65536) and
+ *    the element rounds up iff r16(n) < T, where r16(n) is 16-bit half
+ *    (n & 1) of word ((n >> 1) & 3) of Philox4x32-10 with key (seed low word,
+ *    seed high word) and counter (low word of n >> 3, high word of n >> 3,
+ *    0, 0), and n is the element's row-major index in the orientation being
+ *    quantized (r * cols + c for FQ_AXIS_ROW, c * rows + r for FQ_AXIS_COL).
+ *  - Dequantized value y = BF16_RNE(RN(+-g * s_eff)).
+ *  - A value is clipped when a > 6.
+ *
+ * Layouts (all row-major, contiguous):
+ *  - x, y, dy, dx: BF16 [rows, cols].
+ *  - FQ_AXIS_ROW (1xB groups along each row, the contiguous axis):
+ *      codes [rows, cols/2] bytes (element 2j in the low nibble),
+ *      scales [rows, cols/B] bytes, outer: 1 float (TENSOR) or
+ *      [rows, cols/128] floats (BLOCK128).
+ *  - FQ_AXIS_COL (groups of B consecutive rows in each column, i.e. 1xB
+ *    groups along the rows of x^T): codes [cols, rows/2], scales
+ *    [cols, rows/B], outer 1 float or [cols, rows/128] -- the layout of x^T;
+ *    y stays in the layout of x.
+ *
+ * Pointers: x, y, dy, dx, codes and scales are device pointers aligned to
+ * 16 bytes; outer is a device pointer aligned to 4 bytes; descriptors are
+ * host pointers read only during the call.  The caller owns all memory.
+ *
+ * Asynchrony: calls return after enqueueing on `stream` (a hipStream_t, NULL
+ * for the default stream).  Results are ready when the stream reaches them.
+ * A call that returns an error other than FQ_ERR_DEVICE has enqueued nothing
+ * and written nothing.
+ *
+ * Limits: rows, cols >= 1 and rows * cols <= 2^34 elements.
+ */
+#ifndef FQ_H
+#define FQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    FQ_OK = 0,
+    FQ_ERR_NULL = 1,       /* a required pointer is NULL */
+    FQ_ERR_DESC = 2,       /* unsupported descriptor combination */
+    FQ_ERR_SHAPE = 3,      /* sizes out of range or not divisible by the block */
+    FQ_ERR_ALIGN = 4,      /* a pointer is not aligned as documented */
+    FQ_ERR_WORKSPACE = 5,  /* workspace missing or smaller than required */
+    FQ_ERR_DEVICE = 6      /* a HIP launch or query failed */
+} fq_status;
+
+enum { FQ_SCALE_E8M0 = 0, FQ_SCALE_E4M3 = 1 };
+enum { FQ_OUTER_NONE = 0, FQ_OUTER_TENSOR = 1, FQ_OUTER_BLOCK128 = 2 };
+enum { FQ_ROUND_RNE = 0, FQ_ROUND_SR = 1 };
+enum { FQ_AXIS_ROW = 0, FQ_AXIS_COL = 1 };
+
+/* Quantization format and rounding.  Valid combinations:
+ *   MXFP4: {block_size 32, FQ_SCALE_E8M0, FQ_OUTER_NONE}
+ *   NVFP4: {block_size 16, FQ_SCALE_E4M3, FQ_OUTER_TENSOR or FQ_OUTER_BLOCK128}
+ * with any rounding and axis.  seed is read only for FQ_ROUND_SR. */
+typedef struct {
+    int32_t block_size;
+    int32_t scale_type;
+    int32_t outer;
+    int32_t rounding;
+    int32_t axis;
+    int32_t reserved;      /* must be 0 */
+    uint64_t seed;
+} fq_desc;
+
+/* Presets: the one-line switch between the two formats.
+ * fq_desc_mxfp4() = {32, E8M0, NONE, RNE, ROW, 0, seed 0}
+ * fq_desc_nvfp4() = {16, E4M3, TENSOR, RNE, ROW, 0, seed 0} */
+fq_desc fq_desc_mxfp4(void);
+fq_desc fq_desc_nvfp4(void);
+
+/* Bytes of workspace that fq_quantize / fq_fake_quant need for this
+ * descriptor and shape: 4096 for FQ_OUTER_TENSOR (partial maxima of the
+ * per-tensor reduction), 0 otherwise.  Contents need no initialization and
+ * are not meaningful after the call.  Returns 0 for an invalid descriptor. */
+size_t fq_workspace_size(const fq_desc *desc, int64_t rows, int64_t cols);
+
+/* Quantize: x -> codes, scales and (NVFP4) outer scales.
+ * codes, scales must be non-NULL; outer must be non-NULL for NVFP4 and is
+ * ignored for MXFP4.  ws / ws_bytes: see fq_workspace_size (ws may be NULL
+ * when 0 bytes are needed).  Source: the quantize half of fake quantization
+ * ("Como o Treinamento ...", "Detalhes tecnicos"); format per the header. */
+fq_status fq_quantize(const fq_desc *desc, const void *x_bf16, int64_t rows,
+                      int64_t cols, void *codes, void *scales, float *outer,
+                      void *ws, size_t ws_bytes, void *stream);
+
+/* Dequantize: codes, scales, outer -> y [rows, cols] BF16, where rows x cols
+ * is the shape of the original x and desc->axis says which layout codes and
+ * scales are in.  Rounding and seed are ignored. */
+fq_status fq_dequantize(const fq_desc *desc, const void *codes, const void *scales,
+                        const float *outer, int64_t rows, int64_t cols,
+                        void *y_bf16, void *stream);
+
+/* Fake quantization: y = dequantize(quantize(x)) in one pass over x.
+ * y must be non-NULL; codes, scales and outer may each be NULL to skip that
+ * output.  Source: "Como o Treinamento ...", "Detalhes tecnicos" (fake
+ * quantization in the forward pass); TetraJet-v2 sec. 2.A for the double
+ * block and stochastic rounding. */
+fq_status fq_fake_quant(const fq_desc *desc, const void *x_bf16, int64_t rows,
+                        int64_t cols, void *y_bf16, void *codes, void *scales,
+                        float *outer, void *ws, size_t ws_bytes, void *stream);
+
+/* Straight-through estimator with clipping: dx = dy where the forward did
+ * not clip x (a <= 6), else +0.  a is recomputed from x and the forward's
+ * stored scales (and outer scales) in the forward's layout (desc->axis).
+ * Source: "Como o Treinamento ...", "Detalhes tecnicos" (gradients through
+ * the quantizer by STE; clipping effects). */
+fq_status fq_ste_backward(const fq_desc *desc, const void *x_bf16,
+                          const void *scales, const float *outer,
+                          const void *dy_bf16, int64_t rows, int64_t cols,
+                          void *dx_bf16, void *stream);
+
+/* Workspace for fq_qlinear_fwd: the dequantized X_hat [M, K] BF16 at offset
+ * 0, the dequantized and transposed W_hat^T [N, K] BF16 at offset
+ * round_up(M * K * 2, 256), then 8192 bytes of reduction scratch. */
+size_t fq_qlinear_workspace_size(const fq_desc *desc_x, const fq_desc *desc_w,
+                                 int64_t M, int64_t K, int64_t N);
+
+/* QAT linear forward: Y [M, N] BF16 = FQ(X) [M, K] x FQ(W) [K, N] with FP32
+ * accumulation on the matrix cores.  X is quantized in groups along K (its
+ * rows: desc_x->axis must be FQ_AXIS_ROW), W in groups along K (its
+ * columns: desc_w->axis must be FQ_AXIS_COL), so both operands are blocked
+ * along the contraction.  K must be divisible by both block sizes (and by
+ * 128 for FQ_OUTER_BLOCK128); M, N >= 1; M * K and K * N <= 2^34.
+ * Source: gpt-oss QAT tutorial, "NVFP4: The Next Generation"
+ * (weight-activation quantization of the MLP); TetraJet-v2 sec. 2 (NVFP4
+ * activations and weights in every linear layer). */
+fq_status fq_qlinear_fwd(const fq_desc *desc_x, const fq_desc *desc_w,
+                         const void *x_bf16, const void *w_bf16, int64_t M,
+                         int64_t K, int64_t N, void *y_bf16, void *ws,
+                         size_t ws_bytes, void *stream);
+
+/* Static description of a status code. */
+const char *fq_status_string(fq_status s);
+
+/* Message of the last error on the calling thread ("" if none). */
+const char *fq_last_error(void);
+
+/* Library version, e.g. "0.1.0". */
+const char *fq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FQ_H */

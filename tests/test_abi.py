@@ -1,0 +1,135 @@
+"""The C-ABI library loads, exports every symbol include/fq.h declares, and
+rejects bad arguments with the documented status before touching the device.
+
+No call here reaches a kernel launch: every call either returns a constant
+(presets, sizes, strings) or fails validation.  The pointers passed are fake
+but aligned (validation never dereferences them).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import fp4_block_quantization_fq_amd as fq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "fq.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?\w+\s*\**\s*(fq_\w+)\s*\(", src, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(fq.LIB_PATH):
+        pytest.skip("libfq.so not built")
+    return fq.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert len(names) >= 12, names
+    assert sorted(fq.EXPORTED) == names
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_presets_are_the_one_line_switch(L):
+    mx, nv = L.fq_desc_mxfp4(), L.fq_desc_nvfp4()
+    assert (mx.block_size, mx.scale_type, mx.outer, mx.rounding, mx.axis, mx.seed) == (32, 0, 0, 0, 0, 0)
+    assert (nv.block_size, nv.scale_type, nv.outer, nv.rounding, nv.axis, nv.seed) == (16, 1, 1, 0, 0, 0)
+    assert ctypes.sizeof(fq.FqDesc) == 32
+
+
+def test_workspace_sizes(L):
+    mx, nv = fq.fq_desc_mxfp4(), fq.fq_desc_nvfp4()
+    nv128 = fq.fq_desc_nvfp4(outer=fq.FQ_OUTER_BLOCK128)
+    assert L.fq_workspace_size(ctypes.byref(mx), 1024, 4096) == 0
+    assert L.fq_workspace_size(ctypes.byref(nv), 1024, 4096) == 4096
+    assert L.fq_workspace_size(ctypes.byref(nv128), 1024, 4096) == 0
+    bad = fq.fq_desc_mxfp4()
+    bad.block_size = 16
+    assert L.fq_workspace_size(ctypes.byref(bad), 1024, 4096) == 0
+    M, K, N = 8192, 2880, 5760
+    want = (M * K * 2 + 255) // 256 * 256 + (N * K * 2 + 255) // 256 * 256 + 8192
+    assert L.fq_qlinear_workspace_size(ctypes.byref(nv), ctypes.byref(nv), M, K, N) == want
+
+
+P = ctypes.c_void_p
+
+
+def fake(addr=0x10000):
+    return P(addr)
+
+
+def call_quant(L, d, rows=64, cols=64, x=fake(), codes=fake(), scales=fake(), outer=fake(),
+               ws=fake(), ws_bytes=4096):
+    return L.fq_quantize(ctypes.byref(d) if d is not None else None, x, rows, cols, codes,
+                         scales, outer, ws, ws_bytes, None)
+
+
+def test_quantize_validation(L):
+    mx = fq.fq_desc_mxfp4()
+    nv = fq.fq_desc_nvfp4()
+    assert call_quant(L, None) == fq.FQ_ERR_NULL
+    assert call_quant(L, mx, x=None) == fq.FQ_ERR_NULL
+    assert call_quant(L, mx, codes=None) == fq.FQ_ERR_NULL
+    assert call_quant(L, nv, outer=None) == fq.FQ_ERR_NULL
+    assert call_quant(L, nv, ws=None) == fq.FQ_ERR_NULL
+    assert call_quant(L, mx, x=fake(0x10008)) == fq.FQ_ERR_ALIGN
+    assert call_quant(L, nv, outer=fake(0x10002)) == fq.FQ_ERR_ALIGN
+    assert call_quant(L, nv, ws_bytes=4095) == fq.FQ_ERR_WORKSPACE
+    assert call_quant(L, mx, cols=48) == fq.FQ_ERR_SHAPE           # not a multiple of 32
+    assert call_quant(L, mx, rows=0) == fq.FQ_ERR_SHAPE
+    assert call_quant(L, mx, rows=1 << 20, cols=1 << 15) == fq.FQ_ERR_SHAPE   # > 2^34
+    nv128 = fq.fq_desc_nvfp4(outer=fq.FQ_OUTER_BLOCK128)
+    assert call_quant(L, nv128, cols=64) == fq.FQ_ERR_SHAPE        # not a multiple of 128
+    col = fq.fq_desc_nvfp4(axis=fq.FQ_AXIS_COL)
+    assert call_quant(L, col, rows=24, cols=64) == fq.FQ_ERR_SHAPE  # rows not multiple of 16
+    assert call_quant(L, col, rows=32, cols=20) == fq.FQ_ERR_SHAPE  # cols not multiple of 8
+    for field, val in [("block_size", 8), ("scale_type", 1), ("outer", 1), ("rounding", 2),
+                       ("axis", 3), ("reserved", 1)]:
+        d = fq.fq_desc_mxfp4()
+        setattr(d, field, val)
+        assert call_quant(L, d) == fq.FQ_ERR_DESC, field
+    msg = L.fq_last_error().decode()
+    assert "reserved" in msg
+
+
+def test_other_entry_points_validate(L):
+    mx = fq.fq_desc_mxfp4()
+    nv = fq.fq_desc_nvfp4()
+    assert L.fq_dequantize(ctypes.byref(mx), fake(), None, None, 64, 64, fake(), None) == fq.FQ_ERR_NULL
+    assert L.fq_dequantize(ctypes.byref(nv), fake(), fake(), None, 64, 64, fake(), None) == fq.FQ_ERR_NULL
+    assert L.fq_dequantize(ctypes.byref(mx), fake(), fake(), None, 64, 40, fake(), None) == fq.FQ_ERR_SHAPE
+    assert L.fq_fake_quant(ctypes.byref(mx), fake(), 64, 64, None, None, None, None, None, 0,
+                           None) == fq.FQ_ERR_NULL
+    assert L.fq_fake_quant(ctypes.byref(mx), fake(), 64, 64, fake(), fake(0x10001), None, None,
+                           None, 0, None) == fq.FQ_ERR_ALIGN
+    assert L.fq_fake_quant(ctypes.byref(nv), fake(), 64, 64, fake(), None, None, None, None, 0,
+                           None) == fq.FQ_ERR_NULL
+    assert L.fq_ste_backward(ctypes.byref(mx), fake(), fake(), None, None, 64, 64, fake(),
+                             None) == fq.FQ_ERR_NULL
+    assert L.fq_ste_backward(ctypes.byref(nv), fake(), fake(), None, fake(), 64, 64, fake(),
+                             None) == fq.FQ_ERR_NULL
+    # qlinear: axes must put both blocks along K
+    col = fq.fq_desc_nvfp4(axis=fq.FQ_AXIS_COL)
+    ws = 1 << 30
+    assert L.fq_qlinear_fwd(ctypes.byref(nv), ctypes.byref(nv), fake(), fake(), 128, 128, 128,
+                            fake(), fake(), ws, None) == fq.FQ_ERR_DESC
+    assert L.fq_qlinear_fwd(ctypes.byref(col), ctypes.byref(col), fake(), fake(), 128, 128, 128,
+                            fake(), fake(), ws, None) == fq.FQ_ERR_DESC
+    assert L.fq_qlinear_fwd(ctypes.byref(nv), ctypes.byref(col), fake(), fake(), 128, 96, 128,
+                            fake(), fake(), ws, None) == fq.FQ_ERR_SHAPE
+    assert L.fq_qlinear_fwd(ctypes.byref(nv), ctypes.byref(col), fake(), fake(), 128, 128, 128,
+                            fake(), fake(), 1024, None) == fq.FQ_ERR_WORKSPACE
+
+
+def test_status_strings(L):
+    for s in range(7):
+        assert L.fq_status_string(s).decode().startswith("FQ_")
+    assert L.fq_version().decode().count(".") == 2

@@ -1,0 +1,235 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle,
+element by element and bit for bit -- codes, scales, outer scales, BF16
+outputs and STE gradients, for every format, rounding mode and axis, at sizes
+that span several tiles with ragged tails, on edge-case values, and on the
+five seeded workloads at full size."""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import fp4_block_quantization_fq_amd as fq
+import oracle
+import workloads as wl
+from gpu_util import (assert_same, gpu_fake_quant, make_desc, to_bits, to_dev, to_np)
+
+pytestmark = pytest.mark.gpu
+
+FMTS = ["mx", "nv_tensor", "nv_128"]
+
+# (rows, cols) per format and axis: single block, several tiles, ragged tails
+SHAPES = {
+    ("mx", "row"): [(1, 32), (7, 96), (33, 2880), (64, 4096)],
+    ("nv_tensor", "row"): [(1, 16), (5, 48), (64, 2880), (129, 1040)],
+    ("nv_128", "row"): [(1, 128), (3, 384), (50, 2944)],
+    ("mx", "col"): [(32, 8), (96, 72), (512, 264), (1024, 40)],
+    ("nv_tensor", "col"): [(16, 8), (48, 200), (2880, 136), (1040, 64)],
+    ("nv_128", "col"): [(128, 8), (384, 72), (1024, 136)],
+}
+
+
+def cases():
+    for (fmt, axis), shapes in SHAPES.items():
+        for shape in shapes:
+            for rnd in ("rne", "sr"):
+                yield fmt, axis, rnd, shape
+
+
+@pytest.mark.parametrize("fmt,axis,rnd,shape", list(cases()))
+def test_fake_quant_matches_oracle(fmt, axis, rnd, shape):
+    x = wl.normal_bf16(shape, 1.0, seed=zlib.crc32(repr((fmt, axis, rnd, shape)).encode()))
+    seed = 0x1234_5678_9ABC_DEF0
+    ref = oracle.fake_quant(x, fmt, rnd, axis, seed)
+    got = gpu_fake_quant(x, fmt, rnd, axis, seed)
+    assert_same(got, ref, tag=f"{fmt}/{axis}/{rnd}/{shape}")
+
+
+def _edge_tensors(shape):
+    R, C = shape
+    out = {}
+    out["all_exponents"] = wl.uniform_bits_bf16(shape, 31)
+    z = np.zeros(shape, np.uint16)
+    z[::3, ::5] = 0x8000                                   # -0.0 sprinkled
+    out["zeros"] = z
+    sub = wl.uniform_bits_bf16(shape, 32) & np.uint16(0x807F)  # subnormals only
+    out["subnormals"] = sub
+    big = wl.normal_bf16(shape, 1.0, 33)
+    big.reshape(-1)[::97] = 0x7F7F                         # +max BF16
+    big.reshape(-1)[5::97] = 0xFF7F                        # -max BF16
+    out["max_bf16"] = big
+    one = wl.normal_bf16(shape, 1e-3, 34)
+    one.reshape(-1)[R * C // 2 + 3] = 0x4780               # a single 65536 outlier
+    out["single_outlier"] = one
+    tiny_scale = wl.normal_bf16(shape, 1.0, 35)
+    tiny_scale = (tiny_scale & np.uint16(0x807F)) | np.uint16(0x0100)  # ~2^-125 values
+    out["tiny_normals"] = tiny_scale
+    return out
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("axis", ["row", "col"])
+@pytest.mark.parametrize("rnd", ["rne", "sr"])
+def test_edge_values(fmt, axis, rnd):
+    shape = (256, 384)
+    for name, x in _edge_tensors(shape).items():
+        ref = oracle.fake_quant(x, fmt, rnd, axis, seed=77)
+        got = gpu_fake_quant(x, fmt, rnd, axis, seed=77)
+        assert_same(got, ref, tag=f"{name}/{fmt}/{axis}/{rnd}")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_every_bf16_value(fmt):
+    """Every finite BF16 pattern, in random blocks, through RNE and SR."""
+    allv = np.arange(0, 1 << 16, dtype=np.uint32).astype(np.uint16)
+    allv = allv[(allv & 0x7F80) != 0x7F80]
+    rng = np.random.default_rng(5)
+    reps = []
+    for _ in range(4):
+        reps.append(rng.permutation(allv))
+    v = np.concatenate(reps)
+    n = v.size // 1024 * 1024
+    x = v[:n].reshape(-1, 1024)
+    for rnd in ("rne", "sr"):
+        ref = oracle.fake_quant(x, fmt, rnd, "row", seed=9)
+        got = gpu_fake_quant(x, fmt, rnd, "row", seed=9)
+        assert_same(got, ref, tag=f"all-bf16/{fmt}/{rnd}")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("axis", ["row", "col"])
+def test_quantize_and_dequantize(fmt, axis):
+    shape = (384, 256)
+    x = wl.normal_bf16(shape, 0.3, 41)
+    d = make_desc(fmt, "sr", axis, seed=5)
+    xd = to_dev(x)
+    q = fq.fq_quantize(d, xd)
+    y = fq.fq_dequantize(d, q, *shape)
+    torch.cuda.synchronize()
+    ref = oracle.fake_quant(x, fmt, "sr", axis, 5)
+    got = {"codes": to_np(q.codes), "scales": to_np(q.scales),
+           "outer": None if q.outer is None else to_np(q.outer), "y": to_bits(y)}
+    assert_same(got, ref, tag=f"quantize+dequantize/{fmt}/{axis}")
+    # dequantize of oracle codes
+    qo = fq.Quantized(torch.from_numpy(ref["codes"]).to(xd.device),
+                      torch.from_numpy(ref["scales"]).to(xd.device),
+                      None if ref["outer"] is None else torch.from_numpy(ref["outer"]).to(xd.device))
+    y2 = fq.fq_dequantize(d, qo, *shape)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_bits(y2), ref["y"])
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("axis", ["row", "col"])
+def test_ste_backward(fmt, axis):
+    shape = (512, 384)
+    x = wl.activation_with_outlier_channels(shape, 1.0, 4, 100.0, 51)
+    x.reshape(-1)[::13] = wl.uniform_bits_bf16((x.size + 12) // 13, 52)[: x.reshape(-1)[::13].size]
+    dy = wl.normal_bf16(shape, 1e-3, 53)
+    ref_f = oracle.fake_quant(x, fmt, "rne", axis)
+    ref_dx = oracle.ste_backward(x, ref_f["scales"], ref_f["outer"], dy, fmt, axis)
+    assert (ref_dx != dy).any() or not ref_f["clip"].any()
+    d = make_desc(fmt, "rne", axis)
+    xd = to_dev(x)
+    q = fq.fq_quantize(d, xd)
+    dx = fq.fq_ste_backward(d, xd, q, to_dev(dy))
+    torch.cuda.synchronize()
+    assert np.array_equal(to_bits(dx), ref_dx)
+    # clipped elements get +0, the rest pass dy through
+    assert np.array_equal(to_bits(dx) == 0, (ref_f["clip"] == 1) | (dy == 0))
+
+
+def test_repeat_runs_identical():
+    x = wl.normal_bf16((1024, 1024), 1.0, 61)
+    for fmt in FMTS:
+        for axis in ("row", "col"):
+            a = gpu_fake_quant(x, fmt, "sr", axis, seed=3)
+            b = gpu_fake_quant(x, fmt, "sr", axis, seed=3)
+            assert_same(a, b, tag=f"repeat/{fmt}/{axis}")
+
+
+# ---------------------------------------------------------------------------
+# QAT linear
+# ---------------------------------------------------------------------------
+
+def _qlinear_check(M, K, N, fmt_x="nv_tensor", fmt_w="nv_tensor", seeds=(6, 7), tol=1e-2):
+    x = wl.normal_bf16((M, K), 1.0, seeds[0])
+    w = wl.normal_bf16((K, N), 0.02, seeds[1])
+    ref = oracle.qlinear(x, w, fmt_x, fmt_w)
+    dx, dw = make_desc(fmt_x, "rne", "row"), make_desc(fmt_w, "rne", "col")
+    xd, wd = to_dev(x), to_dev(w)
+    ws = fq.qlinear_workspace(dx, dw, M, K, N, xd.device)
+    y = fq.fq_qlinear_fwd(dx, dw, xd, wd, ws=ws)
+    torch.cuda.synchronize()
+    xhat, what_t = fq.qlinear_workspace_views(ws, M, K, N)
+    assert np.array_equal(to_bits(xhat), ref["xhat"])
+    assert np.array_equal(to_bits(what_t), np.ascontiguousarray(ref["what"].T))
+    yg = oracle.bf16_bits_to_f64(to_bits(y))
+    err = np.linalg.norm(yg - ref["y"]) / np.linalg.norm(ref["y"])
+    assert err <= tol, err
+    return err
+
+
+@pytest.mark.parametrize("M,K,N", [(128, 64, 128), (96, 384, 200), (257, 320, 136),
+                                   (1024, 2880, 576)])
+@pytest.mark.parametrize("fmts", [("nv_tensor", "nv_tensor"), ("mx", "mx"),
+                                  ("nv_128", "nv_128")])
+def test_qlinear_small(M, K, N, fmts):
+    if "nv_128" in fmts and K % 128:
+        pytest.skip("K not a multiple of 128")
+    if "mx" in fmts and K % 32:
+        pytest.skip("K not a multiple of 32")
+    err = _qlinear_check(M, K, N, *fmts)
+    # products of BF16 values are exact in FP32: only accumulation order and
+    # the BF16 store remain
+    assert err < 4e-3
+
+
+# ---------------------------------------------------------------------------
+# the five seeded workloads at full size
+# ---------------------------------------------------------------------------
+
+def test_workload_mxfp4_activation_rne():
+    x = wl.mx_activation()
+    assert_same(gpu_fake_quant(x, "mx"), oracle.fake_quant(x, "mx"), tag="mx 1024x4096")
+
+
+def test_workload_nvfp4_weight_rne():
+    x = wl.nv_weight()
+    assert_same(gpu_fake_quant(x, "nv_tensor"), oracle.fake_quant(x, "nv_tensor"),
+                tag="nv 2880x2880")
+
+
+def test_workload_double_block_rne_and_sr():
+    x = wl.nv_activation()
+    assert_same(gpu_fake_quant(x, "nv_128"), oracle.fake_quant(x, "nv_128"),
+                tag="nv128 rne 16384x4096")
+    assert_same(gpu_fake_quant(x, "nv_128", "sr", seed=1234),
+                oracle.fake_quant(x, "nv_128", "sr", seed=1234), tag="nv128 sr 16384x4096")
+
+
+def test_workload_backward():
+    x = wl.nv_activation()
+    dy = wl.grad_output()
+    ref_f = oracle.fake_quant(x, "nv_128")
+    ref_dx = oracle.ste_backward(x, ref_f["scales"], ref_f["outer"], dy, "nv_128")
+    d = make_desc("nv_128")
+    xd = to_dev(x)
+    q = fq.fq_quantize(d, xd)
+    dx = fq.fq_ste_backward(d, xd, q, to_dev(dy))
+    torch.cuda.synchronize()
+    assert np.array_equal(to_bits(dx), ref_dx)
+    w = wl.backward_weight()
+    for fmt, seed in (("nv_tensor", 1234), ("mx", 1235)):
+        ref = oracle.fake_quant(w, fmt, "sr", "col", seed)
+        dd = make_desc(fmt, "sr", "col", seed)
+        q = fq.fq_quantize(dd, to_dev(w))
+        torch.cuda.synchronize()
+        got = {"codes": to_np(q.codes), "scales": to_np(q.scales),
+               "outer": None if q.outer is None else to_np(q.outer)}
+        assert_same(got, ref, keys=("codes", "scales", "outer"), tag=f"{fmt} sr col 4096x4096")
+
+
+def test_workload_qlinear():
+    err = _qlinear_check(8192, 2880, 5760)
+    assert err < 4e-3
