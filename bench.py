@@ -96,7 +96,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=1024,
+    ap.add_argument("--cpu-rows", type=int, default=16384,
                     help="rows of the workload the CPU oracle is timed on")
     ap.add_argument("--qlinear-iters", type=int, default=20)
     ap.add_argument("--only", default="", help="comma-separated subset of ops (profiling)")

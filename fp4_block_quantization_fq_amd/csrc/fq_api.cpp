@@ -123,7 +123,7 @@ fq_status device_status(hipError_t e, const char *what)
 // Shared body of fq_quantize / fq_fake_quant once arguments are checked.
 fq_status run_quant(const Fmt &f, const fq_desc *d, const void *x, int64_t R, int64_t C,
                     void *y, void *codes, void *scales, float *outer, void *ws,
-                    hipStream_t st)
+                    hipStream_t st, bool cached = false)
 {
     fqimpl::QuantArgs a;
     a.fmt = f.fmt;
@@ -139,6 +139,7 @@ fq_status run_quant(const Fmt &f, const fq_desc *d, const void *x, int64_t R, in
     a.outer = (f.fmt == fqimpl::FMT_MX) ? nullptr : outer;
     a.yt = nullptr;
     a.partials = (uint32_t *)ws;
+    a.cached_outputs = cached;
     uint32_t npart = 0;
     if (f.fmt == fqimpl::FMT_NVT) {
         hipError_t e = fqimpl::launch_absmax(x, R * C, a.partials, &npart, st);
@@ -312,7 +313,8 @@ fq_status fq_qlinear_fwd(const fq_desc *desc_x, const fq_desc *desc_w, const voi
     hipStream_t st = (hipStream_t)stream;
 
     // X_hat = FQ(X) along K (rows of X)
-    FQ_TRY(run_quant(fx, desc_x, x_bf16, M, K, xhat, nullptr, nullptr, nullptr, parts, st));
+    FQ_TRY(run_quant(fx, desc_x, x_bf16, M, K, xhat, nullptr, nullptr, nullptr, parts, st,
+                     /*cached=*/true));
     // W_hat^T: FQ(W) along K (columns of W), written transposed [N, K]
     {
         fqimpl::QuantArgs a;
@@ -328,6 +330,7 @@ fq_status fq_qlinear_fwd(const fq_desc *desc_x, const fq_desc *desc_w, const voi
         a.scales = nullptr;
         a.outer = nullptr;
         a.partials = parts + fqimpl::kAbsmaxPartials;
+        a.cached_outputs = true;
         uint32_t npart = 0;
         if (fw.fmt == fqimpl::FMT_NVT) {
             hipError_t e = fqimpl::launch_absmax(w_bf16, K * N, a.partials, &npart, st);

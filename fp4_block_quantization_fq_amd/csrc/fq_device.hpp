@@ -10,6 +10,20 @@
 //  - Stochastic rounding with E[round(x)] = x (TetraJet-v2, sec. 2.A), drawn
 //    from Philox4x32-10 (Salmon et al., SC'11) keyed by seed and indexed by
 //    element.
+//
+// Work unit: one lane owns 16 consecutive elements along the quantization
+// axis, held as 8 packed BF16 pairs.  That is one NVFP4 block, or half of an
+// MXFP4 block (the partner lane is lane ^ 1).
+//
+// gfx950 conversion instructions used (their rounding was measured against
+// the format definitions on every BF16 input and on FP32 inputs around every
+// rounding threshold):
+//  - v_cvt_scalef32_pk_fp4_{bf16,f32}: two values -> two E2M1 codes of
+//    RNE(x / 2^floor(log2 scale)), sign kept, saturating at 6.  With a
+//    power-of-two scale this is the MXFP4 encoder; with scale 1 it encodes a
+//    precomputed NVFP4 quotient.
+//  - v_cvt_scalef32_pk_{bf16,f32}_fp4: two codes -> +-g * 2^floor(log2 scale),
+//    exact for power-of-two scales (code 8 gives -0.0).
 // The kernels are compiled with -ffp-contract=off: every float expression
 // below is exactly the operation written.
 #pragma once
@@ -23,6 +37,8 @@ enum { FMT_MX = 0, FMT_NVT = 1, FMT_NV128 = 2 };
 enum { RND_RNE = 0, RND_SR = 1 };
 
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float as_f(uint32_t u) { return __uint_as_float(u); }
 __device__ __forceinline__ uint32_t as_u(float f) { return __float_as_uint(f); }
@@ -36,6 +52,14 @@ __device__ __forceinline__ uint32_t pkmax_u16(uint32_t a, uint32_t b)
 
 // BF16 magnitudes order like their bit patterns once the sign is cleared, so
 // the block maximum is an integer maximum over (bits & 0x7FFF).
+__device__ __forceinline__ uint32_t absmax_bits_pairs8(const uint32_t (&xp)[8])
+{
+    const uint32_t M = 0x7FFF7FFFu;
+    uint32_t m01 = pkmax_u16(xp[0] & M, xp[1] & M), m23 = pkmax_u16(xp[2] & M, xp[3] & M);
+    uint32_t m45 = pkmax_u16(xp[4] & M, xp[5] & M), m67 = pkmax_u16(xp[6] & M, xp[7] & M);
+    uint32_t m = pkmax_u16(pkmax_u16(m01, m23), pkmax_u16(m45, m67));
+    return max(m & 0xFFFFu, m >> 16);
+}
 __device__ __forceinline__ uint32_t absmax_bits_8(const uint4 &v)
 {
     const uint32_t M = 0x7FFF7FFFu;
@@ -44,18 +68,16 @@ __device__ __forceinline__ uint32_t absmax_bits_8(const uint4 &v)
 }
 
 // ---- cross-lane maximum with DPP (no LDS traffic) -------------------------
-// quad_perm [1,0,3,2]: partner lane i^1
-__device__ __forceinline__ uint32_t dpp_max_xor1(uint32_t v)
+// Values are non-negative, so a disabled source lane (read as 0) is harmless.
+__device__ __forceinline__ uint32_t dpp_max_xor1(uint32_t v)   // quad_perm [1,0,3,2]
 {
     return max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));
 }
-// quad_perm [2,3,0,1]: partner lane i^2
-__device__ __forceinline__ uint32_t dpp_max_xor2(uint32_t v)
+__device__ __forceinline__ uint32_t dpp_max_xor2(uint32_t v)   // quad_perm [2,3,0,1]
 {
     return max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));
 }
-// row_half_mirror: lane i <-> 7-i within each group of 8 lanes
-__device__ __forceinline__ uint32_t dpp_max_half_mirror(uint32_t v)
+__device__ __forceinline__ uint32_t dpp_max_half_mirror(uint32_t v)   // i <-> 7-i in 8 lanes
 {
     return max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));
 }
@@ -68,6 +90,11 @@ __device__ __forceinline__ uint32_t dpp_max_ror8(uint32_t v)
 {
     return max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xF, 0xF, false));
 }
+// maximum over the 8 lanes 8k..8k+7
+__device__ __forceinline__ uint32_t dpp_max_8lanes(uint32_t v)
+{
+    return dpp_max_half_mirror(dpp_max_xor2(dpp_max_xor1(v)));
+}
 
 // ---- E8M0 (MXFP4) ----------------------------------------------------------
 // Scale code from the BF16 magnitude bits of the block maximum: the BF16
@@ -75,10 +102,9 @@ __device__ __forceinline__ uint32_t dpp_max_ror8(uint32_t v)
 // zero maxima (field 0) fall below the clamp at 2^-127 anyway.
 __device__ __forceinline__ uint32_t mx_scale_code(uint32_t amax_bits16)
 {
-    int e = (int)(amax_bits16 >> 7);      // BF16 exponent field
-    return (uint32_t)max(e - 2, 0);       // clamp(floor(log2) - 2, -127, .) + 127
+    return (uint32_t)max((int)(amax_bits16 >> 7) - 2, 0);
 }
-// 2^(code-127) and its exact reciprocal 2^(127-code) (code <= 252 here).
+// 2^(code-127) (FP32 subnormal 2^-127 for code 0) and its exact reciprocal.
 __device__ __forceinline__ float e8m0_value(uint32_t code)
 {
     return code ? as_f(code << 23) : as_f(0x00400000u);
@@ -105,100 +131,31 @@ __device__ __forceinline__ float e4m3_value(uint32_t code)
     return code >= 8u ? as_f((code + 960u) << 20) : (float)code * 0.001953125f;
 }
 
-// ---- correctly rounded quotient |x| / s ------------------------------------
-// With rcp = RN(1/s) (a correctly rounded division, once per block), the
-// sequence q = RN(ax * rcp); r = ax - q * s (exact by FMA); q' = RN(q + r * rcp)
-// returns RN(ax / s) for every BF16 ax when the quotient and the residual are
-// in the normal range (Markstein's correction step; verified exhaustively for
-// all 2^7 BF16 significands against all 2^23 FP32 divisor significands).
-// Callers keep s >= 2^-64 by rescaling both operands by 2^64 (exact) when the
-// block scale is smaller; quotients below 2^-17 only ever map to code 0.
-__device__ __forceinline__ float quot_rn(float ax, float s, float rcp)
+// ---- correctly rounded quotients -------------------------------------------
+// q = RN(a * rb); r = a - q * b (exact by FMA); q' = RN(q + r * rb), with
+// rb = RN(1/b).  This is RN(a / b):
+//  - for every BF16 a and every FP32 b in the normal range (checked on the
+//    host for all 2^7 x 2^23 significand pairs);
+//  - for a = RN(amax / 6) and b = RN(A / 2688) with BF16 maxima amax <= A
+//    and b >= 2^-64, wherever the result exceeds 2^-11 (checked for all pairs;
+//    below that the E4M3 block scale is 0 either way).
+__device__ __forceinline__ float div_corrected(float a, float b, float rb)
 {
-    float q = ax * rcp;
-    float r = __builtin_fmaf(-q, s, ax);
-    return __builtin_fmaf(r, rcp, q);
+    float q = a * rb;
+    float r = __builtin_fmaf(-q, b, a);
+    return __builtin_fmaf(r, rb, q);
 }
-
-// ---- E2M1 encoders ---------------------------------------------------------
-// In [0,2) the grid step is 0.5, in [2,4) it is 1, in [4,8) it is 2.  Adding
-// 2^22, 2^23 or 2^24 rounds a to that step with the FPU's round-to-nearest-
-// even, and the even multiple is exactly the even E2M1 code.  e is the FP32
-// exponent field of a clamped to [127, 130], so the step is 2^(e-128).
-// Outputs: m (3-bit magnitude code) and g (its value, at most 6).
-__device__ __forceinline__ void e2m1_rne(float a, uint32_t &m, float &g)
+// Division of a BF16 value by 6 and by 2688 (checked for every BF16 input).
+__device__ __forceinline__ float div6(float a) { return div_corrected(a, 6.0f, as_f(0x3E2AAAABu)); }
+__device__ __forceinline__ float nv_outer_scale(float amax)
 {
-    uint32_t e = min(max(as_u(a) >> 23, 127u), 130u);
-    uint32_t Mb = (e << 23) + (22u << 23);        // 2^(e-105)
-    float t = a + as_f(Mb);                       // RNE to the grid step
-    uint32_t steps = as_u(t) - Mb;                // multiples of the step
-    m = min(steps + 2u * e - 254u, 7u);           // + 0/2/4 per binade
-    g = __builtin_fminf(t - as_f(Mb), 6.0f);
-}
-
-// Stochastic rounding with a 16-bit draw r: N = floor(a * 2^16 / step) holds
-// the grid index above the binade base in its upper half and the threshold
-// T = floor(frac * 2^16) in its lower 16 bits; round up iff r < T.
-__device__ __forceinline__ uint32_t e2m1_sr(float a, uint32_t r)
-{
-    uint32_t e = min(max(as_u(a) >> 23, 127u), 130u);
-    float sc = as_f((271u - e) << 23);            // 2^(144-e) = 2^16 / step
-    uint32_t N = (uint32_t)(a * sc);              // exact product, truncation
-    uint32_t down = (N >> 16) + 2u * e - 254u;
-    uint32_t up = (r < (N & 0xFFFFu)) ? 1u : 0u;
-    return min(down + up, 7u);
-}
-
-// E2M1 magnitude code -> value (0, .5, 1, 1.5, 2, 3, 4, 6).
-__device__ __forceinline__ float e2m1_value(uint32_t m)
-{
-    // m >= 2: exponent 126 + (m >> 1), mantissa bit m & 1  ==  (m + 252) << 22
-    float big = as_f((m + 252u) << 22);
-    return m >= 2u ? big : (m ? 0.5f : 0.0f);
-}
-
-// ---- Philox4x32-10 ---------------------------------------------------------
-struct u32x4 { uint32_t v[4]; };
-
-__device__ __forceinline__ u32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2,
-                                               uint32_t c3, uint32_t k0, uint32_t k1)
-{
-#pragma unroll
-    for (int i = 0; i < 10; ++i) {
-        uint64_t p0 = (uint64_t)0xD2511F53u * c0;
-        uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
-        uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
-        uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
-        c1 = (uint32_t)p1;
-        c3 = (uint32_t)p0;
-        c0 = n0;
-        c2 = n2;
-        k0 += 0x9E3779B9u;
-        k1 += 0xBB67AE85u;
-    }
-    u32x4 o;
-    o.v[0] = c0; o.v[1] = c1; o.v[2] = c2; o.v[3] = c3;
-    return o;
-}
-
-// ---- BF16 helpers ----------------------------------------------------------
-__device__ __forceinline__ uint32_t bf16_pair_rne(float lo, float hi)
-{
-    __bf16 a = (__bf16)lo, b = (__bf16)hi;        // v_cvt_pk_bf16_f32 (RNE)
-    return (uint32_t)__builtin_bit_cast(unsigned short, a)
-         | ((uint32_t)__builtin_bit_cast(unsigned short, b) << 16);
-}
-// FP32 bits of element j (0..7) of a 16-byte BF16 vector.
-__device__ __forceinline__ uint32_t elem_bits(const uint4 &v, int j)
-{
-    uint32_t w = (j >> 1) == 0 ? v.x : (j >> 1) == 1 ? v.y : (j >> 1) == 2 ? v.z : v.w;
-    return (j & 1) ? (w & 0xFFFF0000u) : (w << 16);
+    return div_corrected(amax, 2688.0f, as_f(0x39C30C31u));
 }
 
 // ---- per-block scale state ---------------------------------------------------
-// s_eff: effective scale; rcp: RN(1/s_eff') and sq: s_eff' where s_eff' is
-// s_eff rescaled by 2^64 when it is below 2^-64 (then xs = 2^64 scales |x|),
-// so that the quotient sequence stays in the normal range.
+// s_eff: effective scale; rcp: RN(1/sq) with sq = s_eff, or s_eff * 2^64 when
+// s_eff < 2^-64 (then xs = 2^64 scales |x| too, keeping the quotient sequence
+// in the normal range); a zero scale sets xs = 0 so every a is 0.
 struct BlockScale {
     float s_eff;
     float sq;
@@ -207,22 +164,6 @@ struct BlockScale {
     uint32_t code;
 };
 
-__device__ __forceinline__ BlockScale mx_block_scale(uint32_t amax_bits16)
-{
-    BlockScale b;
-    b.code = mx_scale_code(amax_bits16);
-    b.s_eff = e8m0_value(b.code);
-    b.rcp = e8m0_recip(b.code);
-    b.sq = b.s_eff;
-    b.xs = 1.0f;
-    return b;
-}
-
-// Quotient set-up for an NVFP4 block of effective scale s_eff.  A zero scale
-// (the E4M3 code or its product with the outer scale underflowed) maps every
-// element to a = 0: xs = 0 zeroes |x| before the quotient.  Scales below
-// 2^-64 are rescaled with |x| by 2^64; the block's elements are then at most
-// about 9 * s_eff, so the scaled |x| stays finite.
 __device__ __forceinline__ void finish_nv_scale(BlockScale &b)
 {
     b.xs = 1.0f;
@@ -240,35 +181,253 @@ __device__ __forceinline__ void finish_nv_scale(BlockScale &b)
     b.rcp = 1.0f / b.sq;
 }
 
+__device__ __forceinline__ BlockScale mx_block_scale(uint32_t amax_bits16)
+{
+    BlockScale b;
+    b.code = mx_scale_code(amax_bits16);
+    b.s_eff = e8m0_value(b.code);
+    b.rcp = e8m0_recip(b.code);
+    b.sq = b.s_eff;
+    b.xs = 1.0f;
+    return b;
+}
+
+// Outer scale s and its reciprocal rs = RN(1/s) (rs unused when s < 2^-64).
+struct OuterScale {
+    float s;
+    float rs;
+};
+__device__ __forceinline__ OuterScale make_outer(float amax_outer)
+{
+    OuterScale o;
+    o.s = nv_outer_scale(amax_outer);
+    o.rs = (o.s >= 0x1p-64f) ? 1.0f / o.s : 0.0f;
+    return o;
+}
+
 // NVFP4 block scale under outer scale s: e4 = E4M3(RN(RN(amax/6) / s)),
 // s_eff = RN(e4 * s).
-__device__ __forceinline__ BlockScale nv_block_scale(float amax, float s)
+__device__ __forceinline__ BlockScale nv_block_scale(float amax, const OuterScale &o)
 {
     BlockScale b;
     float sc = 0.0f;
-    if (s != 0.0f) {
-        float p = amax / 6.0f;
-        sc = p / s;
+    if (o.s != 0.0f) {
+        const float p = div6(amax);
+        sc = (o.s >= 0x1p-64f) ? div_corrected(p, o.s, o.rs) : p / o.s;
     }
     b.code = e4m3_encode_sat(sc);
-    b.s_eff = e4m3_value(b.code) * s;
+    b.s_eff = e4m3_value(b.code) * o.s;
     finish_nv_scale(b);
     return b;
 }
 
-// Scaled magnitude a = RN(|x| / s_eff) for the block.
+template <int FMT>
+__device__ __forceinline__ BlockScale scale_from_code(uint32_t code, float s)
+{
+    BlockScale b;
+    b.code = code;
+    b.xs = 1.0f;
+    if (FMT == FMT_MX) {
+        b.s_eff = e8m0_value(code);
+        b.rcp = e8m0_recip(code);
+        b.sq = b.s_eff;
+    } else {
+        b.s_eff = e4m3_value(code) * s;
+        finish_nv_scale(b);
+    }
+    return b;
+}
+
+// Scaled magnitude a = RN(|x| / s_eff) (x as FP32 bits).
 template <int FMT>
 __device__ __forceinline__ float scaled_mag(uint32_t xbits, const BlockScale &b)
 {
     float ax = as_f(xbits & 0x7FFFFFFFu);
     if (FMT == FMT_MX) return ax * b.rcp;         // power-of-two scale: exact
-    return quot_rn(ax * b.xs, b.sq, b.rcp);
+    return div_corrected(ax * b.xs, b.sq, b.rcp);
 }
 
-// NVFP4 outer scale amax / (6 * 448).
-__device__ __forceinline__ float nv_outer_scale(float amax)
+// ---- stochastic rounding ---------------------------------------------------
+// With g_k <= a < g_{k+1}, T = floor((a - g_k) / (g_{k+1} - g_k) * 2^16) and
+// the element rounds up iff r16 < T.  rinv = 0xFFFF - r16 (a bijection of the
+// draw) turns the test into a carry: floor(a * 2^16 / step) + rinv carries
+// into bit 16 exactly when r16 < T.  The grid step is 2^(e-128) for the
+// binade exponent field e clamped to [127, 130]; the base code of each binade
+// is 2 * (e - 127).
+__device__ __forceinline__ uint32_t e2m1_sr(float a, uint32_t rinv)
 {
-    return amax / 2688.0f;
+    const uint32_t eb = min(max(as_u(a) & 0x7F800000u, 0x3F800000u), 0x41000000u);
+    const float sc = as_f(0x87800000u - eb);      // 2^(144 - e) = 2^16 / step
+    const uint32_t N = (uint32_t)(a * sc);        // exact product, truncation
+    const uint32_t k = (N + rinv) >> 16;          // grid index above the base, + up
+    return min(k + (eb >> 22) - 254u, 7u);
+}
+
+// ---- Philox4x32-10 ---------------------------------------------------------
+struct u32x4 { uint32_t v[4]; };
+
+__device__ __forceinline__ u32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2,
+                                               uint32_t c3, uint32_t k0, uint32_t k1)
+{
+#pragma unroll
+    for (int i = 0; i < 10; ++i) {
+        uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+        uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+        uint32_t n0 = __builtin_amdgcn_bitop3_b32((uint32_t)(p1 >> 32), c1, k0, 0x96);  // xor3
+        uint32_t n2 = __builtin_amdgcn_bitop3_b32((uint32_t)(p0 >> 32), c3, k1, 0x96);
+        c1 = (uint32_t)p1;
+        c3 = (uint32_t)p0;
+        c0 = n0;
+        c2 = n2;
+        k0 += 0x9E3779B9u;
+        k1 += 0xBB67AE85u;
+    }
+    u32x4 o;
+    o.v[0] = c0; o.v[1] = c1; o.v[2] = c2; o.v[3] = c3;
+    return o;
+}
+
+// 0xFFFF - r16 for element j (0..7) of a Philox output block.
+__device__ __forceinline__ uint32_t rinv16(const u32x4 &o, int j)
+{
+    const uint32_t w = ~o.v[j >> 1];
+    return (j & 1) ? (w >> 16) : (w & 0xFFFFu);
+}
+
+// ---- BF16 helpers ----------------------------------------------------------
+__device__ __forceinline__ uint32_t bf16_pair_rne(float lo, float hi)
+{
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
+}
+__device__ __forceinline__ uint32_t lo_bits(uint32_t pair) { return pair << 16; }
+__device__ __forceinline__ uint32_t hi_bits(uint32_t pair) { return pair & 0xFFFF0000u; }
+
+// hardware converters with a compile-time byte selector
+template <int SEL>
+__device__ __forceinline__ uint32_t hw_enc_bf16(uint32_t old, uint32_t pair, float scale)
+{
+    return __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(old, __builtin_bit_cast(bf16x2, pair), scale, SEL);
+}
+template <int SEL>
+__device__ __forceinline__ uint32_t hw_enc_f32(uint32_t old, float a0, float a1)
+{
+    return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a0, a1, 1.0f, SEL);
+}
+template <int SEL>
+__device__ __forceinline__ uint32_t hw_dec_bf16(uint32_t codes, float scale)
+{
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, SEL));
+}
+template <int SEL>
+__device__ __forceinline__ uint32_t hw_dec_nv(uint32_t codes, float s_eff)
+{
+    const f32x2 g = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, SEL);
+    return bf16_pair_rne(g[0] * s_eff, g[1] * s_eff);
+}
+
+// Dequantize 8 codes (one 32-bit word, element i in nibble i) to 4 BF16 pairs.
+template <int FMT>
+__device__ __forceinline__ void decode8(uint32_t cw, float s_eff, uint32_t *yp)
+{
+    if (FMT == FMT_MX) {
+        yp[0] = hw_dec_bf16<0>(cw, s_eff);
+        yp[1] = hw_dec_bf16<1>(cw, s_eff);
+        yp[2] = hw_dec_bf16<2>(cw, s_eff);
+        yp[3] = hw_dec_bf16<3>(cw, s_eff);
+    } else {
+        yp[0] = hw_dec_nv<0>(cw, s_eff);
+        yp[1] = hw_dec_nv<1>(cw, s_eff);
+        yp[2] = hw_dec_nv<2>(cw, s_eff);
+        yp[3] = hw_dec_nv<3>(cw, s_eff);
+    }
+}
+
+// ---- the block-part encoder ------------------------------------------------
+// xp: NP packed BF16 pairs along the quantization axis (element 2i in the low
+// half of xp[i]), NP = 4 (8 elements) or 8 (16 elements); rnd: Philox output
+// blocks for elements 0-7 and 8-15 (SR only).
+// Outputs: cw (element 2i in the low nibble of byte i, 8 codes per word) and
+// yp (the dequantized BF16 values, packed like xp).
+template <int FMT, int RND, int NP>
+__device__ __forceinline__ void encode_pairs(const uint32_t (&xp)[NP], const BlockScale &b,
+                                             const u32x4 *rnd, uint32_t (&cw)[NP / 4],
+                                             uint32_t (&yp)[NP])
+{
+    constexpr int NW = NP / 4;
+    if (FMT == FMT_MX && RND == RND_RNE) {
+        // hardware encode straight from BF16 at the power-of-two scale
+#pragma unroll
+        for (int h = 0; h < NW; ++h) {
+            uint32_t c = hw_enc_bf16<0>(0u, xp[4 * h + 0], b.s_eff);
+            c = hw_enc_bf16<1>(c, xp[4 * h + 1], b.s_eff);
+            c = hw_enc_bf16<2>(c, xp[4 * h + 2], b.s_eff);
+            c = hw_enc_bf16<3>(c, xp[4 * h + 3], b.s_eff);
+            cw[h] = c;
+        }
+    } else {
+        float a[2 * NP];
+        if (FMT == FMT_MX) {
+#pragma unroll
+            for (int i = 0; i < NP; ++i) {
+                a[2 * i] = __builtin_fabsf(as_f(lo_bits(xp[i]))) * b.rcp;
+                a[2 * i + 1] = __builtin_fabsf(as_f(hi_bits(xp[i]))) * b.rcp;
+            }
+        } else if (b.xs == 1.0f) {
+#pragma unroll
+            for (int i = 0; i < NP; ++i) {
+                a[2 * i] = div_corrected(__builtin_fabsf(as_f(lo_bits(xp[i]))), b.sq, b.rcp);
+                a[2 * i + 1] = div_corrected(__builtin_fabsf(as_f(hi_bits(xp[i]))), b.sq, b.rcp);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < NP; ++i) {
+                a[2 * i] = div_corrected(__builtin_fabsf(as_f(lo_bits(xp[i]))) * b.xs, b.sq, b.rcp);
+                a[2 * i + 1] = div_corrected(__builtin_fabsf(as_f(hi_bits(xp[i]))) * b.xs, b.sq, b.rcp);
+            }
+        }
+        if (RND == RND_RNE) {
+            // signed quotient -> hardware RNE encoder at scale 1
+            float sa[2 * NP];
+#pragma unroll
+            for (int i = 0; i < NP; ++i) {
+                sa[2 * i] = as_f(as_u(a[2 * i]) | ((xp[i] << 16) & 0x80000000u));
+                sa[2 * i + 1] = as_f(as_u(a[2 * i + 1]) | (xp[i] & 0x80000000u));
+            }
+#pragma unroll
+            for (int h = 0; h < NW; ++h) {
+                uint32_t c = hw_enc_f32<0>(0u, sa[8 * h + 0], sa[8 * h + 1]);
+                c = hw_enc_f32<1>(c, sa[8 * h + 2], sa[8 * h + 3]);
+                c = hw_enc_f32<2>(c, sa[8 * h + 4], sa[8 * h + 5]);
+                c = hw_enc_f32<3>(c, sa[8 * h + 6], sa[8 * h + 7]);
+                cw[h] = c;
+            }
+        } else {
+#pragma unroll
+            for (int h = 0; h < NW; ++h) cw[h] = 0u;
+#pragma unroll
+            for (int j = 0; j < 2 * NP; ++j) {
+                const uint32_t pr = xp[j >> 1];
+                const uint32_t sgn = (j & 1) ? ((pr >> 28) & 8u) : ((pr >> 12) & 8u);
+                const uint32_t m = e2m1_sr(a[j], rinv16(rnd[j >> 3], j & 7)) | sgn;
+                cw[j >> 3] |= m << (4 * (j & 7));
+            }
+        }
+    }
+#pragma unroll
+    for (int h = 0; h < NW; ++h) decode8<FMT>(cw[h], b.s_eff, &yp[4 * h]);
+}
+
+// Clip mask of 2*NP elements (bit j set when element j has a <= 6, i.e. kept).
+template <int FMT, int NP>
+__device__ __forceinline__ uint32_t keep_mask(const uint32_t (&xp)[NP], const BlockScale &b)
+{
+    uint32_t k = 0;
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+        k |= (scaled_mag<FMT>(lo_bits(xp[i]), b) <= 6.0f ? 1u : 0u) << (2 * i);
+        k |= (scaled_mag<FMT>(hi_bits(xp[i]), b) <= 6.0f ? 1u : 0u) << (2 * i + 1);
+    }
+    return k;
 }
 
 }  // namespace fqdev

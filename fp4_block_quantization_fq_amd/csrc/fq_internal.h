@@ -27,6 +27,7 @@ struct QuantArgs {
     void *scales;         // or null
     float *outer;         // or null
     uint32_t *partials;   // kAbsmaxPartials words (NV per-tensor only)
+    bool cached_outputs;  // ordinary stores (outputs re-read right away) instead of streaming
 };
 
 hipError_t launch_absmax(const void *x, int64_t n_elems, uint32_t *partials,

@@ -1,20 +1,21 @@
 // fq_kernels.hip -- streaming FP4 quantize / dequantize / STE kernels, gfx950.
 //
-// All kernels are HBM-bound streams.  Work is mapped so that every global
-// access is a 16-byte vector access coalesced across the wavefront:
+// All kernels are HBM-bound streams.  A lane always owns 16 consecutive
+// elements along the quantization axis (one NVFP4 block, half an MXFP4 block),
+// and every global access is a 16-byte vector access coalesced across the
+// wavefront:
 //
 //  * Row axis (groups along the contiguous dimension): the tensor is a flat
-//    array of 8-element chunks (16 bytes of BF16).  Lane i of a wave owns
-//    chunk base+i, so a 16-element NVFP4 block is a lane pair, a 32-element
-//    MXFP4 block a lane quad, and a 128-element outer block a DPP row of 16
-//    lanes.  Block maxima are combined across lanes with DPP, without LDS.
-//  * Column axis (groups of B consecutive rows of one column, i.e. the rows
-//    of x^T): each lane owns an 8-column x B-row tile and loads it as B
-//    row segments of 16 bytes.  The 64 lanes of a wave cover 64 columns x
-//    8 row blocks; for one column the 8 lanes of consecutive row blocks
-//    write adjacent code bytes, so transposed codes leave the wave as
-//    contiguous 64-byte (NVFP4) or 128-byte (MXFP4) runs.  The 128-row outer
-//    block of the double-block format is those 8 lanes (DPP half-row).
+//    array of 16-element segments (32 bytes of BF16).  Lane i of a wave owns
+//    segment base+i, so an MXFP4 block is a lane pair and a 128-element outer
+//    block is 8 lanes; block maxima are combined with DPP, without LDS.
+//  * Column axis (groups of consecutive rows of one column, i.e. the rows of
+//    x^T): a lane owns an 8-column x 16-row tile, loaded as 16 row segments
+//    of 16 bytes.  The 64 lanes of a wave cover 64 columns x 128 rows; the
+//    8 lanes of one column group hold consecutive row blocks, so their
+//    transposed code bytes leave the wave as one contiguous 64-byte run per
+//    column, MXFP4 blocks are lane pairs and the double-block's 128-row outer
+//    block is those 8 lanes.
 //
 // Numerics follow fq_device.hpp; the op definitions are those of fq.h.
 #include "fq_device.hpp"
@@ -24,8 +25,42 @@ using namespace fqdev;
 
 namespace {
 
+// Row-axis streams, chosen by measurement on MI355X (16384 x 4096 BF16):
+//  - round-to-nearest kernels, the STE and dequantize map one 8-element chunk
+//    to a lane (every load and store instruction is one contiguous 1 KB run);
+//  - stochastic-rounding kernels, which are bound by Philox and encoder ALU
+//    work, map a 16-element segment to a lane, halving the per-lane block
+//    scale work;
+//  - one unit per thread and a grid as large as the tensor (capped), so that
+//    every CU has many waves in flight;
+//  - streamed outputs use non-temporal stores (they are not re-read by the
+//    kernel, and keeping them out of the caches helps the input stream); the
+//    QAT linear writes its operands with ordinary stores because the GEMM
+//    reads them right away.
 constexpr int kThreads = 256;
-constexpr uint32_t kRowGridCap = 4096;   // workgroups for grid-stride streams
+constexpr uint32_t kRowGridCap = 1u << 20;
+
+typedef uint32_t u32v4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32v2 __attribute__((ext_vector_type(2)));
+
+template <bool NT>
+__device__ __forceinline__ void st_stream(uint4 *p, const uint4 &v)
+{
+    if (NT) __builtin_nontemporal_store((u32v4){v.x, v.y, v.z, v.w}, reinterpret_cast<u32v4 *>(p));
+    else *p = v;
+}
+template <bool NT>
+__device__ __forceinline__ void st_stream(uint2 *p, const uint2 &v)
+{
+    if (NT) __builtin_nontemporal_store((u32v2){v.x, v.y}, reinterpret_cast<u32v2 *>(p));
+    else *p = v;
+}
+template <bool NT>
+__device__ __forceinline__ void st_stream(uint32_t *p, uint32_t v)
+{
+    if (NT) __builtin_nontemporal_store(v, p);
+    else *p = v;
+}
 
 // ---------------------------------------------------------------------------
 // Per-tensor maximum: partial maxima of |x| (as BF16 magnitude bits), one per
@@ -65,79 +100,95 @@ __global__ __launch_bounds__(kThreads) void k_absmax(const uint4 *__restrict__ x
 }
 
 // NVFP4 per-tensor outer scale from the partial maxima (every thread).
-__device__ __forceinline__ float tensor_scale(const uint32_t *__restrict__ partials,
-                                              uint32_t npart)
+__device__ __forceinline__ OuterScale tensor_scale(const uint32_t *__restrict__ partials,
+                                                   uint32_t npart)
 {
     __shared__ uint32_t red[4];
     uint32_t m = 0;
     for (uint32_t i = threadIdx.x; i < npart; i += kThreads) m = max(m, partials[i]);
     m = block_reduce_max(m, red);
-    return nv_outer_scale(as_f(m << 16));
+    return make_outer(as_f(m << 16));
 }
 
-// Block scale rebuilt from a stored scale code (dequantize, STE).
+// Block scale of this lane's 16 elements (cross-lane for MXFP4 and the
+// double block).  `outer_out` receives the 128-block outer scale (NV128).
 template <int FMT>
-__device__ __forceinline__ BlockScale scale_from_code(uint32_t code, float s)
+__device__ __forceinline__ BlockScale lane_block_scale(uint32_t amax16, const OuterScale &ot,
+                                                       float &outer_out)
 {
-    BlockScale b;
-    b.code = code;
-    b.xs = 1.0f;
-    if (FMT == FMT_MX) {
-        b.s_eff = e8m0_value(code);
-        b.rcp = e8m0_recip(code);
-        b.sq = b.s_eff;
-    } else {
-        b.s_eff = e4m3_value(code) * s;
-        finish_nv_scale(b);
-    }
-    return b;
-}
-
-// Encode one element: returns the 4-bit code and the signed FP32 value
-// g * s_eff (before BF16 rounding).
-template <int FMT, int RND>
-__device__ __forceinline__ uint32_t encode_elem(uint32_t xb, const BlockScale &b,
-                                                uint32_t r16, float &yv)
-{
-    float a = scaled_mag<FMT>(xb, b);
-    uint32_t m;
-    float g;
-    if (RND == RND_RNE) {
-        e2m1_rne(a, m, g);
-    } else {
-        m = e2m1_sr(a, r16);
-        g = e2m1_value(m);
-    }
-    yv = as_f(as_u(g * b.s_eff) | (xb & 0x80000000u));
-    return m | ((xb >> 28) & 8u);
+    if (FMT == FMT_MX) return mx_block_scale(dpp_max_xor1(amax16));
+    if (FMT == FMT_NVT) return nv_block_scale(as_f(amax16 << 16), ot);
+    const uint32_t mo = dpp_max_8lanes(amax16);
+    const OuterScale o = make_outer(as_f(mo << 16));
+    outer_out = o.s;
+    return nv_block_scale(as_f(amax16 << 16), o);
 }
 
 // ---------------------------------------------------------------------------
-// Row-axis quantizer (flat chunk stream)
+// Row-axis quantizer (flat segment stream)
 // ---------------------------------------------------------------------------
-template <int FMT, int RND>
-__device__ __forceinline__ void quant_row_chunk(uint32_t c, const uint4 &v, float s_t,
+template <int FMT, int RND, bool NT>
+__device__ __forceinline__ void quant_row_seg(uint32_t seg, const uint4 &v0, const uint4 &v1,
+                                              const OuterScale &ot, uint4 *__restrict__ y,
+                                              uint2 *__restrict__ codes,
+                                              uint8_t *__restrict__ scales,
+                                              float *__restrict__ outer, uint32_t seed_lo,
+                                              uint32_t seed_hi)
+{
+    const uint32_t lane = threadIdx.x & 63;
+    const uint32_t xp[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+    float so = 0.0f;
+    const BlockScale b = lane_block_scale<FMT>(absmax_bits_pairs8(xp), ot, so);
+    if (FMT == FMT_NV128 && outer && (lane & 7) == 0) outer[seg >> 3] = so;
+    if (scales) {
+        if (FMT == FMT_MX) {
+            if ((lane & 1) == 0) scales[seg >> 1] = (uint8_t)b.code;
+        } else {
+            scales[seg] = (uint8_t)b.code;
+        }
+    }
+    u32x4 rnd[2];
+    if (RND == RND_SR) {
+        rnd[0] = philox4x32_10(2 * seg, 0u, 0u, 0u, seed_lo, seed_hi);
+        rnd[1] = philox4x32_10(2 * seg + 1, 0u, 0u, 0u, seed_lo, seed_hi);
+    }
+    uint32_t cw[2], yp[8];
+    encode_pairs<FMT, RND, 8>(xp, b, rnd, cw, yp);
+    if (codes) st_stream<NT>(&codes[seg], make_uint2(cw[0], cw[1]));
+    if (y) {
+        st_stream<NT>(&y[2 * seg], make_uint4(yp[0], yp[1], yp[2], yp[3]));
+        st_stream<NT>(&y[2 * seg + 1], make_uint4(yp[4], yp[5], yp[6], yp[7]));
+    }
+}
+
+// Chunk mapping: lane owns 8 elements; an NVFP4 block is a lane pair, an
+// MXFP4 block a lane quad and a 128-element outer block a DPP row of 16.
+template <int FMT>
+__device__ __forceinline__ BlockScale chunk_block_scale(uint32_t amax8, const OuterScale &ot,
+                                                        float &outer_out)
+{
+    const uint32_t m = dpp_max_xor1(amax8);
+    if (FMT == FMT_MX) return mx_block_scale(dpp_max_xor2(m));
+    if (FMT == FMT_NVT) return nv_block_scale(as_f(m << 16), ot);
+    const uint32_t mo = dpp_max_ror8(dpp_max_ror4(dpp_max_xor2(m)));
+    const OuterScale o = make_outer(as_f(mo << 16));
+    outer_out = o.s;
+    return nv_block_scale(as_f(m << 16), o);
+}
+
+template <int FMT, int RND, bool NT>
+__device__ __forceinline__ void quant_row_chunk(uint32_t c, const uint4 &v, const OuterScale &ot,
                                                 uint4 *__restrict__ y,
                                                 uint32_t *__restrict__ codes,
                                                 uint8_t *__restrict__ scales,
-                                                float *__restrict__ outer,
-                                                uint32_t seed_lo, uint32_t seed_hi)
+                                                float *__restrict__ outer, uint32_t seed_lo,
+                                                uint32_t seed_hi)
 {
     const uint32_t lane = threadIdx.x & 63;
-    uint32_t mb = dpp_max_xor1(absmax_bits_8(v));
-    BlockScale b;
-    if (FMT == FMT_MX) {
-        mb = dpp_max_xor2(mb);
-        b = mx_block_scale(mb);
-    } else {
-        float s = s_t;
-        if (FMT == FMT_NV128) {
-            uint32_t mo = dpp_max_ror8(dpp_max_ror4(dpp_max_xor2(mb)));
-            s = nv_outer_scale(as_f(mo << 16));
-            if (outer && (lane & 15) == 0) outer[c >> 4] = s;
-        }
-        b = nv_block_scale(as_f(mb << 16), s);
-    }
+    const uint32_t xp[4] = {v.x, v.y, v.z, v.w};
+    float so = 0.0f;
+    const BlockScale b = chunk_block_scale<FMT>(absmax_bits_8(v), ot, so);
+    if (FMT == FMT_NV128 && outer && (lane & 15) == 0) outer[c >> 4] = so;
     if (scales) {
         if (FMT == FMT_MX) {
             if ((lane & 3) == 0) scales[c >> 2] = (uint8_t)b.code;
@@ -145,92 +196,117 @@ __device__ __forceinline__ void quant_row_chunk(uint32_t c, const uint4 &v, floa
             if ((lane & 1) == 0) scales[c >> 1] = (uint8_t)b.code;
         }
     }
-    u32x4 rnd;
-    if (RND == RND_SR) rnd = philox4x32_10(c, 0u, 0u, 0u, seed_lo, seed_hi);
-    uint32_t packed = 0;
-    float yv[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        uint32_t r16 = 0;
-        if (RND == RND_SR) r16 = (rnd.v[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
-        uint32_t code = encode_elem<FMT, RND>(elem_bits(v, j), b, r16, yv[j]);
-        packed |= code << (4 * j);
-    }
-    if (codes) codes[c] = packed;
-    if (y) {
-        y[c] = make_uint4(bf16_pair_rne(yv[0], yv[1]), bf16_pair_rne(yv[2], yv[3]),
-                          bf16_pair_rne(yv[4], yv[5]), bf16_pair_rne(yv[6], yv[7]));
-    }
+    u32x4 rnd[1];
+    if (RND == RND_SR) rnd[0] = philox4x32_10(c, 0u, 0u, 0u, seed_lo, seed_hi);
+    uint32_t cw[1], yp[4];
+    encode_pairs<FMT, RND, 4>(xp, b, rnd, cw, yp);
+    if (codes) st_stream<NT>(&codes[c], cw[0]);
+    if (y) st_stream<NT>(&y[c], make_uint4(yp[0], yp[1], yp[2], yp[3]));
 }
 
-template <int FMT, int RND>
+// MAP = 1: one 8-element chunk per lane (units = chunks); MAP = 0: one
+// 16-element segment per lane (units = segments).
+template <int FMT, int RND, int MAP, bool NT>
 __global__ __launch_bounds__(kThreads) void k_quant_row(
-    const uint4 *__restrict__ x, uint32_t nchunks, uint4 *__restrict__ y,
-    uint32_t *__restrict__ codes, uint8_t *__restrict__ scales, float *__restrict__ outer,
+    const uint4 *__restrict__ x, uint32_t nunits, uint4 *__restrict__ y,
+    void *__restrict__ codes, uint8_t *__restrict__ scales, float *__restrict__ outer,
     const uint32_t *__restrict__ partials, uint32_t npart, uint32_t seed_lo,
     uint32_t seed_hi)
 {
-    float s_t = 0.0f;
+    OuterScale ot = {0.0f, 0.0f};
     if (FMT == FMT_NVT) {
-        s_t = tensor_scale(partials, npart);
-        if (outer && blockIdx.x == 0 && threadIdx.x == 0) outer[0] = s_t;
+        ot = tensor_scale(partials, npart);
+        if (outer && blockIdx.x == 0 && threadIdx.x == 0) outer[0] = ot.s;
     }
-    const uint32_t stride = gridDim.x * kThreads * 2;
-    for (uint32_t base = blockIdx.x * kThreads * 2; base < nchunks; base += stride) {
-        const uint32_t c0 = base + threadIdx.x, c1 = c0 + kThreads;
-        uint4 v0 = make_uint4(0, 0, 0, 0), v1 = make_uint4(0, 0, 0, 0);
-        if (c0 < nchunks) v0 = x[c0];
-        if (c1 < nchunks) v1 = x[c1];
-        if (c0 < nchunks)
-            quant_row_chunk<FMT, RND>(c0, v0, s_t, y, codes, scales, outer, seed_lo, seed_hi);
-        if (c1 < nchunks)
-            quant_row_chunk<FMT, RND>(c1, v1, s_t, y, codes, scales, outer, seed_lo, seed_hi);
+    for (uint32_t u = blockIdx.x * kThreads + threadIdx.x; u < nunits;
+         u += gridDim.x * kThreads) {
+        if (MAP == 1) {
+            const uint4 v = x[u];
+            quant_row_chunk<FMT, RND, NT>(u, v, ot, y, (uint32_t *)codes, scales, outer,
+                                          seed_lo, seed_hi);
+        } else {
+            const uint4 v0 = x[2 * u], v1 = x[2 * u + 1];
+            quant_row_seg<FMT, RND, NT>(u, v0, v1, ot, y, (uint2 *)codes, scales, outer,
+                                        seed_lo, seed_hi);
+        }
     }
 }
 
 // ---------------------------------------------------------------------------
-// Column-axis quantizer (lane = 8 columns x B rows)
+// Column-axis kernels: lane = 8 columns x 16 rows
 // ---------------------------------------------------------------------------
-// BF16 half-word c (0..7) of a 16-byte row segment, as FP32 bits.
-__device__ __forceinline__ uint32_t seg_elem(const uint4 &v, int c) { return elem_bits(v, c); }
+struct ColTile {
+    uint32_t col0;   // first of the lane's 8 columns
+    uint32_t row0;   // first of the lane's 16 rows
+    uint32_t rb;     // lane's row block within its 8-lane group
+    bool valid;
+};
 
-__device__ __forceinline__ void seg_set_pair(uint4 &v, int p, uint32_t w)
+// One workgroup covers 64 columns x 512 rows (4 waves of 128 rows); the 1-D
+// grid runs column tiles fastest.
+__device__ __forceinline__ ColTile col_tile(uint32_t R, uint32_t C)
 {
-    if (p == 0) v.x = w;
-    else if (p == 1) v.y = w;
-    else if (p == 2) v.z = w;
+    const uint32_t lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const uint32_t tiles_c = (C + 63) >> 6;
+    ColTile t;
+    t.rb = lane & 7;
+    t.col0 = (blockIdx.x % tiles_c) * 64 + (lane >> 3) * 8;
+    t.row0 = (((blockIdx.x / tiles_c) * 4 + wave) * 8 + t.rb) * 16;
+    t.valid = t.col0 < C && t.row0 < R;
+    return t;
+}
+
+// Packed BF16 pair of column c (0..7) from two row segments (rows r, r+1).
+__device__ __forceinline__ uint32_t col_pair(const uint4 &a, const uint4 &b, int c)
+{
+    const uint32_t wa = (c >> 1) == 0 ? a.x : (c >> 1) == 1 ? a.y : (c >> 1) == 2 ? a.z : a.w;
+    const uint32_t wb = (c >> 1) == 0 ? b.x : (c >> 1) == 1 ? b.y : (c >> 1) == 2 ? b.z : b.w;
+    return (c & 1) ? ((wa >> 16) | (wb & 0xFFFF0000u)) : ((wa & 0xFFFFu) | (wb << 16));
+}
+__device__ __forceinline__ void seg_set_word(uint4 &v, int k, uint32_t w)
+{
+    if (k == 0) v.x = w;
+    else if (k == 1) v.y = w;
+    else if (k == 2) v.z = w;
     else v.w = w;
 }
+// Put the column-pair results of columns 2k and 2k+1 (pairs along rows) back
+// into the row segments.
+__device__ __forceinline__ void scatter_pairs(uint4 (&v)[16], int k, const uint32_t (&ya)[8],
+                                              const uint32_t (&yb)[8])
+{
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        seg_set_word(v[2 * i], k, (ya[i] & 0xFFFFu) | (yb[i] << 16));
+        seg_set_word(v[2 * i + 1], k, (ya[i] >> 16) | (yb[i] & 0xFFFF0000u));
+    }
+}
 
-template <int FMT, int RND>
+template <int FMT, int RND, bool NT>
 __global__ __launch_bounds__(kThreads) void k_quant_col(
     const uint4 *__restrict__ x, uint32_t R, uint32_t C, uint4 *__restrict__ y,
     uint4 *__restrict__ yt, uint8_t *__restrict__ codes, uint8_t *__restrict__ scales,
     float *__restrict__ outer, const uint32_t *__restrict__ partials, uint32_t npart,
     uint32_t seed_lo, uint32_t seed_hi)
 {
-    constexpr int B = (FMT == FMT_MX) ? 32 : 16;
-    float s_t = 0.0f;
+    constexpr uint32_t B = (FMT == FMT_MX) ? 32 : 16;
+    OuterScale ot = {0.0f, 0.0f};
     if (FMT == FMT_NVT) {
-        s_t = tensor_scale(partials, npart);
-        if (outer && blockIdx.x == 0 && threadIdx.x == 0) outer[0] = s_t;
+        ot = tensor_scale(partials, npart);
+        if (outer && blockIdx.x == 0 && threadIdx.x == 0) outer[0] = ot.s;
     }
-    const uint32_t lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const uint32_t rb = lane & 7, cg = lane >> 3;
-    const uint32_t tiles_c = (C + 63) >> 6;           // 1-D grid: column tiles fastest
-    const uint32_t col0 = (blockIdx.x % tiles_c) * 64 + cg * 8;
-    const uint32_t row0 = (((blockIdx.x / tiles_c) * 4 + wave) * 8 + rb) * B;
-    if (col0 >= C || row0 >= R) return;   // whole 8-lane groups leave together for NV128
-    const uint32_t ldx = C >> 3;            // 16-byte segments per row
+    const ColTile t = col_tile(R, C);
+    if (!t.valid) return;     // MXFP4 pairs and double-block groups leave together
+    const uint32_t ldx = C >> 3;   // 16-byte segments per row
 
-    uint4 v[B];
+    uint4 v[16];
 #pragma unroll
-    for (int r = 0; r < B; ++r) v[r] = x[(size_t)(row0 + r) * ldx + (col0 >> 3)];
+    for (int r = 0; r < 16; ++r) v[r] = x[(size_t)(t.row0 + r) * ldx + (t.col0 >> 3)];
 
-    // per-column block maxima: packed u16 max over the B rows
+    // per-column maxima of the lane's 16 rows: packed u16 max
     uint32_t mw[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int r = 0; r < B; ++r) {
+    for (int r = 0; r < 16; ++r) {
         mw[0] = pkmax_u16(mw[0], v[r].x & 0x7FFF7FFFu);
         mw[1] = pkmax_u16(mw[1], v[r].y & 0x7FFF7FFFu);
         mw[2] = pkmax_u16(mw[2], v[r].z & 0x7FFF7FFFu);
@@ -238,90 +314,60 @@ __global__ __launch_bounds__(kThreads) void k_quant_col(
     }
 
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        BlockScale bs[2];
-        u32x4 rnd[2][B / 8];
+    for (int k = 0; k < 4; ++k) {
+        uint32_t yph[2][8];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            const uint32_t col = col0 + 2 * p + h;
-            uint32_t m = h ? (mw[p] >> 16) : (mw[p] & 0xFFFFu);
-            if (FMT == FMT_MX) {
-                bs[h] = mx_block_scale(m);
-            } else {
-                float s = s_t;
-                if (FMT == FMT_NV128) {
-                    uint32_t mo = dpp_max_half_mirror(dpp_max_xor2(dpp_max_xor1(m)));
-                    s = nv_outer_scale(as_f(mo << 16));
-                    if (outer && (rb & 7) == 0)
-                        outer[(size_t)col * (R >> 7) + (row0 >> 7)] = s;
-                }
-                bs[h] = nv_block_scale(as_f(m << 16), s);
-            }
-            if (scales) scales[(size_t)col * (R / B) + row0 / B] = (uint8_t)bs[h].code;
-            if (RND == RND_SR) {
-                const uint64_t call0 = ((uint64_t)col * R + row0) >> 3;
-#pragma unroll
-                for (int k = 0; k < B / 8; ++k) {
-                    const uint64_t cl = call0 + k;
-                    rnd[h][k] = philox4x32_10((uint32_t)cl, (uint32_t)(cl >> 32), 0u, 0u,
-                                              seed_lo, seed_hi);
-                }
-            }
-        }
-        uint32_t cw[2][B / 8];
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int k = 0; k < B / 8; ++k) cw[h][k] = 0u;
-        uint32_t ytw[2][B / 2];
-        float yprev[2] = {0.0f, 0.0f};
-#pragma unroll
-        for (int r = 0; r < B; ++r) {
-            float yv[2];
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                uint32_t r16 = 0;
-                if (RND == RND_SR)
-                    r16 = (rnd[h][r >> 3].v[(r >> 1) & 3] >> (16 * (r & 1))) & 0xFFFFu;
-                uint32_t code = encode_elem<FMT, RND>(seg_elem(v[r], 2 * p + h), bs[h], r16, yv[h]);
-                cw[h][r >> 3] |= code << (4 * (r & 7));
-                if (r & 1) ytw[h][r >> 1] = bf16_pair_rne(yprev[h], yv[h]);
-                yprev[h] = yv[h];
-            }
-            seg_set_pair(v[r], p, bf16_pair_rne(yv[0], yv[1]));
-        }
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const uint32_t col = col0 + 2 * p + h;
-            if (codes) {
-                uint8_t *dst = codes + (size_t)col * (R >> 1) + (row0 >> 1);
-                if constexpr (B == 16) {
-                    *reinterpret_cast<uint2 *>(dst) = make_uint2(cw[h][0], cw[h][1]);
+            const int c = 2 * k + h;
+            const uint32_t col = t.col0 + c;
+            const uint32_t amax16 = h ? (mw[k] >> 16) : (mw[k] & 0xFFFFu);
+            float so = 0.0f;
+            const BlockScale b = lane_block_scale<FMT>(amax16, ot, so);
+            if (FMT == FMT_NV128 && outer && t.rb == 0)
+                outer[(size_t)col * (R >> 7) + (t.row0 >> 7)] = so;
+            if (scales) {
+                if (FMT == FMT_MX) {
+                    if ((t.rb & 1) == 0) scales[(size_t)col * (R / B) + t.row0 / B] = (uint8_t)b.code;
                 } else {
-                    *reinterpret_cast<uint4 *>(dst) = make_uint4(cw[h][0], cw[h][1], cw[h][2], cw[h][3]);
+                    scales[(size_t)col * (R / B) + t.row0 / B] = (uint8_t)b.code;
                 }
             }
-            if (yt) {
-                uint4 *dst = yt + (((size_t)col * R + row0) >> 3);
+            u32x4 rnd[2];
+            if (RND == RND_SR) {
+                const uint64_t call0 = ((uint64_t)col * R + t.row0) >> 3;
+                rnd[0] = philox4x32_10((uint32_t)call0, (uint32_t)(call0 >> 32), 0u, 0u, seed_lo, seed_hi);
+                rnd[1] = philox4x32_10((uint32_t)(call0 + 1), (uint32_t)((call0 + 1) >> 32), 0u, 0u,
+                                       seed_lo, seed_hi);
+            }
+            uint32_t xp[8];
 #pragma unroll
-                for (int k = 0; k < B / 8; ++k)
-                    dst[k] = make_uint4(ytw[h][4 * k], ytw[h][4 * k + 1], ytw[h][4 * k + 2],
-                                        ytw[h][4 * k + 3]);
+            for (int i = 0; i < 8; ++i) xp[i] = col_pair(v[2 * i], v[2 * i + 1], c);
+            uint32_t cw[2];
+            encode_pairs<FMT, RND, 8>(xp, b, rnd, cw, yph[h]);
+            if (codes)
+                st_stream<NT>(reinterpret_cast<uint2 *>(codes + (size_t)col * (R >> 1) + (t.row0 >> 1)),
+                              make_uint2(cw[0], cw[1]));
+            if (yt) {
+                uint4 *dst = yt + (((size_t)col * R + t.row0) >> 3);
+                st_stream<NT>(&dst[0], make_uint4(yph[h][0], yph[h][1], yph[h][2], yph[h][3]));
+                st_stream<NT>(&dst[1], make_uint4(yph[h][4], yph[h][5], yph[h][6], yph[h][7]));
             }
         }
+        if (y) scatter_pairs(v, k, yph[0], yph[1]);
     }
     if (y) {
 #pragma unroll
-        for (int r = 0; r < B; ++r) y[(size_t)(row0 + r) * ldx + (col0 >> 3)] = v[r];
+        for (int r = 0; r < 16; ++r) st_stream<NT>(&y[(size_t)(t.row0 + r) * ldx + (t.col0 >> 3)], v[r]);
     }
 }
 
 // ---------------------------------------------------------------------------
 // Dequantize
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ float decode_elem(uint32_t code, float s_eff)
+template <int FMT>
+__device__ __forceinline__ float stored_s_eff(uint32_t code, float s)
 {
-    return as_f(as_u(e2m1_value(code & 7u) * s_eff) | ((code & 8u) << 28));
+    return (FMT == FMT_MX) ? e8m0_value(code) : e4m3_value(code) * s;
 }
 
 template <int FMT>
@@ -332,16 +378,13 @@ __global__ __launch_bounds__(kThreads) void k_dequant_row(
     const float s_t = (FMT == FMT_NVT) ? outer[0] : 0.0f;
     for (uint32_t c = blockIdx.x * kThreads + threadIdx.x; c < nchunks;
          c += gridDim.x * kThreads) {
-        const uint32_t packed = codes[c];
+        const uint32_t cw = codes[c];
         float s = s_t;
         if (FMT == FMT_NV128) s = outer[c >> 4];
-        const uint32_t sc = scales[FMT == FMT_MX ? (c >> 2) : (c >> 1)];
-        const float s_eff = (FMT == FMT_MX) ? e8m0_value(sc) : e4m3_value(sc) * s;
-        float yv[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) yv[j] = decode_elem((packed >> (4 * j)) & 15u, s_eff);
-        y[c] = make_uint4(bf16_pair_rne(yv[0], yv[1]), bf16_pair_rne(yv[2], yv[3]),
-                          bf16_pair_rne(yv[4], yv[5]), bf16_pair_rne(yv[6], yv[7]));
+        const float se = stored_s_eff<FMT>(scales[FMT == FMT_MX ? (c >> 2) : (c >> 1)], s);
+        uint32_t yp[4];
+        decode8<FMT>(cw, se, yp);
+        st_stream<true>(&y[c], make_uint4(yp[0], yp[1], yp[2], yp[3]));
     }
 }
 
@@ -350,57 +393,39 @@ __global__ __launch_bounds__(kThreads) void k_dequant_col(
     const uint8_t *__restrict__ codes, const uint8_t *__restrict__ scales,
     const float *__restrict__ outer, uint32_t R, uint32_t C, uint4 *__restrict__ y)
 {
-    constexpr int B = (FMT == FMT_MX) ? 32 : 16;
-    const uint32_t lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const uint32_t rb = lane & 7, cg = lane >> 3;
-    const uint32_t tiles_c = (C + 63) >> 6;           // 1-D grid: column tiles fastest
-    const uint32_t col0 = (blockIdx.x % tiles_c) * 64 + cg * 8;
-    const uint32_t row0 = (((blockIdx.x / tiles_c) * 4 + wave) * 8 + rb) * B;
-    if (col0 >= C || row0 >= R) return;
+    constexpr uint32_t B = (FMT == FMT_MX) ? 32 : 16;
+    const ColTile t = col_tile(R, C);
+    if (!t.valid) return;
     const uint32_t ldx = C >> 3;
-    uint4 v[B];
+    uint4 v[16];
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        uint32_t cw[2][B / 8];
-        float se[2];
+    for (int k = 0; k < 4; ++k) {
+        uint32_t yph[2][8];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            const uint32_t col = col0 + 2 * p + h;
-            const uint8_t *src = codes + (size_t)col * (R >> 1) + (row0 >> 1);
-            if constexpr (B == 16) {
-                uint2 t = *reinterpret_cast<const uint2 *>(src);
-                cw[h][0] = t.x;
-                cw[h][1] = t.y;
-            } else {
-                uint4 t = *reinterpret_cast<const uint4 *>(src);
-                cw[h][0] = t.x;
-                cw[h][1] = t.y;
-                cw[h][2] = t.z;
-                cw[h][3] = t.w;
-            }
-            const uint32_t sc = scales[(size_t)col * (R / B) + row0 / B];
+            const uint32_t col = t.col0 + 2 * k + h;
+            const uint2 cw =
+                *reinterpret_cast<const uint2 *>(codes + (size_t)col * (R >> 1) + (t.row0 >> 1));
             float s = 0.0f;
             if (FMT == FMT_NVT) s = outer[0];
-            if (FMT == FMT_NV128) s = outer[(size_t)col * (R >> 7) + (row0 >> 7)];
-            se[h] = (FMT == FMT_MX) ? e8m0_value(sc) : e4m3_value(sc) * s;
+            if (FMT == FMT_NV128) s = outer[(size_t)col * (R >> 7) + (t.row0 >> 7)];
+            const float se = stored_s_eff<FMT>(scales[(size_t)col * (R / B) + t.row0 / B], s);
+            decode8<FMT>(cw.x, se, &yph[h][0]);
+            decode8<FMT>(cw.y, se, &yph[h][4]);
         }
-#pragma unroll
-        for (int r = 0; r < B; ++r) {
-            float y0 = decode_elem((cw[0][r >> 3] >> (4 * (r & 7))) & 15u, se[0]);
-            float y1 = decode_elem((cw[1][r >> 3] >> (4 * (r & 7))) & 15u, se[1]);
-            seg_set_pair(v[r], p, bf16_pair_rne(y0, y1));
-        }
+        scatter_pairs(v, k, yph[0], yph[1]);
     }
 #pragma unroll
-    for (int r = 0; r < B; ++r) y[(size_t)(row0 + r) * ldx + (col0 >> 3)] = v[r];
+    for (int r = 0; r < 16; ++r) st_stream<true>(&y[(size_t)(t.row0 + r) * ldx + (t.col0 >> 3)], v[r]);
 }
 
 // ---------------------------------------------------------------------------
 // Straight-through estimator with clipping mask
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ uint32_t ste_half(uint32_t dyw, uint32_t keep_lo, uint32_t keep_hi)
+__device__ __forceinline__ uint32_t ste_word(uint32_t dyw, uint32_t keep, int bit)
 {
-    return (keep_lo ? (dyw & 0xFFFFu) : 0u) | (keep_hi ? (dyw & 0xFFFF0000u) : 0u);
+    return (((keep >> bit) & 1u) ? (dyw & 0xFFFFu) : 0u) |
+           (((keep >> (bit + 1)) & 1u) ? (dyw & 0xFFFF0000u) : 0u);
 }
 
 template <int FMT>
@@ -416,13 +441,11 @@ __global__ __launch_bounds__(kThreads) void k_ste_row(
         const uint4 d = dy[c];
         float s = s_t;
         if (FMT == FMT_NV128) s = outer[c >> 4];
-        const BlockScale b =
-            scale_from_code<FMT>(scales[FMT == FMT_MX ? (c >> 2) : (c >> 1)], s);
-        uint32_t keep[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) keep[j] = scaled_mag<FMT>(elem_bits(v, j), b) <= 6.0f;
-        dx[c] = make_uint4(ste_half(d.x, keep[0], keep[1]), ste_half(d.y, keep[2], keep[3]),
-                           ste_half(d.z, keep[4], keep[5]), ste_half(d.w, keep[6], keep[7]));
+        const BlockScale b = scale_from_code<FMT>(scales[FMT == FMT_MX ? (c >> 2) : (c >> 1)], s);
+        const uint32_t xp[4] = {v.x, v.y, v.z, v.w};
+        const uint32_t keep = keep_mask<FMT, 4>(xp, b);
+        st_stream<true>(&dx[c], make_uint4(ste_word(d.x, keep, 0), ste_word(d.y, keep, 2),
+                                           ste_word(d.z, keep, 4), ste_word(d.w, keep, 6)));
     }
 }
 
@@ -432,74 +455,81 @@ __global__ __launch_bounds__(kThreads) void k_ste_col(
     const float *__restrict__ outer, const uint4 *__restrict__ dy, uint32_t R, uint32_t C,
     uint4 *__restrict__ dx)
 {
-    constexpr int B = (FMT == FMT_MX) ? 32 : 16;
-    const uint32_t lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const uint32_t rb = lane & 7, cg = lane >> 3;
-    const uint32_t tiles_c = (C + 63) >> 6;           // 1-D grid: column tiles fastest
-    const uint32_t col0 = (blockIdx.x % tiles_c) * 64 + cg * 8;
-    const uint32_t row0 = (((blockIdx.x / tiles_c) * 4 + wave) * 8 + rb) * B;
-    if (col0 >= C || row0 >= R) return;
+    constexpr uint32_t B = (FMT == FMT_MX) ? 32 : 16;
+    const ColTile t = col_tile(R, C);
+    if (!t.valid) return;
     const uint32_t ldx = C >> 3;
     BlockScale bs[8];
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-        const uint32_t col = col0 + c;
+        const uint32_t col = t.col0 + c;
         float s = 0.0f;
         if (FMT == FMT_NVT) s = outer[0];
-        if (FMT == FMT_NV128) s = outer[(size_t)col * (R >> 7) + (row0 >> 7)];
-        bs[c] = scale_from_code<FMT>(scales[(size_t)col * (R / B) + row0 / B], s);
+        if (FMT == FMT_NV128) s = outer[(size_t)col * (R >> 7) + (t.row0 >> 7)];
+        bs[c] = scale_from_code<FMT>(scales[(size_t)col * (R / B) + t.row0 / B], s);
     }
 #pragma unroll 4
-    for (int r = 0; r < B; ++r) {
-        const size_t idx = (size_t)(row0 + r) * ldx + (col0 >> 3);
+    for (int r = 0; r < 16; ++r) {
+        const size_t idx = (size_t)(t.row0 + r) * ldx + (t.col0 >> 3);
         const uint4 v = x[idx];
         const uint4 d = dy[idx];
-        uint32_t keep[8];
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+        uint32_t keep = 0;
 #pragma unroll
-        for (int c = 0; c < 8; ++c) keep[c] = scaled_mag<FMT>(elem_bits(v, c), bs[c]) <= 6.0f;
-        dx[idx] = make_uint4(ste_half(d.x, keep[0], keep[1]), ste_half(d.y, keep[2], keep[3]),
-                             ste_half(d.z, keep[4], keep[5]), ste_half(d.w, keep[6], keep[7]));
+        for (int c = 0; c < 8; ++c) {
+            const uint32_t xb = (c & 1) ? hi_bits(w[c >> 1]) : lo_bits(w[c >> 1]);
+            keep |= (scaled_mag<FMT>(xb, bs[c]) <= 6.0f ? 1u : 0u) << c;
+        }
+        st_stream<true>(&dx[idx], make_uint4(ste_word(d.x, keep, 0), ste_word(d.y, keep, 2),
+                                             ste_word(d.z, keep, 4), ste_word(d.w, keep, 6)));
     }
 }
 
 // ---------------------------------------------------------------------------
 // launch helpers
 // ---------------------------------------------------------------------------
-uint32_t row_grid(uint64_t nchunks, uint32_t per_block)
+uint32_t row_grid(uint64_t nseg, uint32_t per_block)
 {
-    uint64_t g = (nchunks + per_block - 1) / per_block;
+    uint64_t g = (nseg + per_block - 1) / per_block;
     if (g > kRowGridCap) g = kRowGridCap;
     if (g == 0) g = 1;
     return (uint32_t)g;
 }
 
-// Column-axis grid: one workgroup per 64-column x (4 waves x 8 blocks) tile.
-dim3 col_grid(int64_t R, int64_t C, int B)
+// Column-axis grid: one workgroup per 64-column x 512-row tile.
+dim3 col_grid(int64_t R, int64_t C)
 {
     uint64_t gx = (uint64_t)((C + 63) / 64);
-    uint64_t gy = (uint64_t)((R + 32 * B - 1) / (32 * B));
+    uint64_t gy = (uint64_t)((R + 511) / 512);
     return dim3((uint32_t)(gx * gy), 1, 1);
+}
+
+template <int FMT, int RND, bool NT>
+hipError_t quant_dispatch_nt(const fqimpl::QuantArgs &a, uint32_t npart, hipStream_t st)
+{
+    const uint32_t slo = (uint32_t)a.seed, shi = (uint32_t)(a.seed >> 32);
+    const uint32_t *parts = a.partials;
+    if (!a.col) {
+        constexpr int MAP = (RND == RND_SR) ? 0 : 1;
+        const uint64_t nunits = (uint64_t)a.R * a.C / (MAP == 1 ? 8 : 16);
+        hipLaunchKernelGGL((k_quant_row<FMT, RND, MAP, NT>), dim3(row_grid(nunits, kThreads)),
+                           dim3(kThreads), 0, st, (const uint4 *)a.x, (uint32_t)nunits,
+                           (uint4 *)a.y, a.codes, (uint8_t *)a.scales, a.outer, parts, npart,
+                           slo, shi);
+    } else {
+        hipLaunchKernelGGL((k_quant_col<FMT, RND, NT>), col_grid(a.R, a.C), dim3(kThreads), 0,
+                           st, (const uint4 *)a.x, (uint32_t)a.R, (uint32_t)a.C, (uint4 *)a.y,
+                           (uint4 *)a.yt, (uint8_t *)a.codes, (uint8_t *)a.scales, a.outer,
+                           parts, npart, slo, shi);
+    }
+    return hipGetLastError();
 }
 
 template <int FMT, int RND>
 hipError_t quant_dispatch(const fqimpl::QuantArgs &a, uint32_t npart, hipStream_t st)
 {
-    const uint32_t slo = (uint32_t)a.seed, shi = (uint32_t)(a.seed >> 32);
-    const uint32_t *parts = a.partials;
-    if (!a.col) {
-        const uint64_t nchunks = (uint64_t)a.R * a.C / 8;
-        hipLaunchKernelGGL((k_quant_row<FMT, RND>), dim3(row_grid(nchunks, kThreads * 2)),
-                           dim3(kThreads), 0, st, (const uint4 *)a.x, (uint32_t)nchunks,
-                           (uint4 *)a.y, (uint32_t *)a.codes, (uint8_t *)a.scales, a.outer,
-                           parts, npart, slo, shi);
-    } else {
-        const int B = (FMT == FMT_MX) ? 32 : 16;
-        hipLaunchKernelGGL((k_quant_col<FMT, RND>), col_grid(a.R, a.C, B), dim3(kThreads), 0,
-                           st, (const uint4 *)a.x, (uint32_t)a.R, (uint32_t)a.C, (uint4 *)a.y,
-                           (uint4 *)a.yt, (uint8_t *)a.codes, (uint8_t *)a.scales, a.outer, parts, npart,
-                           slo, shi);
-    }
-    return hipGetLastError();
+    return a.cached_outputs ? quant_dispatch_nt<FMT, RND, false>(a, npart, st)
+                            : quant_dispatch_nt<FMT, RND, true>(a, npart, st);
 }
 
 }  // namespace
@@ -539,14 +569,13 @@ static hipError_t dequant_dispatch(int col, const void *codes, const void *scale
 {
     if (!col) {
         const uint64_t nchunks = (uint64_t)R * C / 8;
-        hipLaunchKernelGGL(k_dequant_row<FMT>, dim3(row_grid(nchunks, kThreads)),
-                           dim3(kThreads), 0, st, (const uint32_t *)codes,
-                           (const uint8_t *)scales, outer, (uint32_t)nchunks, (uint4 *)y);
+        hipLaunchKernelGGL(k_dequant_row<FMT>, dim3(row_grid(nchunks, kThreads)), dim3(kThreads),
+                           0, st, (const uint32_t *)codes, (const uint8_t *)scales, outer,
+                           (uint32_t)nchunks, (uint4 *)y);
     } else {
-        const int B = (FMT == FMT_MX) ? 32 : 16;
-        hipLaunchKernelGGL(k_dequant_col<FMT>, col_grid(R, C, B), dim3(kThreads), 0, st,
-                           (const uint8_t *)codes, (const uint8_t *)scales, outer,
-                           (uint32_t)R, (uint32_t)C, (uint4 *)y);
+        hipLaunchKernelGGL(k_dequant_col<FMT>, col_grid(R, C), dim3(kThreads), 0, st,
+                           (const uint8_t *)codes, (const uint8_t *)scales, outer, (uint32_t)R,
+                           (uint32_t)C, (uint4 *)y);
     }
     return hipGetLastError();
 }
@@ -570,12 +599,11 @@ static hipError_t ste_dispatch(int col, const void *x, const void *scales, const
 {
     if (!col) {
         const uint64_t nchunks = (uint64_t)R * C / 8;
-        hipLaunchKernelGGL(k_ste_row<FMT>, dim3(row_grid(nchunks, kThreads)), dim3(kThreads),
-                           0, st, (const uint4 *)x, (const uint8_t *)scales, outer,
+        hipLaunchKernelGGL(k_ste_row<FMT>, dim3(row_grid(nchunks, kThreads)), dim3(kThreads), 0,
+                           st, (const uint4 *)x, (const uint8_t *)scales, outer,
                            (const uint4 *)dy, (uint32_t)nchunks, (uint4 *)dx);
     } else {
-        const int B = (FMT == FMT_MX) ? 32 : 16;
-        hipLaunchKernelGGL(k_ste_col<FMT>, col_grid(R, C, B), dim3(kThreads), 0, st,
+        hipLaunchKernelGGL(k_ste_col<FMT>, col_grid(R, C), dim3(kThreads), 0, st,
                            (const uint4 *)x, (const uint8_t *)scales, outer, (const uint4 *)dy,
                            (uint32_t)R, (uint32_t)C, (uint4 *)dx);
     }
