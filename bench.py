@@ -200,6 +200,24 @@ def main():
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": load_traffic(dom)}
 
+    # ---------------- copy yardstick (achievable bandwidth) ----------------
+    # torch's device copy of one 16384x4096 BF16 tensor: 2 B read + 2 B written
+    # per element.  Not part of the library; it is the reference the roofline
+    # fractions and the HBM byte counters are compared against.
+    log("bench: copy yardstick")
+    for i in range(NBUF):
+        dxs[i].copy_(xs[i])
+    torch.cuda.synchronize()
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record()
+    for s in range(10):
+        dxs[s % NBUF].copy_(xs[s % NBUF])
+    c1.record()
+    torch.cuda.synchronize()
+    copy_ms = c0.elapsed_time(c1) / 10
+    copy = {"op": "torch copy_ of 16384x4096 bf16", "bytes": 4 * n, "ms": round(copy_ms, 5),
+            "GBps": round(4 * n / (copy_ms * 1e-3) / 1e9, 1)}
+
     # ---------------- QAT linear ----------------
     qlin = None
     if not args.only:
@@ -264,6 +282,7 @@ def main():
                    "rows": ROWS, "cols": COLS, "ops": ops, "step_bytes": step_bytes,
                    "frac_hbm_step": round(value / HBM_PEAK_GBS, 4)},
         "roofline": roofline,
+        "copy_yardstick": copy,
         "cpu_baseline": cpu,
         "kernels": kernels,
         "qlinear": qlin,
