@@ -67,6 +67,7 @@ __device__ __forceinline__ void st_stream(uint32_t *p, uint32_t v)
 // workgroup.  Consumers reduce the partials themselves, so no zero-filled
 // accumulator and no atomics are needed.
 // ---------------------------------------------------------------------------
+template <int NT>
 __device__ __forceinline__ uint32_t block_reduce_max(uint32_t m, uint32_t *red)
 {
 #pragma unroll
@@ -74,28 +75,36 @@ __device__ __forceinline__ uint32_t block_reduce_max(uint32_t m, uint32_t *red)
         m = max(m, (uint32_t)__shfl_xor((int)m, off));
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
     __syncthreads();
-    m = max(max(red[0], red[1]), max(red[2], red[3]));
+    m = red[0];
+#pragma unroll
+    for (int w = 1; w < NT / 64; ++w) m = max(m, red[w]);
     return m;
 }
 
-__global__ __launch_bounds__(kThreads) void k_absmax(const uint4 *__restrict__ x,
-                                                     uint32_t nchunks,
-                                                     uint32_t *__restrict__ partials)
+// One workgroup of kAbsmaxThreads per partial; at most kAbsmaxGrid partials,
+// so that every quantizer workgroup reduces at most 1 KB of them.
+constexpr int kAbsmaxThreads = 1024;
+constexpr uint32_t kAbsmaxGrid = 256;
+static_assert(kAbsmaxGrid <= fqimpl::kAbsmaxPartials, "partials fit the workspace");
+
+__global__ __launch_bounds__(kAbsmaxThreads) void k_absmax(const uint4 *__restrict__ x,
+                                                           uint32_t nchunks,
+                                                           uint32_t *__restrict__ partials)
 {
-    __shared__ uint32_t red[4];
+    __shared__ uint32_t red[kAbsmaxThreads / 64];
     uint32_t m = 0;
-    const uint32_t stride = gridDim.x * kThreads * 4;
-    for (uint32_t base = blockIdx.x * kThreads * 4; base < nchunks; base += stride) {
+    const uint32_t stride = gridDim.x * kAbsmaxThreads * 4;
+    for (uint32_t base = blockIdx.x * kAbsmaxThreads * 4; base < nchunks; base += stride) {
         uint4 v[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            uint32_t c = base + u * kThreads + threadIdx.x;
+            uint32_t c = base + u * kAbsmaxThreads + threadIdx.x;
             v[u] = c < nchunks ? x[c] : make_uint4(0, 0, 0, 0);
         }
 #pragma unroll
         for (int u = 0; u < 4; ++u) m = max(m, absmax_bits_8(v[u]));
     }
-    m = block_reduce_max(m, red);
+    m = block_reduce_max<kAbsmaxThreads>(m, red);
     if (threadIdx.x == 0) partials[blockIdx.x] = m;
 }
 
@@ -103,10 +112,10 @@ __global__ __launch_bounds__(kThreads) void k_absmax(const uint4 *__restrict__ x
 __device__ __forceinline__ OuterScale tensor_scale(const uint32_t *__restrict__ partials,
                                                    uint32_t npart)
 {
-    __shared__ uint32_t red[4];
+    __shared__ uint32_t red[kThreads / 64];
     uint32_t m = 0;
     for (uint32_t i = threadIdx.x; i < npart; i += kThreads) m = max(m, partials[i]);
-    m = block_reduce_max(m, red);
+    m = block_reduce_max<kThreads>(m, red);
     return make_outer(as_f(m << 16));
 }
 
@@ -256,13 +265,6 @@ __device__ __forceinline__ ColTile col_tile(uint32_t R, uint32_t C)
     return t;
 }
 
-// Packed BF16 pair of column c (0..7) from two row segments (rows r, r+1).
-__device__ __forceinline__ uint32_t col_pair(const uint4 &a, const uint4 &b, int c)
-{
-    const uint32_t wa = (c >> 1) == 0 ? a.x : (c >> 1) == 1 ? a.y : (c >> 1) == 2 ? a.z : a.w;
-    const uint32_t wb = (c >> 1) == 0 ? b.x : (c >> 1) == 1 ? b.y : (c >> 1) == 2 ? b.z : b.w;
-    return (c & 1) ? ((wa >> 16) | (wb & 0xFFFF0000u)) : ((wa & 0xFFFFu) | (wb << 16));
-}
 __device__ __forceinline__ void seg_set_word(uint4 &v, int k, uint32_t w)
 {
     if (k == 0) v.x = w;
@@ -282,6 +284,29 @@ __device__ __forceinline__ void scatter_pairs(uint4 (&v)[16], int k, const uint3
     }
 }
 
+// Quantizer tile: a lane holds 8 columns of 16 consecutive rows, eight lanes
+// stack 128 rows, a wave spans 64 columns, and the four waves of a workgroup
+// sit side by side along the columns (256 columns x 128 rows per workgroup):
+// measured faster than stacking them along the rows.
+constexpr uint32_t kColTileC = 256, kColTileR = 128;
+
+__device__ __forceinline__ uint32_t vword(const uint4 &v, int k)
+{
+    return k == 0 ? v.x : k == 1 ? v.y : k == 2 ? v.z : v.w;
+}
+
+__device__ __forceinline__ ColTile quant_col_tile(uint32_t R, uint32_t C)
+{
+    const uint32_t lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const uint32_t tiles_c = (C + kColTileC - 1) / kColTileC;
+    ColTile t;
+    t.rb = lane & 7;
+    t.col0 = (blockIdx.x % tiles_c) * kColTileC + wave * 64 + (lane >> 3) * 8;
+    t.row0 = (blockIdx.x / tiles_c) * kColTileR + t.rb * 16;
+    t.valid = t.col0 < C && t.row0 < R;
+    return t;
+}
+
 template <int FMT, int RND, bool NT>
 __global__ __launch_bounds__(kThreads) void k_quant_col(
     const uint4 *__restrict__ x, uint32_t R, uint32_t C, uint4 *__restrict__ y,
@@ -290,36 +315,37 @@ __global__ __launch_bounds__(kThreads) void k_quant_col(
     uint32_t seed_lo, uint32_t seed_hi)
 {
     constexpr uint32_t B = (FMT == FMT_MX) ? 32 : 16;
+    constexpr int NW = 4;                    // packed words per row segment
+    typedef uint4 VT;
     OuterScale ot = {0.0f, 0.0f};
     if (FMT == FMT_NVT) {
         ot = tensor_scale(partials, npart);
         if (outer && blockIdx.x == 0 && threadIdx.x == 0) outer[0] = ot.s;
     }
-    const ColTile t = col_tile(R, C);
+    const ColTile t = quant_col_tile(R, C);
     if (!t.valid) return;     // MXFP4 pairs and double-block groups leave together
     const uint32_t ldx = C >> 3;   // 16-byte segments per row
+    const VT *__restrict__ xv = x;
 
-    uint4 v[16];
+    VT v[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) v[r] = x[(size_t)(t.row0 + r) * ldx + (t.col0 >> 3)];
+    for (int r = 0; r < 16; ++r) v[r] = xv[(size_t)(t.row0 + r) * ldx + (t.col0 >> 3)];
 
     // per-column maxima of the lane's 16 rows: packed u16 max
-    uint32_t mw[4] = {0u, 0u, 0u, 0u};
+    uint32_t mw[NW];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        mw[0] = pkmax_u16(mw[0], v[r].x & 0x7FFF7FFFu);
-        mw[1] = pkmax_u16(mw[1], v[r].y & 0x7FFF7FFFu);
-        mw[2] = pkmax_u16(mw[2], v[r].z & 0x7FFF7FFFu);
-        mw[3] = pkmax_u16(mw[3], v[r].w & 0x7FFF7FFFu);
-    }
+    for (int k = 0; k < NW; ++k) mw[k] = 0u;
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+#pragma unroll
+        for (int k = 0; k < NW; ++k) mw[k] = pkmax_u16(mw[k], vword(v[r], k) & 0x7FFF7FFFu);
 
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
+    for (int k = 0; k < NW; ++k) {
         uint32_t yph[2][8];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            const int c = 2 * k + h;
-            const uint32_t col = t.col0 + c;
+            const uint32_t col = t.col0 + 2 * k + h;
             const uint32_t amax16 = h ? (mw[k] >> 16) : (mw[k] & 0xFFFFu);
             float so = 0.0f;
             const BlockScale b = lane_block_scale<FMT>(amax16, ot, so);
@@ -339,9 +365,13 @@ __global__ __launch_bounds__(kThreads) void k_quant_col(
                 rnd[1] = philox4x32_10((uint32_t)(call0 + 1), (uint32_t)((call0 + 1) >> 32), 0u, 0u,
                                        seed_lo, seed_hi);
             }
+            // column pairs along rows: element 2i in the low half of xp[i]
             uint32_t xp[8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) xp[i] = col_pair(v[2 * i], v[2 * i + 1], c);
+            for (int i = 0; i < 8; ++i) {
+                const uint32_t wa = vword(v[2 * i], k), wb = vword(v[2 * i + 1], k);
+                xp[i] = h ? ((wa >> 16) | (wb & 0xFFFF0000u)) : ((wa & 0xFFFFu) | (wb << 16));
+            }
             uint32_t cw[2];
             encode_pairs<FMT, RND, 8>(xp, b, rnd, cw, yph[h]);
             if (codes)
@@ -353,7 +383,14 @@ __global__ __launch_bounds__(kThreads) void k_quant_col(
                 st_stream<NT>(&dst[1], make_uint4(yph[h][4], yph[h][5], yph[h][6], yph[h][7]));
             }
         }
-        if (y) scatter_pairs(v, k, yph[0], yph[1]);
+        if (y) {
+            // columns 2k, 2k+1 back into the row segments
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                seg_set_word(v[2 * i], k, (yph[0][i] & 0xFFFFu) | (yph[1][i] << 16));
+                seg_set_word(v[2 * i + 1], k, (yph[0][i] >> 16) | (yph[1][i] & 0xFFFF0000u));
+            }
+        }
     }
     if (y) {
 #pragma unroll
@@ -504,6 +541,14 @@ dim3 col_grid(int64_t R, int64_t C)
     return dim3((uint32_t)(gx * gy), 1, 1);
 }
 
+// Column-axis quantizer grid: one workgroup per kColTileC x kColTileR tile.
+dim3 quant_col_grid(int64_t R, int64_t C)
+{
+    uint64_t gx = (uint64_t)((C + kColTileC - 1) / kColTileC);
+    uint64_t gy = (uint64_t)((R + kColTileR - 1) / kColTileR);
+    return dim3((uint32_t)(gx * gy), 1, 1);
+}
+
 template <int FMT, int RND, bool NT>
 hipError_t quant_dispatch_nt(const fqimpl::QuantArgs &a, uint32_t npart, hipStream_t st)
 {
@@ -517,7 +562,7 @@ hipError_t quant_dispatch_nt(const fqimpl::QuantArgs &a, uint32_t npart, hipStre
                            (uint4 *)a.y, a.codes, (uint8_t *)a.scales, a.outer, parts, npart,
                            slo, shi);
     } else {
-        hipLaunchKernelGGL((k_quant_col<FMT, RND, NT>), col_grid(a.R, a.C), dim3(kThreads), 0,
+        hipLaunchKernelGGL((k_quant_col<FMT, RND, NT>), quant_col_grid(a.R, a.C), dim3(kThreads), 0,
                            st, (const uint4 *)a.x, (uint32_t)a.R, (uint32_t)a.C, (uint4 *)a.y,
                            (uint4 *)a.yt, (uint8_t *)a.codes, (uint8_t *)a.scales, a.outer,
                            parts, npart, slo, shi);
@@ -540,10 +585,10 @@ hipError_t launch_absmax(const void *x, int64_t n_elems, uint32_t *partials,
                          uint32_t *npart_out, hipStream_t stream)
 {
     const uint64_t nchunks = (uint64_t)n_elems / 8;
-    uint64_t g = (nchunks + kThreads * 4 - 1) / (kThreads * 4);
-    if (g > kAbsmaxPartials) g = kAbsmaxPartials;
+    uint64_t g = (nchunks + kAbsmaxThreads * 4 - 1) / (kAbsmaxThreads * 4);
+    if (g > kAbsmaxGrid) g = kAbsmaxGrid;
     if (g == 0) g = 1;
-    hipLaunchKernelGGL(k_absmax, dim3((uint32_t)g), dim3(kThreads), 0, stream,
+    hipLaunchKernelGGL(k_absmax, dim3((uint32_t)g), dim3(kAbsmaxThreads), 0, stream,
                        (const uint4 *)x, (uint32_t)nchunks, partials);
     *npart_out = (uint32_t)g;
     return hipGetLastError();
