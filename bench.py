@@ -20,8 +20,10 @@ written once) over the step time, in GB/s.  Inputs are resident in HBM; the
 step rotates over three input/output buffer sets (~1.9 GB) so no launch
 finds its operands in the 256 MB Infinity Cache.
 
-The QAT linear forward (X 8192x2880 @ W 2880x5760, both NVFP4 RNE) is timed
-after the step and reported in TFLOP/s under "qlinear".  The CPU oracle is
+The QAT linear forward (X 8192x2880 @ W 2880x5760, both NVFP4 RNE) and its
+backward (dY 8192x5760, gradient operands NVFP4 double block with stochastic
+rounding; two products) are timed after the step and reported in TFLOP/s under
+"qlinear" and "qlinear_bwd".  The CPU oracle is
 timed on a bounded sample (the first rows of the same tensors) for
 "cpu_baseline".
 """
@@ -246,6 +248,34 @@ def main():
                 "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": BF16_PEAK_TFLOPS,
                              "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4)}}
 
+    # ---------------- QAT linear backward ----------------
+    qbwd = None
+    if not args.only:
+        log("bench: qlinear backward")
+        dym = wl.normal_bf16((M, N), 1e-3, 8)
+        dyq = to_dev(dym)
+        dgd = fq.fq_desc_nvfp4(outer=fq.FQ_OUTER_BLOCK128, rounding=fq.FQ_ROUND_SR, seed=1234)
+        bws = fq.qlinear_bwd_workspace(dxd, dwd, dgd, M, Kd, N, dev)
+        gx = torch.empty((M, Kd), dtype=torch.bfloat16, device=dev)
+        gw = torch.empty((Kd, N), dtype=torch.bfloat16, device=dev)
+        for _ in range(3):
+            fq.fq_qlinear_bwd(dxd, dwd, dgd, xq, wq, dyq, dx=gx, dw=gw, ws=bws)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.qlinear_iters):
+            fq.fq_qlinear_bwd(dxd, dwd, dgd, xq, wq, dyq, dx=gx, dw=gw, ws=bws)
+        e1.record()
+        torch.cuda.synchronize()
+        bms = e0.elapsed_time(e1) / args.qlinear_iters
+        tfb = 4.0 * M * Kd * N / (bms * 1e-3) / 1e12
+        qbwd = {"workload": "dY 8192x5760 N(0,1e-6) through the linear above; dX and dW "
+                            "products on NVFP4 double-block SR operands (seed 1234)",
+                "ms": round(bms, 4), "TFLOPs": round(tfb, 1),
+                "roofline": {"bound": "mfma", "achieved": round(tfb, 1),
+                             "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                             "frac": round(tfb / BF16_PEAK_TFLOPS, 4)}}
+
     # ---------------- CPU oracle baseline ----------------
     cpu = None
     if not args.no_cpu_baseline and not args.only:
@@ -286,6 +316,7 @@ def main():
         "cpu_baseline": cpu,
         "kernels": kernels,
         "qlinear": qlin,
+        "qlinear_bwd": qbwd,
     }
     print(json.dumps(out), flush=True)
 

@@ -28,7 +28,8 @@ FQ_AXIS_ROW, FQ_AXIS_COL = 0, 1
 EXPORTED = (
     "fq_desc_mxfp4", "fq_desc_nvfp4", "fq_workspace_size", "fq_quantize",
     "fq_dequantize", "fq_fake_quant", "fq_ste_backward",
-    "fq_qlinear_workspace_size", "fq_qlinear_fwd", "fq_status_string",
+    "fq_qlinear_workspace_size", "fq_qlinear_fwd", "fq_qlinear_bwd_workspace_size",
+    "fq_qlinear_bwd", "fq_status_string",
     "fq_last_error", "fq_version",
 )
 
@@ -88,6 +89,10 @@ def lib() -> ctypes.CDLL:
         L.fq_qlinear_workspace_size.restype = sz
         L.fq_qlinear_fwd.argtypes = [dp, dp, vp, vp, i64, i64, i64, vp, vp, sz, vp]
         L.fq_qlinear_fwd.restype = ctypes.c_int
+        L.fq_qlinear_bwd_workspace_size.argtypes = [dp, dp, dp, i64, i64, i64]
+        L.fq_qlinear_bwd_workspace_size.restype = sz
+        L.fq_qlinear_bwd.argtypes = [dp, dp, dp, vp, vp, vp, i64, i64, i64, vp, vp, vp, sz, vp]
+        L.fq_qlinear_bwd.restype = ctypes.c_int
         L.fq_status_string.argtypes = [ctypes.c_int]
         L.fq_status_string.restype = ctypes.c_char_p
         L.fq_last_error.argtypes = []
@@ -267,6 +272,34 @@ def fq_qlinear_fwd(desc_x: FqDesc, desc_w: FqDesc, x, w, y=None, ws=None, stream
     _check(lib().fq_qlinear_fwd(ctypes.byref(desc_x), ctypes.byref(desc_w), _ptr(x), _ptr(w),
                                 M, K, N, _ptr(y), _ptr(ws), ws.numel(), _stream(stream)))
     return y
+
+
+def qlinear_bwd_workspace(desc_x: FqDesc, desc_w: FqDesc, desc_g: FqDesc, M: int, K: int,
+                          N: int, device):
+    torch = _torch()
+    n = lib().fq_qlinear_bwd_workspace_size(ctypes.byref(desc_x), ctypes.byref(desc_w),
+                                            ctypes.byref(desc_g), M, K, N)
+    return torch.empty((n,), dtype=torch.uint8, device=device)
+
+
+def fq_qlinear_bwd(desc_x: FqDesc, desc_w: FqDesc, desc_g: FqDesc, x, w, dy, dx=None, dw=None,
+                   ws=None, stream=None):
+    """(dX [M, K], dW [K, N]) of Y = FQ(X) @ FQ(W) for the upstream gradient dY [M, N]."""
+    torch = _torch()
+    M, K = x.shape
+    K2, N = w.shape
+    if K2 != K or tuple(dy.shape) != (M, N):
+        raise ValueError(f"shapes differ: x {tuple(x.shape)}, w {tuple(w.shape)}, dy {tuple(dy.shape)}")
+    if dx is None:
+        dx = torch.empty((M, K), dtype=torch.bfloat16, device=x.device)
+    if dw is None:
+        dw = torch.empty((K, N), dtype=torch.bfloat16, device=x.device)
+    if ws is None:
+        ws = qlinear_bwd_workspace(desc_x, desc_w, desc_g, M, K, N, x.device)
+    _check(lib().fq_qlinear_bwd(ctypes.byref(desc_x), ctypes.byref(desc_w), ctypes.byref(desc_g),
+                                _ptr(x), _ptr(w), _ptr(dy), M, K, N, _ptr(dx), _ptr(dw), _ptr(ws),
+                                ws.numel(), _stream(stream)))
+    return dx, dw
 
 
 def version() -> str:

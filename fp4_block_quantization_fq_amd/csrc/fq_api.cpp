@@ -344,6 +344,156 @@ fq_status fq_qlinear_fwd(const fq_desc *desc_x, const fq_desc *desc_w, const voi
                          "gemm launch");
 }
 
+// qlinear backward workspace regions, in order (each rounded up to 256 B).
+struct BwdLayout {
+    size_t xhat, xsc, xout, what, wsc, wout, dyq_n, wq_n, xq_mt, dyq_mt, dx_raw, dw_raw, parts,
+        total;
+};
+
+static BwdLayout bwd_layout(const Fmt &fx, const Fmt &fw, int64_t M, int64_t K, int64_t N)
+{
+    BwdLayout L;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = off;
+        off += round256(bytes);
+        return at;
+    };
+    const size_t mk = (size_t)M * K, kn = (size_t)K * N, mn = (size_t)M * N;
+    L.xhat = take(mk * 2);
+    L.xsc = take(mk / fx.B);
+    L.xout = take(fx.fmt == fqimpl::FMT_NV128 ? mk / 128 * 4 : 4);
+    L.what = take(kn * 2);
+    L.wsc = take(kn / fw.B);
+    L.wout = take(fw.fmt == fqimpl::FMT_NV128 ? kn / 128 * 4 : 4);
+    L.dyq_n = take(mn * 2);
+    L.wq_n = take(kn * 2);
+    L.xq_mt = take(mk * 2);
+    L.dyq_mt = take(mn * 2);
+    L.dx_raw = take(mk * 2);
+    L.dw_raw = take(kn * 2);
+    L.parts = take(fqimpl::kAbsmaxPartials * sizeof(uint32_t));
+    L.total = off;
+    return L;
+}
+
+size_t fq_qlinear_bwd_workspace_size(const fq_desc *desc_x, const fq_desc *desc_w,
+                                     const fq_desc *desc_g, int64_t M, int64_t K, int64_t N)
+{
+    Fmt fx, fw, fg;
+    if (check_desc(desc_x, &fx, "desc_x") != FQ_OK || check_desc(desc_w, &fw, "desc_w") != FQ_OK ||
+        check_desc(desc_g, &fg, "desc_g") != FQ_OK)
+        return 0;
+    if (M < 1 || K < 1 || N < 1 || M > kMaxElems || K > kMaxElems || N > kMaxElems) return 0;
+    return bwd_layout(fx, fw, M, K, N).total;
+}
+
+// One quantizer pass of the backward: src [R, C] along rows (col = false,
+// output y [R, C]) or along columns (col = true, output the transpose
+// yt [C, R]); optional scales/outer in the pass's own layout.
+static fq_status bwd_quant(const Fmt &f, const fq_desc *d, uint64_t seed, bool col,
+                           const void *src, int64_t R, int64_t C, void *y, void *yt,
+                           void *scales, float *outer, uint32_t *parts, hipStream_t st)
+{
+    fqimpl::QuantArgs a;
+    a.fmt = f.fmt;
+    a.sr = d->rounding == FQ_ROUND_SR;
+    a.col = col ? 1 : 0;
+    a.seed = seed;
+    a.x = src;
+    a.R = R;
+    a.C = C;
+    a.y = y;
+    a.yt = yt;
+    a.codes = nullptr;
+    a.scales = scales;
+    a.outer = (f.fmt == fqimpl::FMT_MX) ? nullptr : outer;
+    a.partials = parts;
+    a.cached_outputs = true;
+    uint32_t npart = 0;
+    if (f.fmt == fqimpl::FMT_NVT) {
+        hipError_t e = fqimpl::launch_absmax(src, R * C, parts, &npart, st);
+        if (e != hipSuccess) return device_status(e, "tensor absmax launch");
+    }
+    return device_status(fqimpl::launch_quant(a, npart, st), "quantize launch");
+}
+
+fq_status fq_qlinear_bwd(const fq_desc *desc_x, const fq_desc *desc_w, const fq_desc *desc_g,
+                         const void *x_bf16, const void *w_bf16, const void *dy_bf16, int64_t M,
+                         int64_t K, int64_t N, void *dx_bf16, void *dw_bf16, void *ws,
+                         size_t ws_bytes, void *stream)
+{
+    Fmt fx, fw, fg;
+    FQ_TRY(check_desc(desc_x, &fx, "desc_x"));
+    FQ_TRY(check_desc(desc_w, &fw, "desc_w"));
+    FQ_TRY(check_desc(desc_g, &fg, "desc_g"));
+    if (desc_x->axis != FQ_AXIS_ROW)
+        return fail(FQ_ERR_DESC, "desc_x->axis must be FQ_AXIS_ROW (groups along K)");
+    if (desc_w->axis != FQ_AXIS_COL)
+        return fail(FQ_ERR_DESC, "desc_w->axis must be FQ_AXIS_COL (groups along K)");
+    if (M < 1 || K < 1 || N < 1)
+        return fail(FQ_ERR_SHAPE, "M=%lld K=%lld N=%lld must be >= 1", (long long)M,
+                    (long long)K, (long long)N);
+    // forward quantizations (X along K, W along K) and the four backward ones
+    FQ_TRY(check_shape(fx, FQ_AXIS_ROW, M, K));
+    FQ_TRY(check_shape(fw, FQ_AXIS_COL, K, N));
+    FQ_TRY(check_shape(fg, FQ_AXIS_ROW, M, N));     // dY along N
+    FQ_TRY(check_shape(fg, FQ_AXIS_ROW, K, N));     // W_hat along N
+    FQ_TRY(check_shape(fg, FQ_AXIS_COL, M, K));     // X_hat along M
+    FQ_TRY(check_shape(fg, FQ_AXIS_COL, M, N));     // dY along M
+    if (M % 64 != 0 || N % 64 != 0)
+        return fail(FQ_ERR_SHAPE, "M=%lld and N=%lld must be multiples of 64 (contractions)",
+                    (long long)M, (long long)N);
+    if (M * N > kMaxElems)
+        return fail(FQ_ERR_SHAPE, "M*N exceeds 2^34 elements");
+    FQ_TRY(check_ptr(x_bf16, "x", true));
+    FQ_TRY(check_ptr(w_bf16, "w", true));
+    FQ_TRY(check_ptr(dy_bf16, "dy", true));
+    FQ_TRY(check_ptr(dx_bf16, "dx", true));
+    FQ_TRY(check_ptr(dw_bf16, "dw", true));
+    FQ_TRY(check_ptr(ws, "ws", true));
+    const BwdLayout L = bwd_layout(fx, fw, M, K, N);
+    if (ws_bytes < L.total)
+        return fail(FQ_ERR_WORKSPACE, "workspace %zu bytes < %zu required", ws_bytes, L.total);
+
+    char *b = (char *)ws;
+    uint32_t *parts = (uint32_t *)(b + L.parts);
+    hipStream_t st = (hipStream_t)stream;
+    const uint64_t sg = desc_g->seed;
+
+    // the forward's operands and their scales: X_hat [M, K], W_hat [K, N]
+    FQ_TRY(bwd_quant(fx, desc_x, desc_x->seed, false, x_bf16, M, K, b + L.xhat, nullptr,
+                     b + L.xsc, (float *)(b + L.xout), parts, st));
+    FQ_TRY(bwd_quant(fw, desc_w, desc_w->seed, true, w_bf16, K, N, b + L.what, nullptr,
+                     b + L.wsc, (float *)(b + L.wout), parts, st));
+    // dX = STE_X(Q(dY) . Q(W_hat)^T), both quantized along N
+    FQ_TRY(bwd_quant(fg, desc_g, sg + 0, false, dy_bf16, M, N, b + L.dyq_n, nullptr, nullptr,
+                     nullptr, parts, st));
+    FQ_TRY(bwd_quant(fg, desc_g, sg + 1, false, b + L.what, K, N, b + L.wq_n, nullptr, nullptr,
+                     nullptr, parts, st));
+    {
+        hipError_t e = fqimpl::launch_gemm_bf16_nt(b + L.dyq_n, b + L.wq_n, b + L.dx_raw, M, K, N, st);
+        if (e != hipSuccess) return device_status(e, "gemm launch");
+        e = fqimpl::launch_ste(fx.fmt, 0, x_bf16, b + L.xsc,
+                               fx.fmt == fqimpl::FMT_MX ? nullptr : (const float *)(b + L.xout),
+                               b + L.dx_raw, M, K, dx_bf16, st);
+        if (e != hipSuccess) return device_status(e, "ste launch");
+    }
+    // dW = STE_W(Q(X_hat)^T . Q(dY)), both quantized along M, written transposed
+    FQ_TRY(bwd_quant(fg, desc_g, sg + 2, true, b + L.xhat, M, K, nullptr, b + L.xq_mt, nullptr,
+                     nullptr, parts, st));
+    FQ_TRY(bwd_quant(fg, desc_g, sg + 3, true, dy_bf16, M, N, nullptr, b + L.dyq_mt, nullptr,
+                     nullptr, parts, st));
+    {
+        hipError_t e = fqimpl::launch_gemm_bf16_nt(b + L.xq_mt, b + L.dyq_mt, b + L.dw_raw, K, N, M, st);
+        if (e != hipSuccess) return device_status(e, "gemm launch");
+        e = fqimpl::launch_ste(fw.fmt, 1, w_bf16, b + L.wsc,
+                               fw.fmt == fqimpl::FMT_MX ? nullptr : (const float *)(b + L.wout),
+                               b + L.dw_raw, K, N, dw_bf16, st);
+        return device_status(e, "ste launch");
+    }
+}
+
 const char *fq_status_string(fq_status s)
 {
     switch (s) {

@@ -182,6 +182,40 @@ fq_status fq_qlinear_fwd(const fq_desc *desc_x, const fq_desc *desc_w,
                          int64_t K, int64_t N, void *y_bf16, void *ws,
                          size_t ws_bytes, void *stream);
 
+/* Workspace for fq_qlinear_bwd (internal layout; the size depends only on
+ * the arguments). */
+size_t fq_qlinear_bwd_workspace_size(const fq_desc *desc_x, const fq_desc *desc_w,
+                                     const fq_desc *desc_g, int64_t M, int64_t K,
+                                     int64_t N);
+
+/* QAT linear backward of fq_qlinear_fwd (Y = FQ(X) x FQ(W), X [M, K],
+ * W [K, N]), given dY [M, N]:
+ *   dX [M, K] = STE_X( Q(dY) x Q(W_hat)^T ),  Q along N for both operands,
+ *   dW [K, N] = STE_W( Q(X_hat)^T x Q(dY) ),  Q along M for both operands,
+ * where X_hat = FQ(X, desc_x) and W_hat = FQ(W, desc_w) are the forward's
+ * fake-quantized operands (recomputed here), Q quantizes with desc_g's
+ * format and rounding along the contraction axis of each product, and
+ * STE_X / STE_W pass a gradient entry where the forward did not clip that
+ * entry of X / W (a <= 6) and write +0 where it did.  The four Q draws use
+ * Philox keys desc_g->seed + 0 (dY along N), + 1 (W_hat along N), + 2 (X_hat
+ * along M), + 3 (dY along M); desc_g->axis is ignored.  Products accumulate
+ * in FP32 on the matrix cores and are rounded to BF16 before the STE.
+ * Shapes: K a multiple of 8 and of desc_x's and desc_w's block sizes (128
+ * for FQ_OUTER_BLOCK128); M and N multiples of 64 and of desc_g's block size
+ * (128 for FQ_OUTER_BLOCK128); desc_x->axis FQ_AXIS_ROW, desc_w->axis
+ * FQ_AXIS_COL as in the forward.
+ * Pointers x, w, dy, dx, dw, ws: device, 16-byte aligned, caller-owned; ws
+ * at least fq_qlinear_bwd_workspace_size bytes.  Errors as fq_qlinear_fwd.
+ * Source: TetraJet-v2, sec. 2.A (the backward computes on the aligned X_hat,
+ * with stochastic rounding so that E[round(x)] = x, and 1x16 weight groups
+ * realigned for the transposed weight); "Como o Treinamento ...", "Detalhes
+ * tecnicos" (gradients pass the quantizer by STE, clipping effects). */
+fq_status fq_qlinear_bwd(const fq_desc *desc_x, const fq_desc *desc_w,
+                         const fq_desc *desc_g, const void *x_bf16, const void *w_bf16,
+                         const void *dy_bf16, int64_t M, int64_t K, int64_t N,
+                         void *dx_bf16, void *dw_bf16, void *ws, size_t ws_bytes,
+                         void *stream);
+
 /* Static description of a status code. */
 const char *fq_status_string(fq_status s);
 

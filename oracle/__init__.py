@@ -271,3 +271,40 @@ def qlinear(x: np.ndarray, w: np.ndarray, fmt_x: str = "nv_tensor",
     fw = fake_quant(w, fmt_w, rounding_w, "col", seed_w, nthreads)
     Y = bf16_bits_to_f64(fx["y"]) @ bf16_bits_to_f64(fw["y"])
     return {"xhat": fx["y"], "what": fw["y"], "y": Y}
+
+
+def _clip_keep(x: np.ndarray, q: dict, fmt: str, axis: str) -> np.ndarray:
+    """1.0 where the forward kept x (a <= 6), 0.0 where it clipped."""
+    ones = np.full(x.shape, 0x3F80, dtype=np.uint16)      # BF16 1.0
+    return bf16_bits_to_f64(ste_backward(x, q["scales"], q["outer"], ones, fmt, axis))
+
+
+def qlinear_bwd(x: np.ndarray, w: np.ndarray, dy: np.ndarray, fmt_x: str = "nv_tensor",
+                fmt_w: str = "nv_tensor", fmt_g: str = "nv_128", rounding_g: str = "sr",
+                seed_g: int = 0, rounding_x: str = "rne", rounding_w: str = "rne",
+                seed_x: int = 0, seed_w: int = 0, nthreads: int | None = None) -> dict:
+    """QAT linear backward of Y = FQ(X) @ FQ(W) (TetraJet-v2 sec. 2.A).
+
+    X_hat = FQ(X) along K and W_hat = FQ(W) along K are the forward operands.
+    Each backward product quantizes both of its operands along its own
+    contraction axis with fmt_g / rounding_g:
+        dX = keep_X * (Q(dY, along N) @ Q(W_hat, along N)^T)     [M, K]
+        dW = keep_W * (Q(X_hat, along M)^T @ Q(dY, along M))     [K, N]
+    with Philox keys seed_g + 0, + 1, + 2, + 3 for the four Q in that order,
+    and keep_* the STE masks of the forward (1 where a <= 6).  The products
+    are float64 (numpy matmul as the contraction step).
+    """
+    fx = fake_quant(x, fmt_x, rounding_x, "row", seed_x, nthreads)
+    fw = fake_quant(w, fmt_w, rounding_w, "col", seed_w, nthreads)
+    m64 = (1 << 64) - 1
+    q_dy_n = fake_quant(dy, fmt_g, rounding_g, "row", (seed_g + 0) & m64, nthreads)
+    q_w_n = fake_quant(fw["y"], fmt_g, rounding_g, "row", (seed_g + 1) & m64, nthreads)
+    q_x_m = fake_quant(fx["y"], fmt_g, rounding_g, "col", (seed_g + 2) & m64, nthreads)
+    q_dy_m = fake_quant(dy, fmt_g, rounding_g, "col", (seed_g + 3) & m64, nthreads)
+    dx_raw = bf16_bits_to_f64(q_dy_n["y"]) @ bf16_bits_to_f64(q_w_n["y"]).T
+    dw_raw = bf16_bits_to_f64(q_x_m["y"]).T @ bf16_bits_to_f64(q_dy_m["y"])
+    keep_x = _clip_keep(x, fx, fmt_x, "row")
+    keep_w = _clip_keep(w, fw, fmt_w, "col")
+    return {"dx": keep_x * dx_raw, "dw": keep_w * dw_raw, "xhat": fx["y"], "what": fw["y"],
+            "q_dy_n": q_dy_n["y"], "q_w_n": q_w_n["y"], "q_x_m": q_x_m["y"],
+            "q_dy_m": q_dy_m["y"], "keep_x": keep_x, "keep_w": keep_w}

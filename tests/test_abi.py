@@ -129,6 +129,34 @@ def test_other_entry_points_validate(L):
                             fake(), fake(), 1024, None) == fq.FQ_ERR_WORKSPACE
 
 
+def test_qlinear_bwd_validates(L):
+    nv = fq.fq_desc_nvfp4()
+    col = fq.fq_desc_nvfp4(axis=fq.FQ_AXIS_COL)
+    g = fq.fq_desc_nvfp4(outer=fq.FQ_OUTER_BLOCK128, rounding=fq.FQ_ROUND_SR, seed=5)
+    big = 1 << 40
+
+    def call(dx_, dw_, dg_, M=128, K=128, N=128, ws_bytes=big, x=fake(), dy=fake()):
+        return L.fq_qlinear_bwd(ctypes.byref(dx_), ctypes.byref(dw_), ctypes.byref(dg_), x,
+                                fake(), dy, M, K, N, fake(), fake(), fake(), ws_bytes, None)
+
+    assert call(col, col, g) == fq.FQ_ERR_DESC                  # X must be blocked along K (rows)
+    assert call(nv, nv, g) == fq.FQ_ERR_DESC                    # W must be blocked along K (cols)
+    assert call(nv, col, g, M=64) == fq.FQ_ERR_SHAPE            # M not a multiple of 128 (g)
+    assert call(nv, col, g, N=192) == fq.FQ_ERR_SHAPE           # N not a multiple of 128 (g)
+    assert call(nv, col, nv, M=96) == fq.FQ_ERR_SHAPE           # M not a multiple of 64
+    assert call(nv, col, g, K=120) == fq.FQ_ERR_SHAPE           # K not a multiple of 16
+    assert call(nv, col, g, x=None) == fq.FQ_ERR_NULL
+    assert call(nv, col, g, dy=fake(0x10004)) == fq.FQ_ERR_ALIGN
+    need = L.fq_qlinear_bwd_workspace_size(ctypes.byref(nv), ctypes.byref(col), ctypes.byref(g),
+                                           128, 128, 128)
+    assert need > 6 * 128 * 128 * 2
+    assert call(nv, col, g, ws_bytes=need - 1) == fq.FQ_ERR_WORKSPACE
+    bad = fq.fq_desc_mxfp4()
+    bad.reserved = 1
+    assert L.fq_qlinear_bwd_workspace_size(ctypes.byref(nv), ctypes.byref(col), ctypes.byref(bad),
+                                           128, 128, 128) == 0
+
+
 def test_status_strings(L):
     for s in range(7):
         assert L.fq_status_string(s).decode().startswith("FQ_")

@@ -1,0 +1,59 @@
+"""GPU parity of the QAT linear backward (fq_qlinear_bwd) against the
+oracle's composition: dX and dW within 1e-2 relative Frobenius error of the
+float64 products of the same quantized operands, and exactly +0 wherever the
+forward's STE mask drops an entry."""
+import numpy as np
+import pytest
+import torch
+
+import fp4_block_quantization_fq_amd as fq
+import oracle
+import workloads as wl
+from gpu_util import make_desc, to_bits, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _bwd_check(M, K, N, fmt_x, fmt_w, fmt_g, rounding_g="sr", seed_g=1234,
+               seeds=(6, 7, 8), sigmas=(1.0, 0.02, 1e-3), tol=1e-2):
+    x = wl.normal_bf16((M, K), sigmas[0], seeds[0])
+    w = wl.normal_bf16((K, N), sigmas[1], seeds[1])
+    dy = wl.normal_bf16((M, N), sigmas[2], seeds[2])
+    ref = oracle.qlinear_bwd(x, w, dy, fmt_x, fmt_w, fmt_g, rounding_g, seed_g)
+    print(f"qlinear_bwd M={M} K={K} N={N} fmts={fmt_x},{fmt_w},{fmt_g} {rounding_g}", flush=True)
+    dx, dw = fq.fq_qlinear_bwd(make_desc(fmt_x, "rne", "row"), make_desc(fmt_w, "rne", "col"),
+                               make_desc(fmt_g, rounding_g, "row", seed_g),
+                               to_dev(x), to_dev(w), to_dev(dy))
+    torch.cuda.synchronize()
+    errs = {}
+    for name, got, keep in (("dx", dx, ref["keep_x"]), ("dw", dw, ref["keep_w"])):
+        g = oracle.bf16_bits_to_f64(to_bits(got))
+        r = ref[name]
+        assert np.all(g[keep == 0] == 0), name
+        errs[name] = np.linalg.norm(g - r) / np.linalg.norm(r)
+        assert errs[name] <= tol, (name, errs[name])
+    return errs
+
+
+@pytest.mark.parametrize("M,K,N", [(128, 64, 128), (128, 96, 256), (256, 384, 128)])
+@pytest.mark.parametrize("fmts", [("nv_tensor", "nv_tensor", "nv_128"), ("mx", "mx", "mx"),
+                                  ("nv_128", "nv_128", "nv_tensor")])
+def test_qlinear_bwd_small(M, K, N, fmts):
+    if "nv_128" in fmts[:2] and K % 128:
+        pytest.skip("K not a multiple of the 128-element outer block")
+    if "mx" in fmts[:2] and K % 32:
+        pytest.skip("K not a multiple of 32")
+    errs = _bwd_check(M, K, N, *fmts)
+    # products of BF16 values are exact in FP32; only accumulation order and
+    # the BF16 rounding of the product remain
+    assert max(errs.values()) < 4e-3
+
+
+def test_qlinear_bwd_rne_gradient_quantizer():
+    errs = _bwd_check(128, 128, 128, "nv_tensor", "nv_tensor", "nv_128", rounding_g="rne")
+    assert max(errs.values()) < 4e-3
+
+
+def test_workload_qlinear_bwd():
+    errs = _bwd_check(8192, 2880, 5760, "nv_tensor", "nv_tensor", "nv_128")
+    assert max(errs.values()) < 4e-3
