@@ -466,32 +466,30 @@ fq_status fq_qlinear_bwd(const fq_desc *desc_x, const fq_desc *desc_w, const fq_
                      b + L.xsc, (float *)(b + L.xout), parts, st));
     FQ_TRY(bwd_quant(fw, desc_w, desc_w->seed, true, w_bf16, K, N, b + L.what, nullptr,
                      b + L.wsc, (float *)(b + L.wout), parts, st));
-    // dX = STE_X(Q(dY) . Q(W_hat)^T), both quantized along N
+    // operands of dX = STE_X(Q(dY) . Q(W_hat)^T), both quantized along N
     FQ_TRY(bwd_quant(fg, desc_g, sg + 0, false, dy_bf16, M, N, b + L.dyq_n, nullptr, nullptr,
                      nullptr, parts, st));
     FQ_TRY(bwd_quant(fg, desc_g, sg + 1, false, b + L.what, K, N, b + L.wq_n, nullptr, nullptr,
                      nullptr, parts, st));
-    {
-        hipError_t e = fqimpl::launch_gemm_bf16_nt(b + L.dyq_n, b + L.wq_n, b + L.dx_raw, M, K, N, st);
-        if (e != hipSuccess) return device_status(e, "gemm launch");
-        e = fqimpl::launch_ste(fx.fmt, 0, x_bf16, b + L.xsc,
-                               fx.fmt == fqimpl::FMT_MX ? nullptr : (const float *)(b + L.xout),
-                               b + L.dx_raw, M, K, dx_bf16, st);
-        if (e != hipSuccess) return device_status(e, "ste launch");
-    }
-    // dW = STE_W(Q(X_hat)^T . Q(dY)), both quantized along M, written transposed
+    // operands of dW = STE_W(Q(X_hat)^T . Q(dY)), both quantized along M,
+    // written transposed
     FQ_TRY(bwd_quant(fg, desc_g, sg + 2, true, b + L.xhat, M, K, nullptr, b + L.xq_mt, nullptr,
                      nullptr, parts, st));
     FQ_TRY(bwd_quant(fg, desc_g, sg + 3, true, dy_bf16, M, N, nullptr, b + L.dyq_mt, nullptr,
                      nullptr, parts, st));
-    {
-        hipError_t e = fqimpl::launch_gemm_bf16_nt(b + L.xq_mt, b + L.dyq_mt, b + L.dw_raw, K, N, M, st);
-        if (e != hipSuccess) return device_status(e, "gemm launch");
-        e = fqimpl::launch_ste(fw.fmt, 1, w_bf16, b + L.wsc,
-                               fw.fmt == fqimpl::FMT_MX ? nullptr : (const float *)(b + L.wout),
-                               b + L.dw_raw, K, N, dw_bf16, st);
-        return device_status(e, "ste launch");
-    }
+    // both products in one launch, then the two STE masks
+    hipError_t e = fqimpl::launch_gemm_bf16_nt_pair(b + L.dyq_n, b + L.wq_n, b + L.dx_raw, M, K, N,
+                                                    b + L.xq_mt, b + L.dyq_mt, b + L.dw_raw, K, N,
+                                                    M, st);
+    if (e != hipSuccess) return device_status(e, "gemm launch");
+    e = fqimpl::launch_ste(fx.fmt, 0, x_bf16, b + L.xsc,
+                           fx.fmt == fqimpl::FMT_MX ? nullptr : (const float *)(b + L.xout),
+                           b + L.dx_raw, M, K, dx_bf16, st);
+    if (e != hipSuccess) return device_status(e, "ste launch");
+    e = fqimpl::launch_ste(fw.fmt, 1, w_bf16, b + L.wsc,
+                           fw.fmt == fqimpl::FMT_MX ? nullptr : (const float *)(b + L.wout),
+                           b + L.dw_raw, K, N, dw_bf16, st);
+    return device_status(e, "ste launch");
 }
 
 const char *fq_status_string(fq_status s)

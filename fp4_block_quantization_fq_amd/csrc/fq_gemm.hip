@@ -1,27 +1,34 @@
 // fq_gemm.hip -- BF16 x BF16 -> FP32-accumulated -> BF16 GEMM on CDNA4 MFMA.
 //
-// C[M, N] = A[M, K] * Bt[N, K]^T, both operands K-contiguous ("NT"), which
-// is how the QAT linear hands over the fake-quantized activations X_hat and
-// the transposed fake-quantized weight W_hat^T.  This is the one dense
-// contraction of the method (QAT linear forward: weights and activations are
-// both fake-quantized, then multiplied in the wider type -- gpt-oss QAT
-// tutorial, "NVFP4: The Next Generation"; TetraJet-v2, sec. 2).
+// C[M, N] = A[M, K] * Bt[N, K]^T, both operands K-contiguous ("NT").  This is
+// the one dense contraction of the method: the QAT linear multiplies the
+// fake-quantized activations by the fake-quantized weight (gpt-oss QAT
+// tutorial, "NVFP4: The Next Generation"; TetraJet-v2, sec. 2), and its
+// backward multiplies the re-quantized gradient operands (TetraJet-v2,
+// sec. 2.A).  Every operand is handed over K-contiguous: X_hat [M, K] and
+// W_hat^T [N, K] in the forward; Q(dY) [M, N] and Q(W_hat) [K, N] for dX;
+// Q(X_hat)^T [K, M] and Q(dY)^T [N, M] for dW.
 //
 // Tiling: a 256 x 256 output tile per 512-thread workgroup (2 x 4 waves of
-// 128 x 64, two waves per SIMD), K step 64.  Operand tiles go straight from global memory into LDS with gfx950's
-// global_load_lds_dwordx4 (no staging registers), double-buffered, so the
-// loads of step k+1 overlap the MFMAs of step k.  Each wave issues
-// v_mfma_f32_32x32x16_bf16 on (BM/64) x (BN/64) accumulator tiles.
+// 128 x 64, two waves per SIMD), K step 64.  Operand tiles go straight from
+// global memory into LDS with gfx950's global_load_lds_dwordx4 (no staging
+// registers), double-buffered, so the loads of step k+1 overlap the MFMAs of
+// step k.  Each wave issues v_mfma_f32_32x32x16_bf16 on 4 x 2 accumulator
+// tiles, one fragment read interleaved between MFMA pairs.
 //
-// LDS layout: one 128-byte row per tile row (64 BF16 of K), its eight 16-byte
-// chunks XOR-swizzled by (row >> 1) & 7, so the 32 rows an MFMA fragment read
-// touches spread over all 16 chunk positions of two consecutive rows.  The
-// direct loads write 1 KB per wave instruction in lane order; each lane picks
-// the global chunk that belongs in its LDS slot.
+// LDS layout: one 128-byte row per tile row (64 BF16 of K).  Its eight
+// 16-byte chunks are XOR-swizzled by (row & 7) ^ ((row >> 3) & 1), so the
+// 32 rows of a fragment read hit all chunk positions (no bank conflicts,
+// measured).  The direct loads write 1 KB per wave instruction in lane
+// order; each lane fetches the global chunk that belongs in its LDS slot.
 //
 // Workgroups are renumbered so that each XCD (the hardware deals workgroups
 // round-robin over 8 XCDs, each with its own L2) works on a contiguous run of
 // tiles, grouped 8 tile-rows at a time so that B strips are reused in L2.
+//
+// One launch may carry two independent problems (the two products of the
+// backward): their tiles share the grid, the longer one first, so the chip
+// stays busy where either alone would leave a partial last wave.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -33,50 +40,30 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void;
 
-#ifndef FQ_GEMM_PIPE
-#define FQ_GEMM_PIPE 0         // 1: barrier before the last K slice, fragments prefetched
-#endif
-#ifndef FQ_GEMM_WN
-#define FQ_GEMM_WN 4           // waves along N (2 waves along M)
-#endif
-
-constexpr int BK = 64;
+constexpr int BM = 256, BN = 256, BK = 64;
 constexpr int ROW_BYTES = BK * 2;      // 128 bytes of K per tile row
-constexpr int kWavesM = 2, kWavesN = FQ_GEMM_WN;
+constexpr int kWavesM = 2, kWavesN = 4;
 constexpr int kThreads = 64 * kWavesM * kWavesN;
 constexpr int kXcds = 8;
 
-#ifndef FQ_GEMM_SWZ
-#define FQ_GEMM_SWZ 2
-#endif
-#ifndef FQ_GEMM_BM
-#define FQ_GEMM_BM 256
-#endif
-#ifndef FQ_GEMM_BN
-#define FQ_GEMM_BN 256
-#endif
-#ifndef FQ_GEMM_SCHED
-#define FQ_GEMM_SCHED 1
-#endif
+struct Problem {
+    const uint16_t *A;
+    const uint16_t *Bt;
+    uint16_t *C;
+    int M, N, K;
+    int tiles;     // workgroups of this problem in the grid
+};
 
-// Chunk position of 16-byte K chunk `chunk` in LDS row `row`: any 8 rows
-// r..r+7 (r a multiple of 8) get 8 different positions and any 16 rows two
-// different halves, so a fragment read of 32 consecutive rows is free of
-// bank conflicts whether the LDS serves 8 or 16 lanes of 16 bytes per cycle.
 __device__ __forceinline__ int swz(int row, int chunk)
 {
-#if FQ_GEMM_SWZ == 0
-    return chunk ^ ((row >> 1) & 7);
-#elif FQ_GEMM_SWZ == 1
-    return chunk ^ (row & 7);
-#else
     return chunk ^ (row & 7) ^ ((row >> 3) & 1);
-#endif
 }
 
-// Issue the direct loads of one BM-row (or BN-row) operand tile at k0 into
-// LDS.  Wave w, instruction i covers tile rows [w*ROWS/4 + 8i, +8): lane l
-// fills LDS slot (l & 7) of row (l >> 3) with the global chunk swizzled there.
+// Issue the direct loads of one ROWS-row operand tile at k0 into LDS.  Wave
+// w, instruction i covers tile rows [w*ROWS/8 + 8i, +8): lane l fills LDS
+// slot (l & 7) of row (l >> 3) with the global chunk swizzled there.  Rows
+// past the end of the operand are clamped to its last row (their outputs are
+// never stored).
 template <int ROWS>
 __device__ __forceinline__ void load_tile(const uint16_t *__restrict__ g, int row0, int nrows,
                                           int K, int k0, uint8_t *lds_tile, int wave, int lane)
@@ -86,18 +73,14 @@ __device__ __forceinline__ void load_tile(const uint16_t *__restrict__ g, int ro
     for (int i = 0; i < PER_WAVE / 8; ++i) {
         const int r = wave * PER_WAVE + i * 8 + (lane >> 3);
         const int c = swz(r, lane & 7);
-        const int gr = min(row0 + r, nrows - 1);       // clamp: rows past the end feed
-        const uint16_t *src = g + (size_t)gr * K + k0 + c * 8;   // discarded outputs
+        const int gr = min(row0 + r, nrows - 1);
+        const uint16_t *src = g + (size_t)gr * K + k0 + c * 8;
         uint8_t *dst = lds_tile + (wave * PER_WAVE + i * 8) * ROW_BYTES;
         __builtin_amdgcn_global_load_lds((const void *)src, (lds_void *)dst, 16, 0, 0);
     }
 }
 
-template <int BM, int BN>
-__global__ __launch_bounds__(kThreads, 1) void k_gemm_nt(const uint16_t *__restrict__ A,
-                                                         const uint16_t *__restrict__ Bt,
-                                                         uint16_t *__restrict__ C, int M, int N,
-                                                         int K)
+__global__ __launch_bounds__(kThreads, 1) void k_gemm_nt(Problem p0, Problem p1)
 {
     constexpr int WTM = BM / kWavesM, WTN = BN / kWavesN;  // wave tile
     constexpr int TM = WTM / 32, TN = WTN / 32;             // 32x32 tiles per wave
@@ -105,9 +88,17 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_nt(const uint16_t *__restr
     constexpr int STAGE = A_BYTES + B_BYTES;
     __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * STAGE];
 
+    // this workgroup's problem (uniform across the workgroup)
+    const bool second = (int)blockIdx.x >= p0.tiles;
+    const uint16_t *__restrict__ A = second ? p1.A : p0.A;
+    const uint16_t *__restrict__ Bt = second ? p1.Bt : p0.Bt;
+    uint16_t *__restrict__ C = second ? p1.C : p0.C;
+    const int M = second ? p1.M : p0.M, N = second ? p1.N : p0.N, K = second ? p1.K : p0.K;
+    const int b = second ? (int)blockIdx.x - p0.tiles : (int)blockIdx.x;
+
     const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
     const int ntiles = tiles_m * tiles_n;
-    const int b = blockIdx.x;
+    if (b >= ntiles) return;           // padding workgroups (XCD alignment of the second problem)
     int logical = b;
     if (ntiles % kXcds == 0) logical = (b % kXcds) * (ntiles / kXcds) + b / kXcds;
     const int group = 8;
@@ -132,63 +123,6 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_nt(const uint16_t *__restr
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
     const int nk = K / BK;
-#if FQ_GEMM_PIPE
-    // Fragment reads of one 16-wide K slice from an LDS stage.
-    auto read_frags = [&](const uint8_t *stage, int ks, bf16x8 (&fa)[TM], bf16x8 (&fb)[TN]) {
-        const int c = ks * 2 + (lane >> 5);
-#pragma unroll
-        for (int i = 0; i < TM; ++i) {
-            const int r = wm * WTM + i * 32 + (lane & 31);
-            fa[i] = *reinterpret_cast<const bf16x8 *>(stage + r * ROW_BYTES + swz(r, c) * 16);
-        }
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            const int r = wn * WTN + j * 32 + (lane & 31);
-            fb[j] = *reinterpret_cast<const bf16x8 *>(stage + A_BYTES + r * ROW_BYTES + swz(r, c) * 16);
-        }
-    };
-    // prologue: stages 0 and 1 in flight, stage 0 waited for
-    load_tile<BM>(A, row_a0, M, K, 0, lds, wave, lane);
-    load_tile<BN>(Bt, row_b0, N, K, 0, lds + A_BYTES, wave, lane);
-    __builtin_amdgcn_s_waitcnt(0);
-    if (nk > 1) {
-        load_tile<BM>(A, row_a0, M, K, BK, lds + STAGE, wave, lane);
-        load_tile<BN>(Bt, row_b0, N, K, BK, lds + STAGE + A_BYTES, wave, lane);
-    }
-    __syncthreads();
-    bf16x8 fa[TM], fb[TN], na[TM], nb[TN];
-    read_frags(lds, 0, fa, fb);
-
-    for (int kt = 0; kt < nk; ++kt) {
-        uint8_t *cur = lds + (kt & 1) * STAGE;
-        uint8_t *nxt = lds + ((kt + 1) & 1) * STAGE;
-#pragma unroll
-        for (int ks = 0; ks < BK / 16; ++ks) {
-            if (ks < BK / 16 - 1) {
-                read_frags(cur, ks + 1, na, nb);
-            } else {
-                // every wave holds its last fragments of `cur`; stage kt+1 has landed
-                __builtin_amdgcn_s_waitcnt(0);
-                __syncthreads();
-                if (kt + 2 < nk) {
-                    load_tile<BM>(A, row_a0, M, K, (kt + 2) * BK, cur, wave, lane);
-                    load_tile<BN>(Bt, row_b0, N, K, (kt + 2) * BK, cur + A_BYTES, wave, lane);
-                }
-                if (kt + 1 < nk) read_frags(nxt, 0, na, nb);
-            }
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
-#pragma unroll
-                for (int j = 0; j < TN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j],
-                                                                        0, 0, 0);
-#pragma unroll
-            for (int i = 0; i < TM; ++i) fa[i] = na[i];
-#pragma unroll
-            for (int j = 0; j < TN; ++j) fb[j] = nb[j];
-        }
-    }
-#else
     load_tile<BM>(A, row_a0, M, K, 0, lds, wave, lane);
     load_tile<BN>(Bt, row_b0, N, K, 0, lds + A_BYTES, wave, lane);
     __builtin_amdgcn_s_waitcnt(0);
@@ -222,19 +156,15 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_nt(const uint16_t *__restr
                 for (int j = 0; j < TN; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j],
                                                                         0, 0, 0);
-#if FQ_GEMM_SCHED == 1
-            // interleave: one fragment read between MFMAs
+            // interleave: one fragment read between MFMA pairs
             for (int q = 0; q < TM + TN; ++q) {
                 __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
                 __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // MFMA
             }
-#endif
         }
         __builtin_amdgcn_s_waitcnt(0);      // this wave's loads of step kt+1 have landed
         __syncthreads();                    // all loads landed, all reads of `cur` done
     }
-
-#endif
 
     // epilogue: accumulator element v of lane l sits at row (v/4)*8 + (l/32)*4 + v%4,
     // column l%32 of its 32 x 32 tile
@@ -256,6 +186,21 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_nt(const uint16_t *__restr
         }
 }
 
+int tile_count(int64_t M, int64_t N) { return (int)(((M + BM - 1) / BM) * ((N + BN - 1) / BN)); }
+
+Problem make_problem(const void *a, const void *bt, void *c, int64_t M, int64_t N, int64_t K)
+{
+    Problem p;
+    p.A = (const uint16_t *)a;
+    p.Bt = (const uint16_t *)bt;
+    p.C = (uint16_t *)c;
+    p.M = (int)M;
+    p.N = (int)N;
+    p.K = (int)K;
+    p.tiles = tile_count(M, N);
+    return p;
+}
+
 }  // namespace
 
 namespace fqimpl {
@@ -263,11 +208,30 @@ namespace fqimpl {
 hipError_t launch_gemm_bf16_nt(const void *a, const void *bt, void *c, int64_t M, int64_t N,
                                int64_t K, hipStream_t stream)
 {
-    constexpr int BM = FQ_GEMM_BM, BN = FQ_GEMM_BN;
-    const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-    hipLaunchKernelGGL((k_gemm_nt<BM, BN>), dim3((uint32_t)tiles), dim3(kThreads), 0, stream,
-                       (const uint16_t *)a, (const uint16_t *)bt, (uint16_t *)c, (int)M,
-                       (int)N, (int)K);
+    Problem p0 = make_problem(a, bt, c, M, N, K), p1 = p0;
+    p1.tiles = 0;
+    hipLaunchKernelGGL(k_gemm_nt, dim3((uint32_t)p0.tiles), dim3(kThreads), 0, stream, p0, p1);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_bf16_nt_pair(const void *a0, const void *bt0, void *c0, int64_t M0,
+                                    int64_t N0, int64_t K0, const void *a1, const void *bt1,
+                                    void *c1, int64_t M1, int64_t N1, int64_t K1,
+                                    hipStream_t stream)
+{
+    Problem p0 = make_problem(a0, bt0, c0, M0, N0, K0);
+    Problem p1 = make_problem(a1, bt1, c1, M1, N1, K1);
+    // longer per-tile contraction first; the first problem's share of the
+    // grid is padded to a multiple of the XCD count so that the second keeps
+    // its XCD-contiguous tile order
+    if (p1.K > p0.K) {
+        const Problem t = p0;
+        p0 = p1;
+        p1 = t;
+    }
+    p0.tiles = (p0.tiles + kXcds - 1) / kXcds * kXcds;
+    hipLaunchKernelGGL(k_gemm_nt, dim3((uint32_t)(p0.tiles + p1.tiles)), dim3(kThreads), 0,
+                       stream, p0, p1);
     return hipGetLastError();
 }
 

@@ -41,5 +41,10 @@ hipError_t launch_ste(int fmt, int col, const void *x, const void *scales,
                       void *dx, hipStream_t stream);
 hipError_t launch_gemm_bf16_nt(const void *a, const void *bt, void *c, int64_t M,
                                int64_t N, int64_t K, hipStream_t stream);
+// Two independent products C0 = A0 * Bt0^T and C1 = A1 * Bt1^T in one launch.
+hipError_t launch_gemm_bf16_nt_pair(const void *a0, const void *bt0, void *c0, int64_t M0,
+                                    int64_t N0, int64_t K0, const void *a1, const void *bt1,
+                                    void *c1, int64_t M1, int64_t N1, int64_t K1,
+                                    hipStream_t stream);
 
 }  // namespace fqimpl
