@@ -16,7 +16,10 @@ seed 3) and its upstream gradient (N(0, 1e-3^2), seed 4):
 
 Every op writes all of its outputs (codes, scales, outer scales, BF16).
 `value` is the step's algorithmic bytes (each input read once, each output
-written once) over the step time, in GB/s.  Inputs are resident in HBM; the
+written once) over the step time, in GB/s.  The step is captured once per
+buffer set as a HIP graph and the graphs are replayed (`ms_per_step`); the same
+ops launched one by one with events around each (`ms_per_step_eager`) give the
+per-kernel times under "kernels" and the roofline figures.  Inputs are resident in HBM; the
 step rotates over three input/output buffer sets (~1.9 GB) so no launch
 finds its operands in the 256 MB Infinity Cache.
 
@@ -102,6 +105,8 @@ def main():
                     help="rows of the workload the CPU oracle is timed on")
     ap.add_argument("--qlinear-iters", type=int, default=20)
     ap.add_argument("--only", default="", help="comma-separated subset of ops (profiling)")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="time the step from eager launches instead of HIP graph replays")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -167,9 +172,10 @@ def main():
     torch.cuda.synchronize()
 
     K = args.steps
+    # Per-kernel times: every op bracketed by events on the launch stream.
     ev = {op: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(K)] for op in ops}
-    log(f"bench: timing {K} steps")
+    log(f"bench: timing {K} steps op by op")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(K):
@@ -181,7 +187,32 @@ def main():
             b.record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / K
+    ms_per_step_eager = (t1 - t0) * 1e3 / K
+
+    # The step itself: one HIP graph per buffer set holding the whole step
+    # (every op, every launch), replayed K times.  The same kernels on the same
+    # buffers; the graph only removes the per-launch host and queue overhead.
+    ms_per_step = ms_per_step_eager
+    graphs = []
+    if not args.no_graph:
+        log("bench: capturing the step as HIP graphs")
+        cap = torch.cuda.Stream()
+        for i in range(NBUF):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cap):
+                for op in ops:
+                    run_op(op, i)
+            graphs.append(g)
+        for s in range(2 * NBUF):
+            graphs[s % NBUF].replay()
+        torch.cuda.synchronize()
+        log(f"bench: timing {K} graph steps")
+        t0 = time.perf_counter()
+        for s in range(K):
+            graphs[s % NBUF].replay()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        ms_per_step = (t1 - t0) * 1e3 / K
 
     kernels = {}
     step_bytes = 0
@@ -305,6 +336,7 @@ def main():
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
         "steps": K, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step_eager": round(ms_per_step_eager, 4), "step_launch": "graph" if graphs else "eager",
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": "FP4 fake-quant step over a 16384x4096 bf16 activation "

@@ -285,24 +285,43 @@ __device__ __forceinline__ void scatter_pairs(uint4 (&v)[16], int k, const uint3
 }
 
 // Quantizer tile: a lane holds 8 columns of 16 consecutive rows, eight lanes
-// stack 128 rows, a wave spans 64 columns, and the four waves of a workgroup
-// sit side by side along the columns (256 columns x 128 rows per workgroup):
-// measured faster than stacking them along the rows.
-constexpr uint32_t kColTileC = 256, kColTileR = 128;
+// stack 128 rows, a wave spans 64 columns; the four waves of a workgroup sit
+// kColWc side by side along the columns and 4 / kColWc along the rows.  The
+// transposed codes, scales and outer scales are gathered in LDS and leave the
+// workgroup as runs of kColTileR / 2, kColTileR / B and kColTileR / 128
+// entries per column, instead of each lane storing its 8-byte and 1-byte
+// pieces at column stride.
+#ifndef FQ_COL_WC
+#define FQ_COL_WC 4
+#endif
+constexpr uint32_t kColWc = FQ_COL_WC;
+constexpr uint32_t kColTileC = 64 * kColWc, kColTileR = 128 * (4 / kColWc);
+constexpr uint32_t kColCodePitch = kColTileR / 2 + 8;   // bytes; 8 * pitch = 64 mod 256
 
 __device__ __forceinline__ uint32_t vword(const uint4 &v, int k)
 {
     return k == 0 ? v.x : k == 1 ? v.y : k == 2 ? v.z : v.w;
 }
 
-__device__ __forceinline__ ColTile quant_col_tile(uint32_t R, uint32_t C)
+struct QColTile {
+    uint32_t col0, row0, rb;   // lane's first column, first row, row block in its group
+    uint32_t lc, lr;           // the same relative to the workgroup tile
+    uint32_t tc0, tr0;         // workgroup tile origin
+    bool valid;
+};
+
+__device__ __forceinline__ QColTile quant_col_tile(uint32_t R, uint32_t C)
 {
     const uint32_t lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const uint32_t tiles_c = (C + kColTileC - 1) / kColTileC;
-    ColTile t;
+    QColTile t;
     t.rb = lane & 7;
-    t.col0 = (blockIdx.x % tiles_c) * kColTileC + wave * 64 + (lane >> 3) * 8;
-    t.row0 = (blockIdx.x / tiles_c) * kColTileR + t.rb * 16;
+    t.tc0 = (blockIdx.x % tiles_c) * kColTileC;
+    t.tr0 = (blockIdx.x / tiles_c) * kColTileR;
+    t.lc = (wave % kColWc) * 64 + (lane >> 3) * 8;
+    t.lr = (wave / kColWc) * 128 + t.rb * 16;
+    t.col0 = t.tc0 + t.lc;
+    t.row0 = t.tr0 + t.lr;
     t.valid = t.col0 < C && t.row0 < R;
     return t;
 }
@@ -315,86 +334,114 @@ __global__ __launch_bounds__(kThreads) void k_quant_col(
     uint32_t seed_lo, uint32_t seed_hi)
 {
     constexpr uint32_t B = (FMT == FMT_MX) ? 32 : 16;
-    constexpr int NW = 4;                    // packed words per row segment
-    typedef uint4 VT;
+    constexpr uint32_t SPB = kColTileR / B;          // scale bytes per column in the tile
+    constexpr uint32_t OPB = kColTileR / 128;        // outer scales per column in the tile
+    __shared__ __attribute__((aligned(16))) uint8_t s_codes[kColTileC * kColCodePitch];
+    __shared__ uint8_t s_scales[kColTileC * SPB];
+    __shared__ float s_outer[FMT == FMT_NV128 ? kColTileC * OPB : 1];
+
     OuterScale ot = {0.0f, 0.0f};
     if (FMT == FMT_NVT) {
         ot = tensor_scale(partials, npart);
         if (outer && blockIdx.x == 0 && threadIdx.x == 0) outer[0] = ot.s;
     }
-    const ColTile t = quant_col_tile(R, C);
-    if (!t.valid) return;     // MXFP4 pairs and double-block groups leave together
+    const QColTile t = quant_col_tile(R, C);
     const uint32_t ldx = C >> 3;   // 16-byte segments per row
-    const VT *__restrict__ xv = x;
 
-    VT v[16];
+    if (t.valid) {     // MXFP4 pairs and double-block groups are valid together
+        uint4 v[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) v[r] = xv[(size_t)(t.row0 + r) * ldx + (t.col0 >> 3)];
+        for (int r = 0; r < 16; ++r) v[r] = x[(size_t)(t.row0 + r) * ldx + (t.col0 >> 3)];
 
-    // per-column maxima of the lane's 16 rows: packed u16 max
-    uint32_t mw[NW];
+        // per-column maxima of the lane's 16 rows: packed u16 max
+        uint32_t mw[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int k = 0; k < NW; ++k) mw[k] = 0u;
+        for (int r = 0; r < 16; ++r)
 #pragma unroll
-    for (int r = 0; r < 16; ++r)
-#pragma unroll
-        for (int k = 0; k < NW; ++k) mw[k] = pkmax_u16(mw[k], vword(v[r], k) & 0x7FFF7FFFu);
+            for (int k = 0; k < 4; ++k) mw[k] = pkmax_u16(mw[k], vword(v[r], k) & 0x7FFF7FFFu);
 
 #pragma unroll
-    for (int k = 0; k < NW; ++k) {
-        uint32_t yph[2][8];
+        for (int k = 0; k < 4; ++k) {
+            uint32_t yph[2][8];
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const uint32_t col = t.col0 + 2 * k + h;
-            const uint32_t amax16 = h ? (mw[k] >> 16) : (mw[k] & 0xFFFFu);
-            float so = 0.0f;
-            const BlockScale b = lane_block_scale<FMT>(amax16, ot, so);
-            if (FMT == FMT_NV128 && outer && t.rb == 0)
-                outer[(size_t)col * (R >> 7) + (t.row0 >> 7)] = so;
-            if (scales) {
-                if (FMT == FMT_MX) {
-                    if ((t.rb & 1) == 0) scales[(size_t)col * (R / B) + t.row0 / B] = (uint8_t)b.code;
-                } else {
-                    scales[(size_t)col * (R / B) + t.row0 / B] = (uint8_t)b.code;
+            for (int h = 0; h < 2; ++h) {
+                const uint32_t c = 2 * k + h;
+                const uint32_t col = t.col0 + c;
+                const uint32_t amax16 = h ? (mw[k] >> 16) : (mw[k] & 0xFFFFu);
+                float so = 0.0f;
+                const BlockScale b = lane_block_scale<FMT>(amax16, ot, so);
+                if (FMT == FMT_NV128 && t.rb == 0) s_outer[(t.lc + c) * OPB + t.lr / 128] = so;
+                if (FMT != FMT_MX || (t.rb & 1) == 0)
+                    s_scales[(t.lc + c) * SPB + t.lr / B] = (uint8_t)b.code;
+                u32x4 rnd[2];
+                if (RND == RND_SR) {
+                    const uint64_t call0 = ((uint64_t)col * R + t.row0) >> 3;
+                    rnd[0] = philox4x32_10((uint32_t)call0, (uint32_t)(call0 >> 32), 0u, 0u,
+                                           seed_lo, seed_hi);
+                    rnd[1] = philox4x32_10((uint32_t)(call0 + 1), (uint32_t)((call0 + 1) >> 32),
+                                           0u, 0u, seed_lo, seed_hi);
+                }
+                // column pairs along rows: element 2i in the low half of xp[i]
+                uint32_t xp[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const uint32_t wa = vword(v[2 * i], k), wb = vword(v[2 * i + 1], k);
+                    xp[i] = h ? ((wa >> 16) | (wb & 0xFFFF0000u)) : ((wa & 0xFFFFu) | (wb << 16));
+                }
+                uint32_t cw[2];
+                encode_pairs<FMT, RND, 8>(xp, b, rnd, cw, yph[h]);
+                *reinterpret_cast<uint2 *>(&s_codes[(t.lc + c) * kColCodePitch + t.lr / 2]) =
+                    make_uint2(cw[0], cw[1]);
+                if (yt) {
+                    uint4 *dst = yt + (((size_t)col * R + t.row0) >> 3);
+                    st_stream<NT>(&dst[0], make_uint4(yph[h][0], yph[h][1], yph[h][2], yph[h][3]));
+                    st_stream<NT>(&dst[1], make_uint4(yph[h][4], yph[h][5], yph[h][6], yph[h][7]));
                 }
             }
-            u32x4 rnd[2];
-            if (RND == RND_SR) {
-                const uint64_t call0 = ((uint64_t)col * R + t.row0) >> 3;
-                rnd[0] = philox4x32_10((uint32_t)call0, (uint32_t)(call0 >> 32), 0u, 0u, seed_lo, seed_hi);
-                rnd[1] = philox4x32_10((uint32_t)(call0 + 1), (uint32_t)((call0 + 1) >> 32), 0u, 0u,
-                                       seed_lo, seed_hi);
-            }
-            // column pairs along rows: element 2i in the low half of xp[i]
-            uint32_t xp[8];
+            if (y) {
+                // columns 2k, 2k+1 back into the row segments
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const uint32_t wa = vword(v[2 * i], k), wb = vword(v[2 * i + 1], k);
-                xp[i] = h ? ((wa >> 16) | (wb & 0xFFFF0000u)) : ((wa & 0xFFFFu) | (wb << 16));
-            }
-            uint32_t cw[2];
-            encode_pairs<FMT, RND, 8>(xp, b, rnd, cw, yph[h]);
-            if (codes)
-                st_stream<NT>(reinterpret_cast<uint2 *>(codes + (size_t)col * (R >> 1) + (t.row0 >> 1)),
-                              make_uint2(cw[0], cw[1]));
-            if (yt) {
-                uint4 *dst = yt + (((size_t)col * R + t.row0) >> 3);
-                st_stream<NT>(&dst[0], make_uint4(yph[h][0], yph[h][1], yph[h][2], yph[h][3]));
-                st_stream<NT>(&dst[1], make_uint4(yph[h][4], yph[h][5], yph[h][6], yph[h][7]));
+                for (int i = 0; i < 8; ++i) {
+                    seg_set_word(v[2 * i], k, (yph[0][i] & 0xFFFFu) | (yph[1][i] << 16));
+                    seg_set_word(v[2 * i + 1], k, (yph[0][i] >> 16) | (yph[1][i] & 0xFFFF0000u));
+                }
             }
         }
         if (y) {
-            // columns 2k, 2k+1 back into the row segments
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                seg_set_word(v[2 * i], k, (yph[0][i] & 0xFFFFu) | (yph[1][i] << 16));
-                seg_set_word(v[2 * i + 1], k, (yph[0][i] >> 16) | (yph[1][i] & 0xFFFF0000u));
-            }
+            for (int r = 0; r < 16; ++r)
+                st_stream<NT>(&y[(size_t)(t.row0 + r) * ldx + (t.col0 >> 3)], v[r]);
         }
     }
-    if (y) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) st_stream<NT>(&y[(size_t)(t.row0 + r) * ldx + (t.col0 >> 3)], v[r]);
+    __syncthreads();
+
+    // The tile's transposed outputs, column by column.  Only entries whose
+    // column and rows exist are written (R is a multiple of B; a partial last
+    // band of rows fills a prefix of each column's run).
+    const uint32_t rows_here = min(kColTileR, R - t.tr0);
+    if (codes) {
+        constexpr uint32_t P8 = kColTileR / 16;      // 8-byte pieces per column
+        for (uint32_t q = threadIdx.x; q < kColTileC * P8; q += kThreads) {
+            const uint32_t lc = q / P8, j = q % P8;
+            if (t.tc0 + lc < C && j * 16 < rows_here)
+                st_stream<NT>(reinterpret_cast<uint2 *>(codes + (size_t)(t.tc0 + lc) * (R >> 1) +
+                                                        (t.tr0 >> 1) + j * 8),
+                              *reinterpret_cast<const uint2 *>(&s_codes[lc * kColCodePitch + j * 8]));
+        }
+    }
+    if (scales) {
+        for (uint32_t q = threadIdx.x; q < kColTileC * SPB; q += kThreads) {
+            const uint32_t lc = q / SPB, j = q % SPB;
+            if (t.tc0 + lc < C && j * B < rows_here)
+                scales[(size_t)(t.tc0 + lc) * (R / B) + t.tr0 / B + j] = s_scales[q];
+        }
+    }
+    if (FMT == FMT_NV128 && outer) {
+        for (uint32_t q = threadIdx.x; q < kColTileC * OPB; q += kThreads) {
+            const uint32_t lc = q / OPB, j = q % OPB;
+            if (t.tc0 + lc < C && j * 128 < rows_here)
+                outer[(size_t)(t.tc0 + lc) * (R >> 7) + (t.tr0 >> 7) + j] = s_outer[q];
+        }
     }
 }
 
