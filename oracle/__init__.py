@@ -79,6 +79,11 @@ def lib() -> ctypes.CDLL:
         L.fqo_ste_backward_rows.argtypes = [ctypes.c_int, u16p, u8p, f32p, u16p,
                                             i64, i64, u16p, ctypes.c_int]
         L.fqo_ste_backward_rows.restype = ctypes.c_int
+        L.fqo_rht_sign_bit.argtypes = [ctypes.c_uint64, ctypes.c_uint64]
+        L.fqo_rht_sign_bit.restype = ctypes.c_int
+        L.fqo_hadamard_rows.argtypes = [u16p, i64, i64, ctypes.c_int, ctypes.c_uint64,
+                                        ctypes.c_float, u16p, ctypes.c_int]
+        L.fqo_hadamard_rows.restype = ctypes.c_int
         L.fqo_max_threads.argtypes = []
         L.fqo_max_threads.restype = ctypes.c_int
         _lib = L
@@ -308,3 +313,33 @@ def qlinear_bwd(x: np.ndarray, w: np.ndarray, dy: np.ndarray, fmt_x: str = "nv_t
     return {"dx": keep_x * dx_raw, "dw": keep_w * dw_raw, "xhat": fx["y"], "what": fw["y"],
             "q_dy_n": q_dy_n["y"], "q_w_n": q_w_n["y"], "q_x_m": q_x_m["y"],
             "q_dy_m": q_dy_m["y"], "keep_x": keep_x, "keep_w": keep_w}
+
+
+# FP32 value nearest to 1/sqrt(n): 0.25 for n = 16; for n = 128 the bits
+# 0x3DB504F3 (the test suite checks that no other FP32 value is nearer).
+RHT_SCALE_BITS = {16: 0x3E800000, 128: 0x3DB504F3}
+
+
+def rht_scale(n: int) -> float:
+    return float(np.array([RHT_SCALE_BITS[n]], dtype=np.uint32).view(np.float32)[0])
+
+
+def rht_sign_bit(seed: int, j: int) -> int:
+    """1 where position j of the random Hadamard transform flips sign."""
+    return lib().fqo_rht_sign_bit(seed, j)
+
+
+def hadamard(x: np.ndarray, block: int, axis: str = "row", seed: int = 0,
+             nthreads: int | None = None) -> np.ndarray:
+    """Random Hadamard transform of a [R, C] BF16 tensor (uint16 bits) in
+    blocks of `block` (16 or 128) consecutive elements along `axis`; BF16
+    result in the layout of x.  axis="col" is the row transform of x^T."""
+    n = default_threads() if nthreads is None else nthreads
+    src = np.ascontiguousarray(x if axis == "row" else x.T, dtype=np.uint16)
+    R, C = src.shape
+    y = np.empty_like(src)
+    rc = lib().fqo_hadamard_rows(_ptr(src, ctypes.c_uint16), R, C, block, seed,
+                                 rht_scale(block), _ptr(y, ctypes.c_uint16), n)
+    if rc != 0:
+        raise ValueError(f"hadamard: unsupported shape {src.shape} for block {block}")
+    return y if axis == "row" else np.ascontiguousarray(y.T)

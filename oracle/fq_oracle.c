@@ -45,6 +45,7 @@
  */
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 #ifdef _OPENMP
@@ -447,6 +448,62 @@ int fqo_ste_backward_rows(int fmt, const uint16_t *x, const uint8_t *scales,
             dx[r * C + c] = (a > 6.0f) ? (uint16_t)0 : dy[r * C + c];
         }
     }
+    return 0;
+}
+
+/* Random Hadamard transform along rows, in blocks of n = 16 or 128
+ * consecutive elements ("Resumo Tecnico: TetraJet-v2", sec. 2.C OutControl:
+ * a random Hadamard transform is applied to the backward's products so that
+ * outlier energy spreads over the channels before quantization).
+ *
+ * Random signs: position j along the row (the column index) has sign -1
+ * when bit (j mod 128) of Philox4x32-10(key = seed, counter = (j / 128, 0,
+ * 0, 0)) is set (bit t of output word w counts as bit 32w + t), else +1.
+ * Transform of a block v = s o x (exact sign flips of the BF16 values,
+ * widened to FP32): radix-2 butterflies in FP32 with half-widths h = 1, 2,
+ * 4, ..., n/2, each pair (i, i + h) of a 2h-group becoming (a + b, a - b);
+ * this is the Hadamard matrix in Sylvester order.  Then y = BF16_RNE(
+ * RN32(c_n * v)) with c_n the FP32 value nearest to 1/sqrt(n) (0.25 for n =
+ * 16).  The rows of a [R, C] tensor are independent. */
+int fqo_rht_sign_bit(uint64_t seed, uint64_t j)
+{
+    const uint32_t ctr[4] = {(uint32_t)(j >> 7), (uint32_t)(j >> 39), 0u, 0u};
+    const uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+    uint32_t o[4];
+    fqo_philox4x32_10(ctr, key, o);
+    const unsigned b = (unsigned)(j & 127);
+    return (int)((o[b >> 5] >> (b & 31)) & 1u);
+}
+
+int fqo_hadamard_rows(const uint16_t *x, int64_t R, int64_t C, int n, uint64_t seed,
+                      float c_n, uint16_t *y, int nthreads)
+{
+    if (R <= 0 || C <= 0 || (n != 16 && n != 128) || C % n != 0) return -1;
+    uint8_t *neg = (uint8_t *)malloc((size_t)C);     /* the sign of each column */
+    if (!neg) return -2;
+    for (int64_t j = 0; j < C; ++j) neg[j] = (uint8_t)fqo_rht_sign_bit(seed, (uint64_t)j);
+    (void)nthreads;
+#ifdef _OPENMP
+#pragma omp parallel for schedule(static) num_threads(nthreads > 0 ? nthreads : 1)
+#endif
+    for (int64_t r = 0; r < R; ++r) {
+        float v[128];
+        for (int64_t b0 = 0; b0 < C; b0 += n) {
+            for (int i = 0; i < n; ++i) {
+                float e = fqo_bf16_to_f32(x[r * C + b0 + i]);
+                v[i] = neg[b0 + i] ? -e : e;
+            }
+            for (int h = 1; h < n; h *= 2)
+                for (int g = 0; g < n; g += 2 * h)
+                    for (int t = g; t < g + h; ++t) {
+                        float a = v[t], b = v[t + h];
+                        v[t] = a + b;
+                        v[t + h] = a - b;
+                    }
+            for (int i = 0; i < n; ++i) y[r * C + b0 + i] = fqo_f32_to_bf16(c_n * v[i]);
+        }
+    }
+    free(neg);
     return 0;
 }
 
