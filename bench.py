@@ -307,6 +307,42 @@ def main():
                              "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                              "frac": round(tfb / BF16_PEAK_TFLOPS, 4)}}
 
+    # ---------------- random Hadamard transform ----------------
+    rht = None
+    if not args.only:
+        log("bench: hadamard")
+        rht = {}
+        for name, ax in (("row128", fq.FQ_AXIS_ROW), ("col128", fq.FQ_AXIS_COL)):
+            for i in range(NBUF):
+                fq.fq_hadamard(xs[i], 128, ax, 77, y=ys[i])
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for s in range(K):
+                fq.fq_hadamard(xs[s % NBUF], 128, ax, 77, y=ys[s % NBUF])
+            e1.record()
+            torch.cuda.synchronize()
+            hms = e0.elapsed_time(e1) / K
+            rht[name] = {"ms": round(hms, 5), "bytes": 4 * n,
+                         "GBps": round(4 * n / (hms * 1e-3) / 1e9, 1),
+                         "frac_hbm": round(4 * n / (hms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        # the backward again with both products' operands rotated (128-blocks)
+        bws_r = fq.qlinear_bwd_workspace(dxd, dwd, dgd, M, Kd, N, dev, rht_block=128)
+        for _ in range(2):
+            fq.fq_qlinear_bwd(dxd, dwd, dgd, xq, wq, dyq, dx=gx, dw=gw, ws=bws_r,
+                              rht_block=128, rht_seed=55)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.qlinear_iters):
+            fq.fq_qlinear_bwd(dxd, dwd, dgd, xq, wq, dyq, dx=gx, dw=gw, ws=bws_r,
+                              rht_block=128, rht_seed=55)
+        e1.record()
+        torch.cuda.synchronize()
+        rms = e0.elapsed_time(e1) / args.qlinear_iters
+        rht["qlinear_bwd_rht128"] = {"ms": round(rms, 4),
+                                     "TFLOPs": round(4.0 * M * Kd * N / (rms * 1e-3) / 1e12, 1)}
+
     # ---------------- CPU oracle baseline ----------------
     cpu = None
     if not args.no_cpu_baseline and not args.only:
@@ -349,6 +385,7 @@ def main():
         "kernels": kernels,
         "qlinear": qlin,
         "qlinear_bwd": qbwd,
+        "hadamard": rht,
     }
     print(json.dumps(out), flush=True)
 

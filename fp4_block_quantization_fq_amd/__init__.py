@@ -28,8 +28,8 @@ FQ_AXIS_ROW, FQ_AXIS_COL = 0, 1
 EXPORTED = (
     "fq_desc_mxfp4", "fq_desc_nvfp4", "fq_workspace_size", "fq_quantize",
     "fq_dequantize", "fq_fake_quant", "fq_ste_backward",
-    "fq_qlinear_workspace_size", "fq_qlinear_fwd", "fq_qlinear_bwd_workspace_size",
-    "fq_qlinear_bwd", "fq_status_string",
+    "fq_qlinear_workspace_size", "fq_qlinear_fwd", "fq_hadamard",
+    "fq_qlinear_bwd_workspace_size", "fq_qlinear_bwd", "fq_status_string",
     "fq_last_error", "fq_version",
 )
 
@@ -89,9 +89,13 @@ def lib() -> ctypes.CDLL:
         L.fq_qlinear_workspace_size.restype = sz
         L.fq_qlinear_fwd.argtypes = [dp, dp, vp, vp, i64, i64, i64, vp, vp, sz, vp]
         L.fq_qlinear_fwd.restype = ctypes.c_int
-        L.fq_qlinear_bwd_workspace_size.argtypes = [dp, dp, dp, i64, i64, i64]
+        i32, u64 = ctypes.c_int32, ctypes.c_uint64
+        L.fq_hadamard.argtypes = [vp, i64, i64, i32, i32, u64, vp, vp]
+        L.fq_hadamard.restype = ctypes.c_int
+        L.fq_qlinear_bwd_workspace_size.argtypes = [dp, dp, dp, i32, i64, i64, i64]
         L.fq_qlinear_bwd_workspace_size.restype = sz
-        L.fq_qlinear_bwd.argtypes = [dp, dp, dp, vp, vp, vp, i64, i64, i64, vp, vp, vp, sz, vp]
+        L.fq_qlinear_bwd.argtypes = [dp, dp, dp, i32, u64, vp, vp, vp, i64, i64, i64, vp, vp, vp,
+                                     sz, vp]
         L.fq_qlinear_bwd.restype = ctypes.c_int
         L.fq_status_string.argtypes = [ctypes.c_int]
         L.fq_status_string.restype = ctypes.c_char_p
@@ -274,17 +278,28 @@ def fq_qlinear_fwd(desc_x: FqDesc, desc_w: FqDesc, x, w, y=None, ws=None, stream
     return y
 
 
+def fq_hadamard(x, block: int, axis: int = FQ_AXIS_ROW, seed: int = 0, y=None, stream=None):
+    """Random Hadamard transform of a [R, C] BF16 tensor in blocks of 16 or 128."""
+    torch = _torch()
+    rows, cols = x.shape
+    if y is None:
+        y = torch.empty_like(x)
+    _check(lib().fq_hadamard(_ptr(x), rows, cols, axis, block, seed, _ptr(y), _stream(stream)))
+    return y
+
+
 def qlinear_bwd_workspace(desc_x: FqDesc, desc_w: FqDesc, desc_g: FqDesc, M: int, K: int,
-                          N: int, device):
+                          N: int, device, rht_block: int = 0):
     torch = _torch()
     n = lib().fq_qlinear_bwd_workspace_size(ctypes.byref(desc_x), ctypes.byref(desc_w),
-                                            ctypes.byref(desc_g), M, K, N)
+                                            ctypes.byref(desc_g), rht_block, M, K, N)
     return torch.empty((n,), dtype=torch.uint8, device=device)
 
 
 def fq_qlinear_bwd(desc_x: FqDesc, desc_w: FqDesc, desc_g: FqDesc, x, w, dy, dx=None, dw=None,
-                   ws=None, stream=None):
-    """(dX [M, K], dW [K, N]) of Y = FQ(X) @ FQ(W) for the upstream gradient dY [M, N]."""
+                   ws=None, stream=None, rht_block: int = 0, rht_seed: int = 0):
+    """(dX [M, K], dW [K, N]) of Y = FQ(X) @ FQ(W) for the upstream gradient dY [M, N];
+    rht_block 16/128 rotates each product's operands by the random Hadamard transform."""
     torch = _torch()
     M, K = x.shape
     K2, N = w.shape
@@ -295,10 +310,10 @@ def fq_qlinear_bwd(desc_x: FqDesc, desc_w: FqDesc, desc_g: FqDesc, x, w, dy, dx=
     if dw is None:
         dw = torch.empty((K, N), dtype=torch.bfloat16, device=x.device)
     if ws is None:
-        ws = qlinear_bwd_workspace(desc_x, desc_w, desc_g, M, K, N, x.device)
+        ws = qlinear_bwd_workspace(desc_x, desc_w, desc_g, M, K, N, x.device, rht_block)
     _check(lib().fq_qlinear_bwd(ctypes.byref(desc_x), ctypes.byref(desc_w), ctypes.byref(desc_g),
-                                _ptr(x), _ptr(w), _ptr(dy), M, K, N, _ptr(dx), _ptr(dw), _ptr(ws),
-                                ws.numel(), _stream(stream)))
+                                rht_block, rht_seed, _ptr(x), _ptr(w), _ptr(dy), M, K, N,
+                                _ptr(dx), _ptr(dw), _ptr(ws), ws.numel(), _stream(stream)))
     return dx, dw
 
 

@@ -347,10 +347,11 @@ fq_status fq_qlinear_fwd(const fq_desc *desc_x, const fq_desc *desc_w, const voi
 // qlinear backward workspace regions, in order (each rounded up to 256 B).
 struct BwdLayout {
     size_t xhat, xsc, xout, what, wsc, wout, dyq_n, wq_n, xq_mt, dyq_mt, dx_raw, dw_raw, parts,
-        total;
+        rdy_n, rw_n, rx_m, rdy_m, total;
 };
 
-static BwdLayout bwd_layout(const Fmt &fx, const Fmt &fw, int64_t M, int64_t K, int64_t N)
+static BwdLayout bwd_layout(const Fmt &fx, const Fmt &fw, bool rht, int64_t M, int64_t K,
+                            int64_t N)
 {
     BwdLayout L;
     size_t off = 0;
@@ -373,19 +374,53 @@ static BwdLayout bwd_layout(const Fmt &fx, const Fmt &fw, int64_t M, int64_t K, 
     L.dx_raw = take(mk * 2);
     L.dw_raw = take(kn * 2);
     L.parts = take(fqimpl::kAbsmaxPartials * sizeof(uint32_t));
+    // rotated operands (random Hadamard transform), only when requested
+    L.rdy_n = take(rht ? mn * 2 : 0);
+    L.rw_n = take(rht ? kn * 2 : 0);
+    L.rx_m = take(rht ? mk * 2 : 0);
+    L.rdy_m = take(rht ? mn * 2 : 0);
     L.total = off;
     return L;
 }
 
 size_t fq_qlinear_bwd_workspace_size(const fq_desc *desc_x, const fq_desc *desc_w,
-                                     const fq_desc *desc_g, int64_t M, int64_t K, int64_t N)
+                                     const fq_desc *desc_g, int32_t rht_block, int64_t M,
+                                     int64_t K, int64_t N)
 {
     Fmt fx, fw, fg;
     if (check_desc(desc_x, &fx, "desc_x") != FQ_OK || check_desc(desc_w, &fw, "desc_w") != FQ_OK ||
         check_desc(desc_g, &fg, "desc_g") != FQ_OK)
         return 0;
+    if (rht_block != 0 && rht_block != 16 && rht_block != 128) return 0;
     if (M < 1 || K < 1 || N < 1 || M > kMaxElems || K > kMaxElems || N > kMaxElems) return 0;
-    return bwd_layout(fx, fw, M, K, N).total;
+    return bwd_layout(fx, fw, rht_block != 0, M, K, N).total;
+}
+
+fq_status fq_hadamard(const void *x_bf16, int64_t rows, int64_t cols, int32_t axis,
+                      int32_t block, uint64_t seed, void *y_bf16, void *stream)
+{
+    if (axis != FQ_AXIS_ROW && axis != FQ_AXIS_COL)
+        return fail(FQ_ERR_DESC, "axis=%d is not FQ_AXIS_ROW/COL", axis);
+    if (block != 16 && block != 128) return fail(FQ_ERR_DESC, "block=%d is not 16 or 128", block);
+    if (rows < 1 || cols < 1) return fail(FQ_ERR_SHAPE, "rows=%lld cols=%lld must be >= 1",
+                                          (long long)rows, (long long)cols);
+    if (rows > kMaxElems || cols > kMaxElems || rows * cols > kMaxElems)
+        return fail(FQ_ERR_SHAPE, "rows*cols exceeds 2^34 elements");
+    const int64_t q = axis == FQ_AXIS_ROW ? cols : rows;
+    if (q % block != 0)
+        return fail(FQ_ERR_SHAPE, "%s=%lld must be a multiple of the block %d",
+                    axis == FQ_AXIS_ROW ? "cols" : "rows", (long long)q, block);
+    if (axis == FQ_AXIS_COL && cols % 8 != 0)
+        return fail(FQ_ERR_SHAPE, "cols=%lld must be a multiple of 8 for FQ_AXIS_COL",
+                    (long long)cols);
+    FQ_TRY(check_ptr(x_bf16, "x", true));
+    FQ_TRY(check_ptr(y_bf16, "y", true));
+    const char *xb = (const char *)x_bf16, *yb = (const char *)y_bf16;
+    const size_t bytes = (size_t)rows * cols * 2;
+    if (xb < yb + bytes && yb < xb + bytes) return fail(FQ_ERR_SHAPE, "x and y overlap");
+    return device_status(fqimpl::launch_hadamard(x_bf16, rows, cols, axis == FQ_AXIS_COL, block,
+                                                 seed, y_bf16, false, (hipStream_t)stream),
+                         "hadamard launch");
 }
 
 // One quantizer pass of the backward: src [R, C] along rows (col = false,
@@ -419,9 +454,9 @@ static fq_status bwd_quant(const Fmt &f, const fq_desc *d, uint64_t seed, bool c
 }
 
 fq_status fq_qlinear_bwd(const fq_desc *desc_x, const fq_desc *desc_w, const fq_desc *desc_g,
-                         const void *x_bf16, const void *w_bf16, const void *dy_bf16, int64_t M,
-                         int64_t K, int64_t N, void *dx_bf16, void *dw_bf16, void *ws,
-                         size_t ws_bytes, void *stream)
+                         int32_t rht_block, uint64_t rht_seed, const void *x_bf16,
+                         const void *w_bf16, const void *dy_bf16, int64_t M, int64_t K, int64_t N,
+                         void *dx_bf16, void *dw_bf16, void *ws, size_t ws_bytes, void *stream)
 {
     Fmt fx, fw, fg;
     FQ_TRY(check_desc(desc_x, &fx, "desc_x"));
@@ -444,6 +479,11 @@ fq_status fq_qlinear_bwd(const fq_desc *desc_x, const fq_desc *desc_w, const fq_
     if (M % 64 != 0 || N % 64 != 0)
         return fail(FQ_ERR_SHAPE, "M=%lld and N=%lld must be multiples of 64 (contractions)",
                     (long long)M, (long long)N);
+    if (rht_block != 0 && rht_block != 16 && rht_block != 128)
+        return fail(FQ_ERR_DESC, "rht_block=%d is not 0, 16 or 128", rht_block);
+    if (rht_block != 0 && (M % rht_block != 0 || N % rht_block != 0))
+        return fail(FQ_ERR_SHAPE, "M=%lld and N=%lld must be multiples of rht_block=%d",
+                    (long long)M, (long long)N, rht_block);
     if (M * N > kMaxElems)
         return fail(FQ_ERR_SHAPE, "M*N exceeds 2^34 elements");
     FQ_TRY(check_ptr(x_bf16, "x", true));
@@ -452,7 +492,8 @@ fq_status fq_qlinear_bwd(const fq_desc *desc_x, const fq_desc *desc_w, const fq_
     FQ_TRY(check_ptr(dx_bf16, "dx", true));
     FQ_TRY(check_ptr(dw_bf16, "dw", true));
     FQ_TRY(check_ptr(ws, "ws", true));
-    const BwdLayout L = bwd_layout(fx, fw, M, K, N);
+    const bool rht = rht_block != 0;
+    const BwdLayout L = bwd_layout(fx, fw, rht, M, K, N);
     if (ws_bytes < L.total)
         return fail(FQ_ERR_WORKSPACE, "workspace %zu bytes < %zu required", ws_bytes, L.total);
 
@@ -466,16 +507,32 @@ fq_status fq_qlinear_bwd(const fq_desc *desc_x, const fq_desc *desc_w, const fq_
                      b + L.xsc, (float *)(b + L.xout), parts, st));
     FQ_TRY(bwd_quant(fw, desc_w, desc_w->seed, true, w_bf16, K, N, b + L.what, nullptr,
                      b + L.wsc, (float *)(b + L.wout), parts, st));
+    // the operands before quantization, rotated along each contraction axis
+    const void *op_dy_n = dy_bf16, *op_w_n = b + L.what, *op_x_m = b + L.xhat, *op_dy_m = dy_bf16;
+    if (rht) {
+        struct { const void *src; int64_t R, C; int col; size_t dst; } rot[4] = {
+            {dy_bf16, M, N, 0, L.rdy_n}, {b + L.what, K, N, 0, L.rw_n},
+            {b + L.xhat, M, K, 1, L.rx_m}, {dy_bf16, M, N, 1, L.rdy_m}};
+        for (const auto &r : rot) {
+            hipError_t e = fqimpl::launch_hadamard(r.src, r.R, r.C, r.col, rht_block, rht_seed,
+                                                   b + r.dst, true, st);
+            if (e != hipSuccess) return device_status(e, "hadamard launch");
+        }
+        op_dy_n = b + L.rdy_n;
+        op_w_n = b + L.rw_n;
+        op_x_m = b + L.rx_m;
+        op_dy_m = b + L.rdy_m;
+    }
     // operands of dX = STE_X(Q(dY) . Q(W_hat)^T), both quantized along N
-    FQ_TRY(bwd_quant(fg, desc_g, sg + 0, false, dy_bf16, M, N, b + L.dyq_n, nullptr, nullptr,
+    FQ_TRY(bwd_quant(fg, desc_g, sg + 0, false, op_dy_n, M, N, b + L.dyq_n, nullptr, nullptr,
                      nullptr, parts, st));
-    FQ_TRY(bwd_quant(fg, desc_g, sg + 1, false, b + L.what, K, N, b + L.wq_n, nullptr, nullptr,
+    FQ_TRY(bwd_quant(fg, desc_g, sg + 1, false, op_w_n, K, N, b + L.wq_n, nullptr, nullptr,
                      nullptr, parts, st));
     // operands of dW = STE_W(Q(X_hat)^T . Q(dY)), both quantized along M,
     // written transposed
-    FQ_TRY(bwd_quant(fg, desc_g, sg + 2, true, b + L.xhat, M, K, nullptr, b + L.xq_mt, nullptr,
+    FQ_TRY(bwd_quant(fg, desc_g, sg + 2, true, op_x_m, M, K, nullptr, b + L.xq_mt, nullptr,
                      nullptr, parts, st));
-    FQ_TRY(bwd_quant(fg, desc_g, sg + 3, true, dy_bf16, M, N, nullptr, b + L.dyq_mt, nullptr,
+    FQ_TRY(bwd_quant(fg, desc_g, sg + 3, true, op_dy_m, M, N, nullptr, b + L.dyq_mt, nullptr,
                      nullptr, parts, st));
     // both products in one launch, then the two STE masks
     hipError_t e = fqimpl::launch_gemm_bf16_nt_pair(b + L.dyq_n, b + L.wq_n, b + L.dx_raw, M, K, N,

@@ -1,0 +1,201 @@
+// fq_hadamard.hip -- random Hadamard transform of BF16 tensors on gfx950.
+//
+// "Resumo Tecnico: TetraJet-v2", sec. 2.C (OutControl): the products of the
+// backward pass are computed on operands rotated by a random Hadamard
+// transform, which spreads the energy of outlier channels before the FP4
+// quantizer sees them.  Rotating both operands of a product along its
+// contraction axis by the same orthogonal (H S / sqrt(n)) leaves the product
+// unchanged in exact arithmetic.
+//
+// Definition (blocks of n = 16 or 128 consecutive elements along the axis):
+//   s_j = -1 where bit (j mod 128) of Philox4x32-10(key = seed,
+//         counter = (j / 128, 0, 0, 0)) is set, bit t of word w being bit
+//         32w + t; j is the position along the transformed axis;
+//   v   = s o x, widened to FP32 (exact);
+//   radix-2 butterflies in FP32, half-widths h = 1, 2, ..., n/2, each pair
+//   (i, i + h) of a 2h-group -> (a + b, a - b)  (Sylvester order);
+//   y   = BF16_RNE(RN32(c_n * v)), c_n the FP32 value nearest to 1/sqrt(n).
+//
+// Row axis: a lane owns 16 consecutive elements of a row (two 16-byte loads);
+// the first four butterfly stages stay in the lane, and for n = 128 the last
+// three pair lanes 1, 2 and 4 apart (a 128-element block is 8 consecutive
+// lanes).  Column axis: a lane owns 8 columns of 16 consecutive rows (sixteen
+// 16-byte row loads, the quantizer's column tile); the stages run down each
+// column, crossing lanes 1, 2 and 4 apart for n = 128.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fq_device.hpp"
+#include "fq_internal.h"
+
+namespace {
+
+using namespace fqdev;
+
+constexpr int kThreads = 256;
+
+typedef uint32_t u32v4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void st_out(uint4 *p, const uint4 &v, bool nt)
+{
+    if (nt) __builtin_nontemporal_store((u32v4){v.x, v.y, v.z, v.w}, reinterpret_cast<u32v4 *>(p));
+    else *p = v;
+}
+
+// The 16 sign bits of positions j0 .. j0 + 15 (j0 a multiple of 16).
+__device__ __forceinline__ uint32_t sign_bits16(uint64_t j0, uint32_t seed_lo, uint32_t seed_hi)
+{
+    const u32x4 o = philox4x32_10((uint32_t)(j0 >> 7), (uint32_t)(j0 >> 39), 0u, 0u, seed_lo,
+                                  seed_hi);
+    const uint32_t b = (uint32_t)(j0 & 127);
+    const uint32_t w = o.v[b >> 5];
+    return (w >> (b & 31)) & 0xFFFFu;
+}
+
+// In-lane stages h = 1, 2, 4, 8 over 16 values.
+__device__ __forceinline__ void fwht16(float (&v)[16])
+{
+#pragma unroll
+    for (int h = 1; h < 16; h *= 2)
+#pragma unroll
+        for (int g = 0; g < 16; g += 2 * h)
+#pragma unroll
+            for (int t = g; t < g + h; ++t) {
+                const float a = v[t], b = v[t + h];
+                v[t] = a + b;
+                v[t + h] = a - b;
+            }
+}
+
+// Cross-lane stages for n = 128: lane offsets 1, 2, 4 (element half-widths
+// 16, 32, 64).  The lower lane of a pair keeps a + b, the upper a - b, with a
+// the lower lane's value.
+__device__ __forceinline__ void fwht_lanes(float (&v)[16], uint32_t lane_in_block)
+{
+#pragma unroll
+    for (int d = 1; d < 8; d *= 2) {
+        const bool upper = (lane_in_block & d) != 0;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const float p = __shfl_xor(v[i], d);
+            v[i] = upper ? (p - v[i]) : (v[i] + p);
+        }
+    }
+}
+
+__device__ __forceinline__ float flip(float e, uint32_t bits, int i)
+{
+    return as_f(as_u(e) ^ (((bits >> i) & 1u) << 31));
+}
+
+template <int N>
+__global__ __launch_bounds__(kThreads) void k_hadamard_row(const uint4 *__restrict__ x,
+                                                           uint32_t nseg, uint32_t C,
+                                                           uint4 *__restrict__ y, float c_n,
+                                                           uint32_t seed_lo, uint32_t seed_hi,
+                                                           int nt)
+{
+    for (uint32_t u = blockIdx.x * kThreads + threadIdx.x; u < nseg; u += gridDim.x * kThreads) {
+        const uint4 a = x[2 * u], b = x[2 * u + 1];
+        const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+        const uint64_t col0 = ((uint64_t)u * 16) % C;
+        const uint32_t bits = sign_bits16(col0, seed_lo, seed_hi);
+        float v[16];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            v[2 * i] = flip(as_f(lo_bits(w[i])), bits, 2 * i);
+            v[2 * i + 1] = flip(as_f(hi_bits(w[i])), bits, 2 * i + 1);
+        }
+        fwht16(v);
+        if (N == 128) fwht_lanes(v, (uint32_t)(col0 >> 4) & 7);
+        uint32_t o[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) o[i] = bf16_pair_rne(c_n * v[2 * i], c_n * v[2 * i + 1]);
+        st_out(&y[2 * u], make_uint4(o[0], o[1], o[2], o[3]), nt);
+        st_out(&y[2 * u + 1], make_uint4(o[4], o[5], o[6], o[7]), nt);
+    }
+}
+
+// Column tile as the column quantizer's: 8 columns x 16 rows per lane, 8
+// lanes stacking 128 rows, a workgroup 64 columns x 512 rows.
+template <int N>
+__global__ __launch_bounds__(kThreads) void k_hadamard_col(const uint4 *__restrict__ x,
+                                                           uint32_t R, uint32_t C,
+                                                           uint4 *__restrict__ y, float c_n,
+                                                           uint32_t seed_lo, uint32_t seed_hi,
+                                                           int nt)
+{
+    const uint32_t lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const uint32_t tiles_c = (C + 63) >> 6;
+    const uint32_t rb = lane & 7;
+    const uint32_t col0 = (blockIdx.x % tiles_c) * 64 + (lane >> 3) * 8;
+    const uint32_t row0 = (((blockIdx.x / tiles_c) * 4 + wave) * 8 + rb) * 16;
+    if (col0 >= C || row0 >= R) return;     // 128-row groups are valid together (R % N == 0)
+    const uint32_t ldx = C >> 3;
+    uint4 v[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) v[r] = x[(size_t)(row0 + r) * ldx + (col0 >> 3)];
+    const uint32_t bits = sign_bits16(row0, seed_lo, seed_hi);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        float lo[16], hi[16];      // columns 2k and 2k+1 down the 16 rows
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const uint32_t wd = k == 0 ? v[r].x : k == 1 ? v[r].y : k == 2 ? v[r].z : v[r].w;
+            lo[r] = flip(as_f(lo_bits(wd)), bits, r);
+            hi[r] = flip(as_f(hi_bits(wd)), bits, r);
+        }
+        fwht16(lo);
+        fwht16(hi);
+        if (N == 128) {
+            fwht_lanes(lo, rb);
+            fwht_lanes(hi, rb);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const uint32_t wd = bf16_pair_rne(c_n * lo[r], c_n * hi[r]);
+            if (k == 0) v[r].x = wd;
+            else if (k == 1) v[r].y = wd;
+            else if (k == 2) v[r].z = wd;
+            else v[r].w = wd;
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) st_out(&y[(size_t)(row0 + r) * ldx + (col0 >> 3)], v[r], nt != 0);
+}
+
+}  // namespace
+
+namespace fqimpl {
+
+hipError_t launch_hadamard(const void *x, int64_t R, int64_t C, int col, int n, uint64_t seed,
+                           void *y, bool cached, hipStream_t st)
+{
+    const float c_n = n == 16 ? 0.25f : __builtin_bit_cast(float, 0x3DB504F3u);
+    const uint32_t slo = (uint32_t)seed, shi = (uint32_t)(seed >> 32);
+    const int nt = cached ? 0 : 1;
+    if (!col) {
+        const uint64_t nseg = (uint64_t)R * C / 16;
+        uint64_t g = (nseg + kThreads - 1) / kThreads;
+        if (g > (1u << 20)) g = 1u << 20;
+        if (n == 16)
+            hipLaunchKernelGGL(k_hadamard_row<16>, dim3((uint32_t)g), dim3(kThreads), 0, st,
+                               (const uint4 *)x, (uint32_t)nseg, (uint32_t)C, (uint4 *)y, c_n, slo,
+                               shi, nt);
+        else
+            hipLaunchKernelGGL(k_hadamard_row<128>, dim3((uint32_t)g), dim3(kThreads), 0, st,
+                               (const uint4 *)x, (uint32_t)nseg, (uint32_t)C, (uint4 *)y, c_n, slo,
+                               shi, nt);
+    } else {
+        const dim3 grid((uint32_t)(((C + 63) / 64) * ((R + 511) / 512)));
+        if (n == 16)
+            hipLaunchKernelGGL(k_hadamard_col<16>, grid, dim3(kThreads), 0, st, (const uint4 *)x,
+                               (uint32_t)R, (uint32_t)C, (uint4 *)y, c_n, slo, shi, nt);
+        else
+            hipLaunchKernelGGL(k_hadamard_col<128>, grid, dim3(kThreads), 0, st, (const uint4 *)x,
+                               (uint32_t)R, (uint32_t)C, (uint4 *)y, c_n, slo, shi, nt);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace fqimpl

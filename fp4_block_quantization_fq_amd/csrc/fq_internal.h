@@ -39,6 +39,10 @@ hipError_t launch_dequant(int fmt, int col, const void *codes, const void *scale
 hipError_t launch_ste(int fmt, int col, const void *x, const void *scales,
                       const float *outer, const void *dy, int64_t R, int64_t C,
                       void *dx, hipStream_t stream);
+// Random Hadamard transform of x [R, C] in blocks of n (16 or 128) along the
+// rows (col = 0) or the columns (col = 1) into y (same layout).
+hipError_t launch_hadamard(const void *x, int64_t R, int64_t C, int col, int n, uint64_t seed,
+                           void *y, bool cached, hipStream_t stream);
 hipError_t launch_gemm_bf16_nt(const void *a, const void *bt, void *c, int64_t M,
                                int64_t N, int64_t K, hipStream_t stream);
 // Two independent products C0 = A0 * Bt0^T and C1 = A1 * Bt1^T in one launch.

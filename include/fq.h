@@ -182,11 +182,26 @@ fq_status fq_qlinear_fwd(const fq_desc *desc_x, const fq_desc *desc_w,
                          int64_t K, int64_t N, void *y_bf16, void *ws,
                          size_t ws_bytes, void *stream);
 
+/* Random Hadamard transform: y = BF16_RNE(RN32(c_n * H_n (s o x))) in
+ * blocks of n = 16 or 128 consecutive elements along `axis` (FQ_AXIS_ROW:
+ * along each row; FQ_AXIS_COL: down each column), where H_n is the Hadamard
+ * matrix in Sylvester order applied by radix-2 FP32 butterflies (half-widths
+ * 1, 2, ..., n/2; a pair (a, b) becomes (a + b, a - b)), c_n the FP32 value
+ * nearest to 1/sqrt(n), and s_j = -1 where bit (j mod 128) of
+ * Philox4x32-10(key = seed, counter = (j / 128, 0, 0, 0)) is set (bit t of
+ * output word w counts as bit 32w + t), j the position along the axis.
+ * x, y: device [rows, cols] BF16, 16-byte aligned, not overlapping.  The
+ * transformed axis must be a multiple of n; FQ_AXIS_COL needs cols % 8 == 0.
+ * Source: "Resumo Tecnico: TetraJet-v2", sec. 2.C (OutControl: a random
+ * Hadamard transform on the backward's products spreads outlier energy). */
+fq_status fq_hadamard(const void *x_bf16, int64_t rows, int64_t cols, int32_t axis,
+                      int32_t block, uint64_t seed, void *y_bf16, void *stream);
+
 /* Workspace for fq_qlinear_bwd (internal layout; the size depends only on
  * the arguments). */
 size_t fq_qlinear_bwd_workspace_size(const fq_desc *desc_x, const fq_desc *desc_w,
-                                     const fq_desc *desc_g, int64_t M, int64_t K,
-                                     int64_t N);
+                                     const fq_desc *desc_g, int32_t rht_block, int64_t M,
+                                     int64_t K, int64_t N);
 
 /* QAT linear backward of fq_qlinear_fwd (Y = FQ(X) x FQ(W), X [M, K],
  * W [K, N]), given dY [M, N]:
@@ -198,23 +213,28 @@ size_t fq_qlinear_bwd_workspace_size(const fq_desc *desc_x, const fq_desc *desc_
  * STE_X / STE_W pass a gradient entry where the forward did not clip that
  * entry of X / W (a <= 6) and write +0 where it did.  The four Q draws use
  * Philox keys desc_g->seed + 0 (dY along N), + 1 (W_hat along N), + 2 (X_hat
- * along M), + 3 (dY along M); desc_g->axis is ignored.  Products accumulate
+ * along M), + 3 (dY along M); desc_g->axis is ignored.  rht_block = 16 or
+ * 128 first rotates both operands of each product along its contraction axis
+ * by the random Hadamard transform of fq_hadamard with seed rht_seed (which
+ * cancels in the exact product); 0 leaves them as they are.  Products accumulate
  * in FP32 on the matrix cores and are rounded to BF16 before the STE.
  * Shapes: K a multiple of 8 and of desc_x's and desc_w's block sizes (128
  * for FQ_OUTER_BLOCK128); M and N multiples of 64 and of desc_g's block size
- * (128 for FQ_OUTER_BLOCK128); desc_x->axis FQ_AXIS_ROW, desc_w->axis
- * FQ_AXIS_COL as in the forward.
+ * (128 for FQ_OUTER_BLOCK128) and of rht_block; desc_x->axis FQ_AXIS_ROW,
+ * desc_w->axis FQ_AXIS_COL as in the forward.
  * Pointers x, w, dy, dx, dw, ws: device, 16-byte aligned, caller-owned; ws
  * at least fq_qlinear_bwd_workspace_size bytes.  Errors as fq_qlinear_fwd.
  * Source: TetraJet-v2, sec. 2.A (the backward computes on the aligned X_hat,
  * with stochastic rounding so that E[round(x)] = x, and 1x16 weight groups
- * realigned for the transposed weight); "Como o Treinamento ...", "Detalhes
- * tecnicos" (gradients pass the quantizer by STE, clipping effects). */
+ * realigned for the transposed weight) and sec. 2.C (random Hadamard
+ * transform of the backward's products); "Como o Treinamento ...",
+ * "Detalhes tecnicos" (gradients pass the quantizer by STE, clipping
+ * effects). */
 fq_status fq_qlinear_bwd(const fq_desc *desc_x, const fq_desc *desc_w,
-                         const fq_desc *desc_g, const void *x_bf16, const void *w_bf16,
-                         const void *dy_bf16, int64_t M, int64_t K, int64_t N,
-                         void *dx_bf16, void *dw_bf16, void *ws, size_t ws_bytes,
-                         void *stream);
+                         const fq_desc *desc_g, int32_t rht_block, uint64_t rht_seed,
+                         const void *x_bf16, const void *w_bf16, const void *dy_bf16,
+                         int64_t M, int64_t K, int64_t N, void *dx_bf16, void *dw_bf16,
+                         void *ws, size_t ws_bytes, void *stream);
 
 /* Static description of a status code. */
 const char *fq_status_string(fq_status s);

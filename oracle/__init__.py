@@ -287,7 +287,8 @@ def _clip_keep(x: np.ndarray, q: dict, fmt: str, axis: str) -> np.ndarray:
 def qlinear_bwd(x: np.ndarray, w: np.ndarray, dy: np.ndarray, fmt_x: str = "nv_tensor",
                 fmt_w: str = "nv_tensor", fmt_g: str = "nv_128", rounding_g: str = "sr",
                 seed_g: int = 0, rounding_x: str = "rne", rounding_w: str = "rne",
-                seed_x: int = 0, seed_w: int = 0, nthreads: int | None = None) -> dict:
+                seed_x: int = 0, seed_w: int = 0, rht_block: int = 0, rht_seed: int = 0,
+                nthreads: int | None = None) -> dict:
     """QAT linear backward of Y = FQ(X) @ FQ(W) (TetraJet-v2 sec. 2.A).
 
     X_hat = FQ(X) along K and W_hat = FQ(W) along K are the forward operands.
@@ -296,16 +297,22 @@ def qlinear_bwd(x: np.ndarray, w: np.ndarray, dy: np.ndarray, fmt_x: str = "nv_t
         dX = keep_X * (Q(dY, along N) @ Q(W_hat, along N)^T)     [M, K]
         dW = keep_W * (Q(X_hat, along M)^T @ Q(dY, along M))     [K, N]
     with Philox keys seed_g + 0, + 1, + 2, + 3 for the four Q in that order,
-    and keep_* the STE masks of the forward (1 where a <= 6).  The products
-    are float64 (numpy matmul as the contraction step).
+    and keep_* the STE masks of the forward (1 where a <= 6).  With rht_block
+    16 or 128 each Q's input is first rotated along that Q's axis by the
+    random Hadamard transform (seed rht_seed; TetraJet-v2 sec. 2.C).  The
+    products are float64 (numpy matmul as the contraction step).
     """
     fx = fake_quant(x, fmt_x, rounding_x, "row", seed_x, nthreads)
     fw = fake_quant(w, fmt_w, rounding_w, "col", seed_w, nthreads)
     m64 = (1 << 64) - 1
-    q_dy_n = fake_quant(dy, fmt_g, rounding_g, "row", (seed_g + 0) & m64, nthreads)
-    q_w_n = fake_quant(fw["y"], fmt_g, rounding_g, "row", (seed_g + 1) & m64, nthreads)
-    q_x_m = fake_quant(fx["y"], fmt_g, rounding_g, "col", (seed_g + 2) & m64, nthreads)
-    q_dy_m = fake_quant(dy, fmt_g, rounding_g, "col", (seed_g + 3) & m64, nthreads)
+    rot = (lambda t, ax: hadamard(t, rht_block, ax, rht_seed, nthreads)) if rht_block else \
+        (lambda t, ax: t)
+    q_dy_n = fake_quant(rot(dy, "row"), fmt_g, rounding_g, "row", (seed_g + 0) & m64, nthreads)
+    q_w_n = fake_quant(rot(fw["y"], "row"), fmt_g, rounding_g, "row", (seed_g + 1) & m64,
+                       nthreads)
+    q_x_m = fake_quant(rot(fx["y"], "col"), fmt_g, rounding_g, "col", (seed_g + 2) & m64,
+                       nthreads)
+    q_dy_m = fake_quant(rot(dy, "col"), fmt_g, rounding_g, "col", (seed_g + 3) & m64, nthreads)
     dx_raw = bf16_bits_to_f64(q_dy_n["y"]) @ bf16_bits_to_f64(q_w_n["y"]).T
     dw_raw = bf16_bits_to_f64(q_x_m["y"]).T @ bf16_bits_to_f64(q_dy_m["y"])
     keep_x = _clip_keep(x, fx, fmt_x, "row")

@@ -135,9 +135,9 @@ def test_qlinear_bwd_validates(L):
     g = fq.fq_desc_nvfp4(outer=fq.FQ_OUTER_BLOCK128, rounding=fq.FQ_ROUND_SR, seed=5)
     big = 1 << 40
 
-    def call(dx_, dw_, dg_, M=128, K=128, N=128, ws_bytes=big, x=fake(), dy=fake()):
-        return L.fq_qlinear_bwd(ctypes.byref(dx_), ctypes.byref(dw_), ctypes.byref(dg_), x,
-                                fake(), dy, M, K, N, fake(), fake(), fake(), ws_bytes, None)
+    def call(dx_, dw_, dg_, M=128, K=128, N=128, ws_bytes=big, x=fake(), dy=fake(), rht=0):
+        return L.fq_qlinear_bwd(ctypes.byref(dx_), ctypes.byref(dw_), ctypes.byref(dg_), rht, 7,
+                                x, fake(), dy, M, K, N, fake(), fake(), fake(), ws_bytes, None)
 
     assert call(col, col, g) == fq.FQ_ERR_DESC                  # X must be blocked along K (rows)
     assert call(nv, nv, g) == fq.FQ_ERR_DESC                    # W must be blocked along K (cols)
@@ -147,14 +147,32 @@ def test_qlinear_bwd_validates(L):
     assert call(nv, col, g, K=120) == fq.FQ_ERR_SHAPE           # K not a multiple of 16
     assert call(nv, col, g, x=None) == fq.FQ_ERR_NULL
     assert call(nv, col, g, dy=fake(0x10004)) == fq.FQ_ERR_ALIGN
+    assert call(nv, col, g, rht=32) == fq.FQ_ERR_DESC           # RHT blocks are 16 or 128
+    assert call(nv, col, nv, M=192, N=192, rht=128) == fq.FQ_ERR_SHAPE   # M % 128
     need = L.fq_qlinear_bwd_workspace_size(ctypes.byref(nv), ctypes.byref(col), ctypes.byref(g),
-                                           128, 128, 128)
+                                           0, 128, 128, 128)
     assert need > 6 * 128 * 128 * 2
     assert call(nv, col, g, ws_bytes=need - 1) == fq.FQ_ERR_WORKSPACE
+    need_r = L.fq_qlinear_bwd_workspace_size(ctypes.byref(nv), ctypes.byref(col), ctypes.byref(g),
+                                             128, 128, 128, 128)
+    assert need_r >= need + 4 * 128 * 128 * 2
+    assert call(nv, col, g, ws_bytes=need_r - 1, rht=128) == fq.FQ_ERR_WORKSPACE
     bad = fq.fq_desc_mxfp4()
     bad.reserved = 1
     assert L.fq_qlinear_bwd_workspace_size(ctypes.byref(nv), ctypes.byref(col), ctypes.byref(bad),
-                                           128, 128, 128) == 0
+                                           0, 128, 128, 128) == 0
+
+
+def test_hadamard_validates(L):
+    x, y = fake(0x10000), fake(0x40000)
+    assert L.fq_hadamard(x, 64, 96, fq.FQ_AXIS_ROW, 64, 1, y, None) == fq.FQ_ERR_DESC
+    assert L.fq_hadamard(x, 64, 96, 2, 16, 1, y, None) == fq.FQ_ERR_DESC
+    assert L.fq_hadamard(x, 64, 96, fq.FQ_AXIS_ROW, 128, 1, y, None) == fq.FQ_ERR_SHAPE
+    assert L.fq_hadamard(x, 96, 64, fq.FQ_AXIS_COL, 128, 1, y, None) == fq.FQ_ERR_SHAPE
+    assert L.fq_hadamard(x, 128, 12, fq.FQ_AXIS_COL, 16, 1, y, None) == fq.FQ_ERR_SHAPE
+    assert L.fq_hadamard(None, 64, 128, fq.FQ_AXIS_ROW, 16, 1, y, None) == fq.FQ_ERR_NULL
+    assert L.fq_hadamard(fake(0x10008), 64, 128, fq.FQ_AXIS_ROW, 16, 1, y, None) == fq.FQ_ERR_ALIGN
+    assert L.fq_hadamard(x, 64, 128, fq.FQ_AXIS_ROW, 16, 1, fake(0x10100), None) == fq.FQ_ERR_SHAPE
 
 
 def test_status_strings(L):
