@@ -42,6 +42,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+FP4_PEAK_TFLOPS = 10100.0       # MI355X dense FP4 matrix peak, TFLOP/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense BF16 MFMA, TFLOP/s
 METRIC = "FP4 fake-quant GB/s and % of HBM peak (MXFP4/NVFP4, 16384x4096 bf16)"
 ROWS, COLS = 16384, 4096
@@ -279,6 +280,29 @@ def main():
                 "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": BF16_PEAK_TFLOPS,
                              "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4)}}
 
+    # ---------------- the same linear with MXFP4 operands (FP4 matrix cores) ----------------
+    qmx = None
+    if not args.only:
+        log("bench: qlinear mxfp4")
+        dxm = fq.fq_desc_mxfp4()
+        dwm = fq.fq_desc_mxfp4(axis=fq.FQ_AXIS_COL)
+        for _ in range(3):
+            fq.fq_qlinear_fwd(dxm, dwm, xq, wq, y=yq, ws=qws)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.qlinear_iters):
+            fq.fq_qlinear_fwd(dxm, dwm, xq, wq, y=yq, ws=qws)
+        e1.record()
+        torch.cuda.synchronize()
+        mms = e0.elapsed_time(e1) / args.qlinear_iters
+        tfm = 2.0 * M * Kd * N / (mms * 1e-3) / 1e12
+        qmx = {"workload": "the same X @ W with both operands MXFP4 RNE: codes and E8M0 scales "
+                           "multiplied on the scaled FP4 matrix cores",
+               "ms": round(mms, 4), "TFLOPs": round(tfm, 1),
+               "roofline": {"bound": "mfma", "achieved": round(tfm, 1), "peak": FP4_PEAK_TFLOPS,
+                            "unit": "TFLOP/s", "frac": round(tfm / FP4_PEAK_TFLOPS, 4)}}
+
     # ---------------- QAT linear backward ----------------
     qbwd = None
     if not args.only:
@@ -384,6 +408,7 @@ def main():
         "cpu_baseline": cpu,
         "kernels": kernels,
         "qlinear": qlin,
+        "qlinear_mxfp4": qmx,
         "qlinear_bwd": qbwd,
         "hadamard": rht,
     }

@@ -262,6 +262,17 @@ def qlinear_workspace_views(ws, M: int, K: int, N: int):
     return xhat, what_t
 
 
+def qlinear_workspace_mx_views(ws, M: int, K: int, N: int):
+    """(X codes [M, K/2], X scales [M, K/32], W^T codes [N, K/2], W^T scales
+    [N, K/32]) in a qlinear workspace used by an MXFP4 x MXFP4 linear."""
+    r = lambda v: (v + 255) // 256 * 256
+    c1 = r(M * K // 2)
+    c2 = c1 + r(M * K // 32)
+    c3 = c2 + r(N * K // 2)
+    return (ws[: M * K // 2].view(M, K // 2), ws[c1: c1 + M * K // 32].view(M, K // 32),
+            ws[c2: c2 + N * K // 2].view(N, K // 2), ws[c3: c3 + N * K // 32].view(N, K // 32))
+
+
 def fq_qlinear_fwd(desc_x: FqDesc, desc_w: FqDesc, x, w, y=None, ws=None, stream=None):
     """Y [M, N] = FQ(X) @ FQ(W) (BF16 out, FP32 accumulation)."""
     torch = _torch()

@@ -268,6 +268,22 @@ fq_status fq_ste_backward(const fq_desc *desc, const void *x_bf16, const void *s
 // qlinear workspace: X_hat [M, K], W_hat^T [N, K] (BF16), reduction scratch.
 static size_t round256(size_t v) { return (v + 255) & ~size_t(255); }
 
+// The MXFP4 x MXFP4 linear keeps codes and scales instead of BF16 operands,
+// inside the same workspace: X codes [M, K/2], X scales [M, K/32], W codes
+// and scales in the transposed layout [N, K/2], [N, K/32].
+struct MxLinLayout {
+    size_t xc, xs, wc, wsc;
+};
+static MxLinLayout mx_lin_layout(int64_t M, int64_t K, int64_t N)
+{
+    MxLinLayout L;
+    L.xc = 0;
+    L.xs = round256((size_t)M * K / 2);
+    L.wc = L.xs + round256((size_t)M * K / 32);
+    L.wsc = L.wc + round256((size_t)N * K / 2);
+    return L;
+}
+
 size_t fq_qlinear_workspace_size(const fq_desc *desc_x, const fq_desc *desc_w, int64_t M,
                                  int64_t K, int64_t N)
 {
@@ -307,10 +323,46 @@ fq_status fq_qlinear_fwd(const fq_desc *desc_x, const fq_desc *desc_w, const voi
         return fail(FQ_ERR_WORKSPACE, "workspace %zu bytes < %zu required", ws_bytes, need);
 
     char *base = (char *)ws;
+    hipStream_t st = (hipStream_t)stream;
+    uint32_t *parts = (uint32_t *)(base + round256((size_t)M * K * 2) + round256((size_t)N * K * 2));
+
+    if (fx.fmt == fqimpl::FMT_MX && fw.fmt == fqimpl::FMT_MX && K % 64 == 0) {
+        // MXFP4 x MXFP4: the codes and E8M0 scales go straight to the scaled
+        // FP4 matrix cores, nothing is dequantized
+        const MxLinLayout L = mx_lin_layout(M, K, N);
+        FQ_TRY(run_quant(fx, desc_x, x_bf16, M, K, nullptr, base + L.xc, base + L.xs, nullptr,
+                         parts, st, /*cached=*/true));
+        fqimpl::QuantArgs a;
+        a.fmt = fw.fmt;
+        a.sr = desc_w->rounding == FQ_ROUND_SR;
+        a.col = 1;
+        a.seed = desc_w->seed;
+        a.x = w_bf16;
+        a.R = K;
+        a.C = N;
+        a.y = nullptr;
+        a.yt = nullptr;
+        a.codes = base + L.wc;
+        a.scales = base + L.wsc;
+        a.outer = nullptr;
+        a.partials = parts;
+        a.cached_outputs = true;
+        hipError_t e = fqimpl::launch_quant(a, 0, st);
+        if (e != hipSuccess) return device_status(e, "transposed quantize launch");
+        fqimpl::Fp4Operands o;
+        o.a_codes = base + L.xc;
+        o.a_scales = base + L.xs;
+        o.b_codes = base + L.wc;
+        o.b_scales = base + L.wsc;
+        o.c = y_bf16;
+        o.M = M;
+        o.N = N;
+        o.K = K;
+        return device_status(fqimpl::launch_gemm_mxfp4_nt_pair(o, o, 1, st), "fp4 gemm launch");
+    }
+
     void *xhat = base;
     char *what_t = base + round256((size_t)M * K * 2);
-    uint32_t *parts = (uint32_t *)(what_t + round256((size_t)N * K * 2));
-    hipStream_t st = (hipStream_t)stream;
 
     // X_hat = FQ(X) along K (rows of X)
     FQ_TRY(run_quant(fx, desc_x, x_bf16, M, K, xhat, nullptr, nullptr, nullptr, parts, st,

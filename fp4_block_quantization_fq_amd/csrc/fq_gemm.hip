@@ -29,6 +29,16 @@
 // One launch may carry two independent problems (the two products of the
 // backward): their tiles share the grid, the longer one first, so the chip
 // stays busy where either alone would leave a partial last wave.
+//
+// MXFP4 operands need no dequantization at all: gfx950's
+// v_mfma_scale_f32_32x32x64_f8f6f4 multiplies E2M1 codes directly and applies
+// one E8M0 scale per 32-element block of each operand row, which is exactly
+// the MXFP4 encoding (OCP Microscaling v1.0).  k_gemm_mxfp4_nt streams the
+// packed codes (16 bytes = one 32-element block = one fragment half) through
+// the same LDS tiles and swizzle as the BF16 kernel, 256 K-elements per stage
+// instead of 64, and stages each row's eight E8M0 scales of a stage in LDS.
+// The products of codes times powers of two are exact, so the result equals
+// the FP32-accumulated product of the dequantized operands.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -186,6 +196,189 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_nt(Problem p0, Problem p1)
         }
 }
 
+// ---------------------------------------------------------------------------
+// MXFP4 x MXFP4 on the scaled FP4 matrix cores
+// ---------------------------------------------------------------------------
+typedef int v8i __attribute__((ext_vector_type(8)));
+
+struct Fp4Problem {
+    const uint8_t *A;    // E2M1 codes [M, K/2], element 2i in the low nibble of byte i
+    const uint8_t *As;   // E8M0 scales [M, K/32]
+    const uint8_t *B;    // codes [N, K/2]
+    const uint8_t *Bs;   // scales [N, K/32]
+    uint16_t *C;         // BF16 [M, N]
+    int M, N, K;
+    int tiles;
+};
+
+constexpr int FK = 256;            // K elements per stage: 128 bytes of codes per row
+constexpr int FSB = FK / 32;       // E8M0 scales per row per stage
+
+// Direct loads of one ROWS-row code tile (128 bytes per row) into LDS, as
+// load_tile; chunks past the end of K load chunk 0 instead (never used).
+template <int ROWS>
+__device__ __forceinline__ void load_codes(const uint8_t *__restrict__ g, int row0, int nrows,
+                                           size_t pitch, size_t off0, int valid_chunks,
+                                           uint8_t *lds_tile, int wave, int lane)
+{
+    constexpr int PER_WAVE = ROWS / (kWavesM * kWavesN);
+#pragma unroll
+    for (int i = 0; i < PER_WAVE / 8; ++i) {
+        const int r = wave * PER_WAVE + i * 8 + (lane >> 3);
+        int c = swz(r, lane & 7);
+        if (c >= valid_chunks) c = 0;
+        const int gr = min(row0 + r, nrows - 1);
+        const uint8_t *src = g + (size_t)gr * pitch + off0 + c * 16;
+        uint8_t *dst = lds_tile + (wave * PER_WAVE + i * 8) * ROW_BYTES;
+        __builtin_amdgcn_global_load_lds((const void *)src, (lds_void *)dst, 16, 0, 0);
+    }
+}
+
+// The eight E8M0 scales of one operand row for stage kt (blocks past the end
+// of K read as 0; their products are never formed).  Rows past the end of the
+// operand are clamped like the codes.
+__device__ __forceinline__ uint2 load_scales(const uint8_t *__restrict__ s, int row, int nrows,
+                                             int nblk, int kt)
+{
+    const uint8_t *p = s + (size_t)min(row, nrows - 1) * nblk + kt * FSB;
+    const int have = min(FSB, nblk - kt * FSB);     // even: K is a multiple of 64
+    uint32_t w[2] = {0u, 0u};
+#pragma unroll
+    for (int q = 0; q < FSB / 2; ++q)
+        if (2 * q < have) {
+            const uint32_t h = *reinterpret_cast<const uint16_t *>(p + 2 * q);
+            w[q >> 1] |= h << (16 * (q & 1));
+        }
+    return make_uint2(w[0], w[1]);
+}
+
+__global__ __launch_bounds__(kThreads, 1) void k_gemm_mxfp4_nt(Fp4Problem p0, Fp4Problem p1)
+{
+    constexpr int WTM = BM / kWavesM, WTN = BN / kWavesN;
+    constexpr int TM = WTM / 32, TN = WTN / 32;
+    constexpr int A_BYTES = BM * ROW_BYTES, B_BYTES = BN * ROW_BYTES;
+    constexpr int STAGE = A_BYTES + B_BYTES;
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * STAGE];
+    __shared__ uint2 s_scale[2][BM + BN];            // per stage: A rows, then B rows
+
+    const bool second = (int)blockIdx.x >= p0.tiles;
+    const uint8_t *__restrict__ A = second ? p1.A : p0.A;
+    const uint8_t *__restrict__ As = second ? p1.As : p0.As;
+    const uint8_t *__restrict__ Bc = second ? p1.B : p0.B;
+    const uint8_t *__restrict__ Bs = second ? p1.Bs : p0.Bs;
+    uint16_t *__restrict__ C = second ? p1.C : p0.C;
+    const int M = second ? p1.M : p0.M, N = second ? p1.N : p0.N, K = second ? p1.K : p0.K;
+    const int b = second ? (int)blockIdx.x - p0.tiles : (int)blockIdx.x;
+
+    const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+    const int ntiles = tiles_m * tiles_n;
+    if (b >= ntiles) return;
+    int logical = b;
+    if (ntiles % kXcds == 0) logical = (b % kXcds) * (ntiles / kXcds) + b / kXcds;
+    const int group = 8;
+    const int tiles_per_group = group * tiles_n;
+    const int g = logical / tiles_per_group;
+    const int first_m = g * group;
+    const int gm = min(tiles_m - first_m, group);
+    const int in_g = logical % tiles_per_group;
+    const int tm = first_m + in_g % gm;
+    const int tn = in_g / gm;
+
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int wm = wave / kWavesN, wn = wave % kWavesN;
+    const int row_a0 = tm * BM, row_b0 = tn * BN;
+    const size_t pitch = (size_t)K / 2;
+    const int nblk = K / 32, nsub = K / 64;          // scale blocks, 64-element MFMA steps
+    const int nk = (K + FK - 1) / FK;
+    // this thread's scale row for the stage loads: A rows first, then B rows
+    const bool sc_b = tid >= BM;
+    const int sc_row = sc_b ? row_b0 + (tid - BM) : row_a0 + tid;
+
+    floatx16 acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+    auto issue_stage = [&](int kt, uint8_t *st) {
+        const int valid_chunks = min(8, (K - kt * FK) / 32);
+        load_codes<BM>(A, row_a0, M, pitch, (size_t)kt * (FK / 2), valid_chunks, st, wave, lane);
+        load_codes<BN>(Bc, row_b0, N, pitch, (size_t)kt * (FK / 2), valid_chunks, st + A_BYTES,
+                       wave, lane);
+    };
+    issue_stage(0, lds);
+    s_scale[0][tid] = sc_b ? load_scales(Bs, sc_row, N, nblk, 0) : load_scales(As, sc_row, M, nblk, 0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+
+    for (int kt = 0; kt < nk; ++kt) {
+        uint8_t *cur = lds + (kt & 1) * STAGE;
+        uint2 next_sc = make_uint2(0u, 0u);
+        if (kt + 1 < nk) {
+            issue_stage(kt + 1, lds + ((kt + 1) & 1) * STAGE);
+            next_sc = sc_b ? load_scales(Bs, sc_row, N, nblk, kt + 1)
+                           : load_scales(As, sc_row, M, nblk, kt + 1);
+        }
+        // this lane's scale words for the stage: its 4 A rows and 2 B rows
+        uint2 sa[TM], sb[TN];
+#pragma unroll
+        for (int i = 0; i < TM; ++i) sa[i] = s_scale[kt & 1][wm * WTM + i * 32 + (lane & 31)];
+#pragma unroll
+        for (int j = 0; j < TN; ++j) sb[j] = s_scale[kt & 1][BM + wn * WTN + j * 32 + (lane & 31)];
+        const uint8_t *sa_t = cur, *sb_t = cur + A_BYTES;
+#pragma unroll
+        for (int ks = 0; ks < FK / 64; ++ks) {
+            if (kt * (FK / 64) + ks >= nsub) break;         // uniform: the K tail
+            const int c = ks * 2 + (lane >> 5);               // 16-byte chunk = 32 codes
+            const int sh = 8 * (c & 3);
+            v8i af[TM], bfr[TN];
+            int sca[TM], scb[TN];
+#pragma unroll
+            for (int i = 0; i < TM; ++i) {
+                const int r = wm * WTM + i * 32 + (lane & 31);
+                const uint4 q = *reinterpret_cast<const uint4 *>(sa_t + r * ROW_BYTES + swz(r, c) * 16);
+                af[i] = (v8i){(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
+                sca[i] = (int)(((c < 4 ? sa[i].x : sa[i].y) >> sh) & 0xFFu);
+            }
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                const int r = wn * WTN + j * 32 + (lane & 31);
+                const uint4 q = *reinterpret_cast<const uint4 *>(sb_t + r * ROW_BYTES + swz(r, c) * 16);
+                bfr[j] = (v8i){(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
+                scb[j] = (int)(((c < 4 ? sb[j].x : sb[j].y) >> sh) & 0xFFu);
+            }
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                        af[i], bfr[j], acc[i][j], 4, 4, 0, sca[i], 0, scb[j]);
+        }
+        if (kt + 1 < nk) s_scale[(kt + 1) & 1][tid] = next_sc;
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+    }
+
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const int col = tn * BN + wn * WTN + j * 32 + (lane & 31);
+            if (col >= N) continue;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int row = tm * BM + wm * WTM + i * 32 + (v >> 2) * 8 +
+                                (lane >> 5) * 4 + (v & 3);
+                if (row < M) {
+                    __bf16 h = (__bf16)acc[i][j][v];
+                    C[(size_t)row * N + col] = __builtin_bit_cast(uint16_t, h);
+                }
+            }
+        }
+}
+
 int tile_count(int64_t M, int64_t N) { return (int)(((M + BM - 1) / BM) * ((N + BN - 1) / BN)); }
 
 Problem make_problem(const void *a, const void *bt, void *c, int64_t M, int64_t N, int64_t K)
@@ -231,6 +424,38 @@ hipError_t launch_gemm_bf16_nt_pair(const void *a0, const void *bt0, void *c0, i
     }
     p0.tiles = (p0.tiles + kXcds - 1) / kXcds * kXcds;
     hipLaunchKernelGGL(k_gemm_nt, dim3((uint32_t)(p0.tiles + p1.tiles)), dim3(kThreads), 0,
+                       stream, p0, p1);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_mxfp4_nt_pair(const Fp4Operands &o0, const Fp4Operands &o1, int count,
+                                     hipStream_t stream)
+{
+    auto mk = [](const Fp4Operands &o) {
+        Fp4Problem p;
+        p.A = (const uint8_t *)o.a_codes;
+        p.As = (const uint8_t *)o.a_scales;
+        p.B = (const uint8_t *)o.b_codes;
+        p.Bs = (const uint8_t *)o.b_scales;
+        p.C = (uint16_t *)o.c;
+        p.M = (int)o.M;
+        p.N = (int)o.N;
+        p.K = (int)o.K;
+        p.tiles = tile_count(o.M, o.N);
+        return p;
+    };
+    Fp4Problem p0 = mk(o0), p1 = mk(count > 1 ? o1 : o0);
+    if (count < 2) {
+        p1.tiles = 0;
+    } else {
+        if (p1.K > p0.K) {
+            const Fp4Problem t = p0;
+            p0 = p1;
+            p1 = t;
+        }
+        p0.tiles = (p0.tiles + kXcds - 1) / kXcds * kXcds;
+    }
+    hipLaunchKernelGGL(k_gemm_mxfp4_nt, dim3((uint32_t)(p0.tiles + p1.tiles)), dim3(kThreads), 0,
                        stream, p0, p1);
     return hipGetLastError();
 }

@@ -39,6 +39,17 @@ hipError_t launch_dequant(int fmt, int col, const void *codes, const void *scale
 hipError_t launch_ste(int fmt, int col, const void *x, const void *scales,
                       const float *outer, const void *dy, int64_t R, int64_t C,
                       void *dx, hipStream_t stream);
+// MXFP4 product on the scaled FP4 matrix cores: C [M, N] BF16 = A . B^T with
+// A given as E2M1 codes [M, K/2] and E8M0 scales [M, K/32], B as codes
+// [N, K/2] and scales [N, K/32]; K a multiple of 64.
+struct Fp4Operands {
+    const void *a_codes, *a_scales, *b_codes, *b_scales;
+    void *c;
+    int64_t M, N, K;
+};
+hipError_t launch_gemm_mxfp4_nt_pair(const Fp4Operands &o0, const Fp4Operands &o1, int count,
+                                     hipStream_t stream);
+
 // Random Hadamard transform of x [R, C] in blocks of n (16 or 128) along the
 // rows (col = 0) or the columns (col = 1) into y (same layout).
 hipError_t launch_hadamard(const void *x, int64_t R, int64_t C, int col, int n, uint64_t seed,

@@ -164,7 +164,12 @@ fq_status fq_ste_backward(const fq_desc *desc, const void *x_bf16,
 
 /* Workspace for fq_qlinear_fwd: the dequantized X_hat [M, K] BF16 at offset
  * 0, the dequantized and transposed W_hat^T [N, K] BF16 at offset
- * round_up(M * K * 2, 256), then 8192 bytes of reduction scratch. */
+ * round_up(M * K * 2, 256), then 8192 bytes of reduction scratch.  When both
+ * descriptors are MXFP4 and K is a multiple of 64, the operands stay encoded
+ * instead: X's codes [M, K/2] at 0, X's E8M0 scales [M, K/32] at
+ * c1 = round_up(M * K / 2, 256), W's codes in the transposed layout [N, K/2]
+ * at c2 = c1 + round_up(M * K / 32, 256), W's scales [N, K/32] at
+ * c2 + round_up(N * K / 2, 256) (same total size). */
 size_t fq_qlinear_workspace_size(const fq_desc *desc_x, const fq_desc *desc_w,
                                  int64_t M, int64_t K, int64_t N);
 
@@ -176,7 +181,10 @@ size_t fq_qlinear_workspace_size(const fq_desc *desc_x, const fq_desc *desc_w,
  * 128 for FQ_OUTER_BLOCK128); M, N >= 1; M * K and K * N <= 2^34.
  * Source: gpt-oss QAT tutorial, "NVFP4: The Next Generation"
  * (weight-activation quantization of the MLP); TetraJet-v2 sec. 2 (NVFP4
- * activations and weights in every linear layer). */
+ * activations and weights in every linear layer).  MXFP4 x MXFP4 (K % 64 ==
+ * 0) multiplies the E2M1 codes with their E8M0 block scales on the scaled FP4
+ * matrix cores (OCP Microscaling v1.0 block scaling), which is the same
+ * product of the same dequantized values. */
 fq_status fq_qlinear_fwd(const fq_desc *desc_x, const fq_desc *desc_w,
                          const void *x_bf16, const void *w_bf16, int64_t M,
                          int64_t K, int64_t N, void *y_bf16, void *ws,

@@ -161,9 +161,17 @@ def _qlinear_check(M, K, N, fmt_x="nv_tensor", fmt_w="nv_tensor", seeds=(6, 7), 
     ws = fq.qlinear_workspace(dx, dw, M, K, N, xd.device)
     y = fq.fq_qlinear_fwd(dx, dw, xd, wd, ws=ws)
     torch.cuda.synchronize()
-    xhat, what_t = fq.qlinear_workspace_views(ws, M, K, N)
-    assert np.array_equal(to_bits(xhat), ref["xhat"])
-    assert np.array_equal(to_bits(what_t), np.ascontiguousarray(ref["what"].T))
+    if fmt_x == "mx" and fmt_w == "mx" and K % 64 == 0:
+        # encoded operands on the FP4 matrix cores: codes and scales are bit-exact
+        xc, xs, wc, wsc = (t.cpu().numpy() for t in fq.qlinear_workspace_mx_views(ws, M, K, N))
+        qx = oracle.fake_quant(x, "mx", "rne", "row")
+        qw = oracle.fake_quant(w, "mx", "rne", "col")
+        assert np.array_equal(xc, qx["codes"]) and np.array_equal(xs, qx["scales"])
+        assert np.array_equal(wc, qw["codes"]) and np.array_equal(wsc, qw["scales"])
+    else:
+        xhat, what_t = fq.qlinear_workspace_views(ws, M, K, N)
+        assert np.array_equal(to_bits(xhat), ref["xhat"])
+        assert np.array_equal(to_bits(what_t), np.ascontiguousarray(ref["what"].T))
     yg = oracle.bf16_bits_to_f64(to_bits(y))
     err = np.linalg.norm(yg - ref["y"]) / np.linalg.norm(ref["y"])
     assert err <= tol, err
@@ -171,7 +179,7 @@ def _qlinear_check(M, K, N, fmt_x="nv_tensor", fmt_w="nv_tensor", seeds=(6, 7), 
 
 
 @pytest.mark.parametrize("M,K,N", [(128, 64, 128), (96, 384, 200), (257, 320, 136),
-                                   (1024, 2880, 576)])
+                                   (1024, 2880, 576), (300, 448, 264), (512, 1024, 512)])
 @pytest.mark.parametrize("fmts", [("nv_tensor", "nv_tensor"), ("mx", "mx"),
                                   ("nv_128", "nv_128")])
 def test_qlinear_small(M, K, N, fmts):
@@ -232,4 +240,10 @@ def test_workload_backward():
 
 def test_workload_qlinear():
     err = _qlinear_check(8192, 2880, 5760)
+    assert err < 4e-3
+
+
+def test_workload_qlinear_mxfp4():
+    # the same shape with both operands MXFP4: codes and scales on the FP4 matrix cores
+    err = _qlinear_check(8192, 2880, 5760, "mx", "mx")
     assert err < 4e-3
