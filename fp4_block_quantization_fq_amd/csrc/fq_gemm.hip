@@ -234,32 +234,23 @@ __device__ __forceinline__ void load_codes(const uint8_t *__restrict__ g, int ro
     }
 }
 
-// The eight E8M0 scales of one operand row for stage kt (blocks past the end
-// of K read as 0; their products are never formed).  Rows past the end of the
-// operand are clamped like the codes.
-__device__ __forceinline__ uint2 load_scales(const uint8_t *__restrict__ s, int row, int nrows,
-                                             int nblk, int kt)
-{
-    const uint8_t *p = s + (size_t)min(row, nrows - 1) * nblk + kt * FSB;
-    const int have = min(FSB, nblk - kt * FSB);     // even: K is a multiple of 64
-    uint32_t w[2] = {0u, 0u};
-#pragma unroll
-    for (int q = 0; q < FSB / 2; ++q)
-        if (2 * q < have) {
-            const uint32_t h = *reinterpret_cast<const uint16_t *>(p + 2 * q);
-            w[q >> 1] |= h << (16 * (q & 1));
-        }
-    return make_uint2(w[0], w[1]);
-}
-
 __global__ __launch_bounds__(kThreads, 1) void k_gemm_mxfp4_nt(Fp4Problem p0, Fp4Problem p1)
 {
     constexpr int WTM = BM / kWavesM, WTN = BN / kWavesN;
     constexpr int TM = WTM / 32, TN = WTN / 32;
     constexpr int A_BYTES = BM * ROW_BYTES, B_BYTES = BN * ROW_BYTES;
     constexpr int STAGE = A_BYTES + B_BYTES;
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * STAGE];
-    __shared__ uint2 s_scale[2][BM + BN];            // per stage: A rows, then B rows
+    // The two stage buffers are separate variables, and the loop below is
+    // unrolled by two so that every access names its buffer statically: the
+    // compiler then knows that the reads of one buffer cannot see the direct
+    // loads in flight into the other, and inserts no wait for those loads
+    // before the stage's fragment reads (one shared array indexed by kt & 1
+    // makes it wait for them, serializing load and compute).
+    __shared__ __attribute__((aligned(1024))) uint8_t lds0[STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds1[STAGE];
+    // per stage and operand row (A rows, then B rows): its eight E8M0 scales,
+    // block b of the stage in byte b
+    __shared__ uint64_t sc0[BM + BN], sc1[BM + BN];
 
     const bool second = (int)blockIdx.x >= p0.tiles;
     const uint8_t *__restrict__ A = second ? p1.A : p0.A;
@@ -290,9 +281,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mxfp4_nt(Fp4Problem p0, Fp
     const size_t pitch = (size_t)K / 2;
     const int nblk = K / 32, nsub = K / 64;          // scale blocks, 64-element MFMA steps
     const int nk = (K + FK - 1) / FK;
-    // this thread's scale row for the stage loads: A rows first, then B rows
+    // This thread stages the scales of one operand row (A rows first, then B
+    // rows; rows past the end are clamped like the codes).  The row holds
+    // nblk = K/32 bytes, an even number, so its 2-byte loads are aligned.
     const bool sc_b = tid >= BM;
-    const int sc_row = sc_b ? row_b0 + (tid - BM) : row_a0 + tid;
+    const uint8_t *sc_src = sc_b ? Bs + (size_t)min(row_b0 + tid - BM, N - 1) * nblk
+                                 : As + (size_t)min(row_a0 + tid, M - 1) * nblk;
 
     floatx16 acc[TM][TN];
 #pragma unroll
@@ -308,31 +302,37 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mxfp4_nt(Fp4Problem p0, Fp
         load_codes<BN>(Bc, row_b0, N, pitch, (size_t)kt * (FK / 2), valid_chunks, st + A_BYTES,
                        wave, lane);
     };
-    issue_stage(0, lds);
-    s_scale[0][tid] = sc_b ? load_scales(Bs, sc_row, N, nblk, 0) : load_scales(As, sc_row, M, nblk, 0);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+    // The eight scales of stage kt as four 2-byte loads, issued without a
+    // branch and consumed only at the end of the stage (so that no wait for
+    // them lands before the MFMAs).  Past the end of K they re-read the row's
+    // last two scales, which no product uses.
+    auto load_scales = [&](int kt, uint32_t (&h)[FSB / 2]) {
+#pragma unroll
+        for (int q = 0; q < FSB / 2; ++q)
+            h[q] = *reinterpret_cast<const uint16_t *>(sc_src + min(kt * FSB + 2 * q, nblk - 2));
+    };
+    auto pack_scales = [](const uint32_t (&h)[FSB / 2]) {
+        return (uint64_t)(h[0] | (h[1] << 16)) | ((uint64_t)(h[2] | (h[3] << 16)) << 32);
+    };
 
-    for (int kt = 0; kt < nk; ++kt) {
-        uint8_t *cur = lds + (kt & 1) * STAGE;
-        uint2 next_sc = make_uint2(0u, 0u);
-        if (kt + 1 < nk) {
-            issue_stage(kt + 1, lds + ((kt + 1) & 1) * STAGE);
-            next_sc = sc_b ? load_scales(Bs, sc_row, N, nblk, kt + 1)
-                           : load_scales(As, sc_row, M, nblk, kt + 1);
-        }
-        // this lane's scale words for the stage: its 4 A rows and 2 B rows
-        uint2 sa[TM], sb[TN];
+    // One stage: issue the loads of stage kt+1 into `nxt`, run the MFMAs of
+    // stage kt from `cur`, then publish the next scales and wait for all.
+    auto stage = [&](int kt, const uint8_t *cur, uint8_t *nxt, const uint64_t *scur,
+                     uint64_t *snxt) {
+        uint32_t h[FSB / 2];
+        load_scales(kt + 1, h);
+        if (kt + 1 < nk) issue_stage(kt + 1, nxt);
+        // this lane's scale words for the stage: its TM A rows and TN B rows
+        uint64_t sa[TM], sb[TN];
 #pragma unroll
-        for (int i = 0; i < TM; ++i) sa[i] = s_scale[kt & 1][wm * WTM + i * 32 + (lane & 31)];
+        for (int i = 0; i < TM; ++i) sa[i] = scur[wm * WTM + i * 32 + (lane & 31)];
 #pragma unroll
-        for (int j = 0; j < TN; ++j) sb[j] = s_scale[kt & 1][BM + wn * WTN + j * 32 + (lane & 31)];
+        for (int j = 0; j < TN; ++j) sb[j] = scur[BM + wn * WTN + j * 32 + (lane & 31)];
         const uint8_t *sa_t = cur, *sb_t = cur + A_BYTES;
 #pragma unroll
         for (int ks = 0; ks < FK / 64; ++ks) {
             if (kt * (FK / 64) + ks >= nsub) break;         // uniform: the K tail
             const int c = ks * 2 + (lane >> 5);               // 16-byte chunk = 32 codes
-            const int sh = 8 * (c & 3);
             v8i af[TM], bfr[TN];
             int sca[TM], scb[TN];
 #pragma unroll
@@ -340,14 +340,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mxfp4_nt(Fp4Problem p0, Fp
                 const int r = wm * WTM + i * 32 + (lane & 31);
                 const uint4 q = *reinterpret_cast<const uint4 *>(sa_t + r * ROW_BYTES + swz(r, c) * 16);
                 af[i] = (v8i){(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
-                sca[i] = (int)(((c < 4 ? sa[i].x : sa[i].y) >> sh) & 0xFFu);
+                sca[i] = (int)((sa[i] >> (8 * c)) & 0xFFu);
             }
 #pragma unroll
             for (int j = 0; j < TN; ++j) {
                 const int r = wn * WTN + j * 32 + (lane & 31);
                 const uint4 q = *reinterpret_cast<const uint4 *>(sb_t + r * ROW_BYTES + swz(r, c) * 16);
                 bfr[j] = (v8i){(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
-                scb[j] = (int)(((c < 4 ? sb[j].x : sb[j].y) >> sh) & 0xFFu);
+                scb[j] = (int)((sb[j] >> (8 * c)) & 0xFFu);
             }
 #pragma unroll
             for (int i = 0; i < TM; ++i)
@@ -356,9 +356,24 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mxfp4_nt(Fp4Problem p0, Fp
                     acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
                         af[i], bfr[j], acc[i][j], 4, 4, 0, sca[i], 0, scb[j]);
         }
-        if (kt + 1 < nk) s_scale[(kt + 1) & 1][tid] = next_sc;
+        // the other scale buffer was last read in the previous stage, before
+        // its closing barrier; past the last stage the values go unused
+        snxt[tid] = pack_scales(h);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
+    };
+
+    {
+        uint32_t h[FSB / 2];
+        load_scales(0, h);
+        issue_stage(0, lds0);
+        sc0[tid] = pack_scales(h);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    for (int kt = 0; kt < nk; kt += 2) {
+        stage(kt, lds0, lds1, sc0, sc1);
+        if (kt + 1 < nk) stage(kt + 1, lds1, lds0, sc1, sc0);
     }
 
 #pragma unroll
