@@ -1,21 +1,21 @@
 // fq_kernels.hip -- streaming FP4 quantize / dequantize / STE kernels, gfx950.
 //
-// All kernels are HBM-bound streams.  A lane always owns 16 consecutive
-// elements along the quantization axis (one NVFP4 block, half an MXFP4 block),
-// and every global access is a 16-byte vector access coalesced across the
-// wavefront:
+// All kernels are HBM-bound streams.  A lane works on 16 consecutive
+// elements along the quantization axis at a time (one NVFP4 block, half an
+// MXFP4 block), and the BF16 tensors move as 16-byte vector accesses
+// coalesced across the wavefront:
 //
 //  * Row axis (groups along the contiguous dimension): the tensor is a flat
 //    array of 16-element segments (32 bytes of BF16).  Lane i of a wave owns
 //    segment base+i, so an MXFP4 block is a lane pair and a 128-element outer
 //    block is 8 lanes; block maxima are combined with DPP, without LDS.
 //  * Column axis (groups of consecutive rows of one column, i.e. the rows of
-//    x^T): a lane owns an 8-column x 16-row tile, loaded as 16 row segments
-//    of 16 bytes.  The 64 lanes of a wave cover 64 columns x 128 rows; the
-//    8 lanes of one column group hold consecutive row blocks, so their
-//    transposed code bytes leave the wave as one contiguous 64-byte run per
-//    column, MXFP4 blocks are lane pairs and the double-block's 128-row outer
-//    block is those 8 lanes.
+//    x^T).  The quantizer stages a 64-column x 128-row tile in LDS and then
+//    gives each lane one 16-row segment of one column, the row-axis work
+//    unit; see k_quant_col.  The dequantizer and the STE, which need no
+//    cross-lane work, let a lane own an 8-column x 16-row tile loaded as 16
+//    row segments of 16 bytes: the 8 lanes of one column group hold
+//    consecutive row blocks, so 64 lanes cover 64 columns x 128 rows.
 //
 // Numerics follow fq_device.hpp; the op definitions are those of fq.h.
 #include "fq_device.hpp"
@@ -42,6 +42,7 @@ constexpr uint32_t kRowGridCap = 1u << 20;
 
 typedef uint32_t u32v4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32v2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void;
 
 template <bool NT>
 __device__ __forceinline__ void st_stream(uint4 *p, const uint4 &v)
@@ -284,46 +285,33 @@ __device__ __forceinline__ void scatter_pairs(uint4 (&v)[16], int k, const uint3
     }
 }
 
-// Quantizer tile: a lane holds 8 columns of 16 consecutive rows, eight lanes
-// stack 128 rows, a wave spans 64 columns; the four waves of a workgroup sit
-// kColWc side by side along the columns and 4 / kColWc along the rows.  The
-// transposed codes, scales and outer scales are gathered in LDS and leave the
-// workgroup as runs of kColTileR / 2, kColTileR / B and kColTileR / 128
-// entries per column, instead of each lane storing its 8-byte and 1-byte
-// pieces at column stride.
-#ifndef FQ_COL_WC
-#define FQ_COL_WC 4
-#endif
-constexpr uint32_t kColWc = FQ_COL_WC;
-constexpr uint32_t kColTileC = 64 * kColWc, kColTileR = 128 * (4 / kColWc);
-constexpr uint32_t kColCodePitch = kColTileR / 2 + 8;   // bytes; 8 * pitch = 64 mod 256
+// Column quantizer: the tile goes through LDS, so that every lane works on
+// one 16-row segment of one column at a time, exactly like a row-axis lane on
+// its 16-element segment (same block scale, draws and encoder), with a small
+// register footprint and many waves per CU.
+//
+//  * A workgroup owns a kQcCols x kQcRows tile (64 columns x 128 rows).  Its
+//    waves copy it into LDS with direct loads (global_load_lds_dwordx4: no
+//    registers, 1 KB of 8 full 128-byte row pieces per instruction).  LDS
+//    block b holds tile rows 8b .. 8b+7, 128 bytes each; the 16-byte chunk of
+//    columns 8g .. 8g+7 of a row in block b sits in slot g ^ (b >> 1), so the
+//    eight segments a wave reads at once (8 row blocks of one chunk) hit
+//    eight different slots, i.e. all banks.
+//  * Lane l of wave w takes row block rb = l & 7 (rows 16 rb .. 16 rb + 15)
+//    of tile columns (l >> 3) + 8 w + 32 u, u = 0, 1.  The eight lanes of a
+//    column are consecutive, so an MXFP4 block is a lane pair and the
+//    double block's 128-row outer block is the 8 lanes, as on the row axis.
+//  * Codes (8 bytes), the scale byte and the outer scale of a segment go
+//    straight to their transposed rows ([C, R/2], [C, R/B], [C, R/128]): the
+//    eight lanes of a column write one contiguous run.  The fake-quantized
+//    BF16 values replace the inputs in LDS and leave as full rows at the end.
+constexpr uint32_t kQcCols = 64, kQcRows = 128;
+constexpr uint32_t kQcBlockBytes = 8 * kQcCols * 2;      // 8 rows of 128 bytes
 
-__device__ __forceinline__ uint32_t vword(const uint4 &v, int k)
+__device__ __forceinline__ uint32_t qc_offset(uint32_t row, uint32_t chunk)
 {
-    return k == 0 ? v.x : k == 1 ? v.y : k == 2 ? v.z : v.w;
-}
-
-struct QColTile {
-    uint32_t col0, row0, rb;   // lane's first column, first row, row block in its group
-    uint32_t lc, lr;           // the same relative to the workgroup tile
-    uint32_t tc0, tr0;         // workgroup tile origin
-    bool valid;
-};
-
-__device__ __forceinline__ QColTile quant_col_tile(uint32_t R, uint32_t C)
-{
-    const uint32_t lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const uint32_t tiles_c = (C + kColTileC - 1) / kColTileC;
-    QColTile t;
-    t.rb = lane & 7;
-    t.tc0 = (blockIdx.x % tiles_c) * kColTileC;
-    t.tr0 = (blockIdx.x / tiles_c) * kColTileR;
-    t.lc = (wave % kColWc) * 64 + (lane >> 3) * 8;
-    t.lr = (wave / kColWc) * 128 + t.rb * 16;
-    t.col0 = t.tc0 + t.lc;
-    t.row0 = t.tr0 + t.lr;
-    t.valid = t.col0 < C && t.row0 < R;
-    return t;
+    const uint32_t b = row >> 3;
+    return b * kQcBlockBytes + (row & 7) * (kQcCols * 2) + ((chunk ^ (b >> 1)) & 7) * 16;
 }
 
 template <int FMT, int RND, bool NT>
@@ -334,114 +322,99 @@ __global__ __launch_bounds__(kThreads) void k_quant_col(
     uint32_t seed_lo, uint32_t seed_hi)
 {
     constexpr uint32_t B = (FMT == FMT_MX) ? 32 : 16;
-    constexpr uint32_t SPB = kColTileR / B;          // scale bytes per column in the tile
-    constexpr uint32_t OPB = kColTileR / 128;        // outer scales per column in the tile
-    __shared__ __attribute__((aligned(16))) uint8_t s_codes[kColTileC * kColCodePitch];
-    __shared__ uint8_t s_scales[kColTileC * SPB];
-    __shared__ float s_outer[FMT == FMT_NV128 ? kColTileC * OPB : 1];
+    __shared__ __attribute__((aligned(1024))) uint8_t s_tile[kQcRows / 8 * kQcBlockBytes];
 
     OuterScale ot = {0.0f, 0.0f};
     if (FMT == FMT_NVT) {
         ot = tensor_scale(partials, npart);
         if (outer && blockIdx.x == 0 && threadIdx.x == 0) outer[0] = ot.s;
     }
-    const QColTile t = quant_col_tile(R, C);
-    const uint32_t ldx = C >> 3;   // 16-byte segments per row
+    const uint32_t lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const uint32_t tiles_c = (C + kQcCols - 1) / kQcCols;
+    const uint32_t tc0 = (blockIdx.x % tiles_c) * kQcCols;
+    const uint32_t tr0 = (blockIdx.x / tiles_c) * kQcRows;
+    const uint32_t ldx = C >> 3;                     // 16-byte chunks per row
 
-    if (t.valid) {     // MXFP4 pairs and double-block groups are valid together
-        uint4 v[16];
+    // Direct loads: wave w fills blocks 4w .. 4w+3; lane l brings row l >> 3
+    // of the block into slot l & 7, i.e. global chunk (l & 7) ^ (b >> 1).
+    // Rows and chunks outside the tensor re-read its last row / chunk (the
+    // segments they would feed are never used).
 #pragma unroll
-        for (int r = 0; r < 16; ++r) v[r] = x[(size_t)(t.row0 + r) * ldx + (t.col0 >> 3)];
+    for (uint32_t i = 0; i < 4; ++i) {
+        const uint32_t blk = wave * 4 + i;
+        const uint32_t row = min(tr0 + blk * 8 + (lane >> 3), R - 1);
+        const uint32_t chunk = min((tc0 >> 3) + (((lane & 7) ^ (blk >> 1)) & 7), ldx - 1);
+        __builtin_amdgcn_global_load_lds((const void *)(x + (size_t)row * ldx + chunk),
+                                         (lds_void *)(s_tile + blk * kQcBlockBytes), 16, 0, 0);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
 
-        // per-column maxima of the lane's 16 rows: packed u16 max
-        uint32_t mw[4] = {0u, 0u, 0u, 0u};
+    const uint32_t rb = lane & 7;
+    const uint32_t row0 = tr0 + rb * 16;             // first row of this lane's segments
+#pragma unroll 1
+    for (uint32_t u = 0; u < 2; ++u) {
+        const uint32_t lc = (lane >> 3) + 8 * wave + 32 * u;
+        const uint32_t col = tc0 + lc;
+        // MXFP4 pairs and double-block groups share their column and are
+        // valid together (R is a multiple of B, and of 128 for the double block)
+        if (col >= C || row0 >= R) continue;
+        const uint32_t byte_in_chunk = (lc & 7) * 2;
+        uint32_t xp[8];
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-#pragma unroll
-            for (int k = 0; k < 4; ++k) mw[k] = pkmax_u16(mw[k], vword(v[r], k) & 0x7FFF7FFFu);
-
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            uint32_t yph[2][8];
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const uint32_t c = 2 * k + h;
-                const uint32_t col = t.col0 + c;
-                const uint32_t amax16 = h ? (mw[k] >> 16) : (mw[k] & 0xFFFFu);
-                float so = 0.0f;
-                const BlockScale b = lane_block_scale<FMT>(amax16, ot, so);
-                if (FMT == FMT_NV128 && t.rb == 0) s_outer[(t.lc + c) * OPB + t.lr / 128] = so;
-                if (FMT != FMT_MX || (t.rb & 1) == 0)
-                    s_scales[(t.lc + c) * SPB + t.lr / B] = (uint8_t)b.code;
-                u32x4 rnd[2];
-                if (RND == RND_SR) {
-                    const uint64_t call0 = ((uint64_t)col * R + t.row0) >> 3;
-                    rnd[0] = philox4x32_10((uint32_t)call0, (uint32_t)(call0 >> 32), 0u, 0u,
-                                           seed_lo, seed_hi);
-                    rnd[1] = philox4x32_10((uint32_t)(call0 + 1), (uint32_t)((call0 + 1) >> 32),
-                                           0u, 0u, seed_lo, seed_hi);
-                }
-                // column pairs along rows: element 2i in the low half of xp[i]
-                uint32_t xp[8];
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const uint32_t wa = vword(v[2 * i], k), wb = vword(v[2 * i + 1], k);
-                    xp[i] = h ? ((wa >> 16) | (wb & 0xFFFF0000u)) : ((wa & 0xFFFFu) | (wb << 16));
-                }
-                uint32_t cw[2];
-                encode_pairs<FMT, RND, 8>(xp, b, rnd, cw, yph[h]);
-                *reinterpret_cast<uint2 *>(&s_codes[(t.lc + c) * kColCodePitch + t.lr / 2]) =
-                    make_uint2(cw[0], cw[1]);
-                if (yt) {
-                    uint4 *dst = yt + (((size_t)col * R + t.row0) >> 3);
-                    st_stream<NT>(&dst[0], make_uint4(yph[h][0], yph[h][1], yph[h][2], yph[h][3]));
-                    st_stream<NT>(&dst[1], make_uint4(yph[h][4], yph[h][5], yph[h][6], yph[h][7]));
-                }
-            }
-            if (y) {
-                // columns 2k, 2k+1 back into the row segments
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    seg_set_word(v[2 * i], k, (yph[0][i] & 0xFFFFu) | (yph[1][i] << 16));
-                    seg_set_word(v[2 * i + 1], k, (yph[0][i] >> 16) | (yph[1][i] & 0xFFFF0000u));
-                }
-            }
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t r = rb * 16 + 2 * i;
+            const uint32_t lo = *reinterpret_cast<const uint16_t *>(
+                s_tile + qc_offset(r, lc >> 3) + byte_in_chunk);
+            const uint32_t hi = *reinterpret_cast<const uint16_t *>(
+                s_tile + qc_offset(r + 1, lc >> 3) + byte_in_chunk);
+            xp[i] = lo | (hi << 16);
+        }
+        float so = 0.0f;
+        const BlockScale b = lane_block_scale<FMT>(absmax_bits_pairs8(xp), ot, so);
+        if (FMT == FMT_NV128 && outer && rb == 0)
+            outer[(size_t)col * (R >> 7) + (row0 >> 7)] = so;
+        if (scales && (FMT != FMT_MX || (rb & 1) == 0))
+            scales[(size_t)col * (R / B) + row0 / B] = (uint8_t)b.code;
+        u32x4 rnd[2];
+        if (RND == RND_SR) {
+            const uint64_t call0 = ((uint64_t)col * R + row0) >> 3;
+            rnd[0] = philox4x32_10((uint32_t)call0, (uint32_t)(call0 >> 32), 0u, 0u, seed_lo,
+                                   seed_hi);
+            rnd[1] = philox4x32_10((uint32_t)(call0 + 1), (uint32_t)((call0 + 1) >> 32), 0u, 0u,
+                                   seed_lo, seed_hi);
+        }
+        uint32_t cw[2], yq[8];
+        encode_pairs<FMT, RND, 8>(xp, b, rnd, cw, yq);
+        if (codes)
+            st_stream<NT>(reinterpret_cast<uint2 *>(codes + (size_t)col * (R >> 1) + (row0 >> 1)),
+                          make_uint2(cw[0], cw[1]));
+        if (yt) {
+            uint4 *dst = yt + (((size_t)col * R + row0) >> 3);
+            st_stream<NT>(&dst[0], make_uint4(yq[0], yq[1], yq[2], yq[3]));
+            st_stream<NT>(&dst[1], make_uint4(yq[4], yq[5], yq[6], yq[7]));
         }
         if (y) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-                st_stream<NT>(&y[(size_t)(t.row0 + r) * ldx + (t.col0 >> 3)], v[r]);
+            for (int i = 0; i < 8; ++i) {
+                const uint32_t r = rb * 16 + 2 * i;
+                *reinterpret_cast<uint16_t *>(s_tile + qc_offset(r, lc >> 3) + byte_in_chunk) =
+                    (uint16_t)yq[i];
+                *reinterpret_cast<uint16_t *>(s_tile + qc_offset(r + 1, lc >> 3) + byte_in_chunk) =
+                    (uint16_t)(yq[i] >> 16);
+            }
         }
     }
+    if (!y) return;
     __syncthreads();
-
-    // The tile's transposed outputs, column by column.  Only entries whose
-    // column and rows exist are written (R is a multiple of B; a partial last
-    // band of rows fills a prefix of each column's run).
-    const uint32_t rows_here = min(kColTileR, R - t.tr0);
-    if (codes) {
-        constexpr uint32_t P8 = kColTileR / 16;      // 8-byte pieces per column
-        for (uint32_t q = threadIdx.x; q < kColTileC * P8; q += kThreads) {
-            const uint32_t lc = q / P8, j = q % P8;
-            if (t.tc0 + lc < C && j * 16 < rows_here)
-                st_stream<NT>(reinterpret_cast<uint2 *>(codes + (size_t)(t.tc0 + lc) * (R >> 1) +
-                                                        (t.tr0 >> 1) + j * 8),
-                              *reinterpret_cast<const uint2 *>(&s_codes[lc * kColCodePitch + j * 8]));
-        }
-    }
-    if (scales) {
-        for (uint32_t q = threadIdx.x; q < kColTileC * SPB; q += kThreads) {
-            const uint32_t lc = q / SPB, j = q % SPB;
-            if (t.tc0 + lc < C && j * B < rows_here)
-                scales[(size_t)(t.tc0 + lc) * (R / B) + t.tr0 / B + j] = s_scales[q];
-        }
-    }
-    if (FMT == FMT_NV128 && outer) {
-        for (uint32_t q = threadIdx.x; q < kColTileC * OPB; q += kThreads) {
-            const uint32_t lc = q / OPB, j = q % OPB;
-            if (t.tc0 + lc < C && j * 128 < rows_here)
-                outer[(size_t)(t.tc0 + lc) * (R >> 7) + (t.tr0 >> 7) + j] = s_outer[q];
-        }
+    // the fake-quantized tile back to [R, C] as full 128-byte row pieces
+#pragma unroll
+    for (uint32_t i = 0; i < 4; ++i) {
+        const uint32_t q = i * kThreads + threadIdx.x;
+        const uint32_t r = q >> 3, chunk = q & 7;
+        if (tr0 + r < R && tc0 + chunk * 8 < C)
+            st_stream<NT>(&y[(size_t)(tr0 + r) * ldx + (tc0 >> 3) + chunk],
+                          *reinterpret_cast<const uint4 *>(s_tile + qc_offset(r, chunk)));
     }
 }
 
@@ -588,11 +561,11 @@ dim3 col_grid(int64_t R, int64_t C)
     return dim3((uint32_t)(gx * gy), 1, 1);
 }
 
-// Column-axis quantizer grid: one workgroup per kColTileC x kColTileR tile.
+// Column-axis quantizer grid: one workgroup per kQcCols x kQcRows tile.
 dim3 quant_col_grid(int64_t R, int64_t C)
 {
-    uint64_t gx = (uint64_t)((C + kColTileC - 1) / kColTileC);
-    uint64_t gy = (uint64_t)((R + kColTileR - 1) / kColTileR);
+    uint64_t gx = (uint64_t)((C + kQcCols - 1) / kQcCols);
+    uint64_t gy = (uint64_t)((R + kQcRows - 1) / kQcRows);
     return dim3((uint32_t)(gx * gy), 1, 1);
 }
 
