@@ -16,12 +16,14 @@ seed 3) and its upstream gradient (N(0, 1e-3^2), seed 4):
 
 Every op writes all of its outputs (codes, scales, outer scales, BF16).
 `value` is the step's algorithmic bytes (each input read once, each output
-written once) over the step time, in GB/s.  The step is captured once per
-buffer set as a HIP graph and the graphs are replayed (`ms_per_step`); the same
-ops launched one by one with events around each (`ms_per_step_eager`) give the
-per-kernel times under "kernels" and the roofline figures.  Inputs are resident in HBM; the
-step rotates over three input/output buffer sets (~1.9 GB) so no launch
-finds its operands in the 256 MB Infinity Cache.
+written once) over the step time, in GB/s.  Inputs are resident in HBM.  There
+are three input/output buffer sets (~1.9 GB) and op k of step s works on set
+(s + k) mod 3, so consecutive ops never share an input tensor and every op
+streams its operands from HBM, not from the 256 MB Infinity Cache.  The step
+is captured once per starting set as a HIP graph and the graphs are replayed
+(`ms_per_step`); the same ops launched one by one with events around each
+(`ms_per_step_eager`) give the per-kernel times under "kernels" and the
+roofline figures.
 
 The QAT linear forward (X 8192x2880 @ W 2880x5760, both NVFP4 RNE) and its
 backward (dY 8192x5760, gradient operands NVFP4 double block with stochastic
@@ -166,10 +168,16 @@ def main():
         fq.fq_fake_quant(d_nv128, xs[i], y=ys[i], out=outs["nv128_rne_row"][i])
     torch.cuda.synchronize()
 
+    # Op k of step s works on buffer set (s + k) % NBUF: consecutive ops never
+    # share an input, so no op finds the tensor the previous one just streamed
+    # in the 256 MB Infinity Cache.
+    def run_step(s):
+        for k, op in enumerate(ops):
+            run_op(op, (s + k) % NBUF)
+
     log(f"bench: warmup {args.warmup} steps")
     for s in range(args.warmup):
-        for op in ops:
-            run_op(op, s % NBUF)
+        run_step(s)
     torch.cuda.synchronize()
 
     K = args.steps
@@ -180,11 +188,10 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(K):
-        i = s % NBUF
-        for op in ops:
+        for k, op in enumerate(ops):
             a, b = ev[op][s]
             a.record()
-            run_op(op, i)
+            run_op(op, (s + k) % NBUF)
             b.record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
@@ -201,8 +208,7 @@ def main():
         for i in range(NBUF):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g, stream=cap):
-                for op in ops:
-                    run_op(op, i)
+                run_step(i)
             graphs.append(g)
         for s in range(2 * NBUF):
             graphs[s % NBUF].replay()
