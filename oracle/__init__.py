@@ -256,6 +256,29 @@ def ste_backward(x: np.ndarray, scales: np.ndarray, outer, dy: np.ndarray,
     return dx if axis == "row" else np.ascontiguousarray(dx.T)
 
 
+def keep_mask(clip: np.ndarray) -> np.ndarray:
+    """Bit-packed STE keep mask of a fake_quant clip array, in the layout of x.
+
+    The straight-through gradient passes where the forward kept the element,
+    i.e. where a = RN(|x| / s_eff) <= 6 ("Resumo Tecnico: TetraJet-v2", sec.
+    2.A, the clipping that the gradient must respect; the same test as
+    ste_backward).  Byte (r, c // 8) holds elements (r, 8*(c//8)) .. +7, bit
+    c mod 8 set when element (r, c) was kept.  C must be a multiple of 8.
+    """
+    clip = np.ascontiguousarray(clip, dtype=np.uint8)
+    assert clip.ndim == 2 and clip.shape[1] % 8 == 0
+    return np.packbits(clip == 0, axis=1, bitorder="little")
+
+
+def ste_backward_mask(keep: np.ndarray, dy: np.ndarray) -> np.ndarray:
+    """dx = dy where the keep bit of the element is set, else +0 (BF16 bits)."""
+    dy = np.ascontiguousarray(dy, dtype=np.uint16)
+    bits = np.unpackbits(np.ascontiguousarray(keep, dtype=np.uint8), axis=1,
+                         bitorder="little")
+    assert bits.shape == dy.shape
+    return np.where(bits == 1, dy, np.uint16(0)).astype(np.uint16)
+
+
 def bf16_bits_to_f64(a: np.ndarray) -> np.ndarray:
     """Exact widening of BF16 bit patterns to float64."""
     a = np.ascontiguousarray(a, dtype=np.uint16)

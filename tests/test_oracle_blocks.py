@@ -155,3 +155,42 @@ def test_sr_worked_examples_at_tensor_level():
     se = 0.5 / np.sqrt(n)
     assert abs(p1 - 39424 / 65536) < 5 * se
     assert abs(p2 - 0.75) < 5 * se
+
+
+def test_keep_mask_worked_block():
+    # the worked MX block: only element 7 (-7, a = 7 > 6) is clipped, so bit 7
+    # of byte 0 is clear and every other bit of the 32 elements is set
+    x = [1, -0.30078125, 5.5, 0.25, -2.5, 0.75, 3.5, -7, 1.25, -1.75, 5] + [0] * 21
+    r = oracle.fake_quant(bf([x]), "mx")
+    assert oracle.keep_mask(r["clip"]).tolist() == [[0x7F, 0xFF, 0xFF, 0xFF]]
+    dy = bf([np.arange(1, 33, dtype=np.float32)])
+    dx = oracle.ste_backward_mask(oracle.keep_mask(r["clip"]), dy)
+    want = dy.copy()
+    want[0, 7] = 0
+    assert dx.tolist() == want.tolist()
+
+
+def test_keep_mask_nv_tensor_worked_block():
+    # the clipped element of the NVFP4 example is element 32 (a = 6.142857):
+    # byte 4, bit 0
+    x = _nv_tensor_example()
+    r = oracle.fake_quant(x, "nv_tensor")
+    k = oracle.keep_mask(r["clip"])[0].tolist()
+    assert k == [0xFF] * 4 + [0xFE, 0xFF]
+
+
+def test_keep_mask_ste_equals_recomputed_ste():
+    # The mask is taken from the forward's own quotients; ste_backward
+    # recomputes a from the stored scale codes.  Both must pass the same
+    # gradients, on every format and axis, on data that clips.
+    from workloads import activation_with_outlier_channels, grad_output
+    x = activation_with_outlier_channels((256, 384), 1.0, 6, 100.0, seed=5)
+    dy = grad_output(256, 384, seed=6)
+    for fmt in ("mx", "nv_tensor", "nv_128"):
+        for axis in ("row", "col"):
+            for rnd in ("rne", "sr"):
+                r = oracle.fake_quant(x, fmt, rnd, axis, seed=9)
+                assert r["clip"].any()
+                want = oracle.ste_backward(x, r["scales"], r["outer"], dy, fmt, axis)
+                got = oracle.ste_backward_mask(oracle.keep_mask(r["clip"]), dy)
+                assert np.array_equal(got, want), (fmt, axis, rnd)
