@@ -27,7 +27,8 @@ FQ_AXIS_ROW, FQ_AXIS_COL = 0, 1
 # every symbol include/fq.h declares
 EXPORTED = (
     "fq_desc_mxfp4", "fq_desc_nvfp4", "fq_workspace_size", "fq_quantize",
-    "fq_dequantize", "fq_fake_quant", "fq_ste_backward",
+    "fq_dequantize", "fq_fake_quant", "fq_fake_quant_mask", "fq_ste_backward",
+    "fq_ste_backward_mask",
     "fq_qlinear_workspace_size", "fq_qlinear_fwd", "fq_hadamard",
     "fq_qlinear_bwd_workspace_size", "fq_qlinear_bwd", "fq_status_string",
     "fq_last_error", "fq_version",
@@ -84,6 +85,10 @@ def lib() -> ctypes.CDLL:
         L.fq_fake_quant.argtypes = [dp, vp, i64, i64, vp, vp, vp, vp, vp, sz, vp]
         L.fq_fake_quant.restype = ctypes.c_int
         L.fq_ste_backward.argtypes = [dp, vp, vp, vp, vp, i64, i64, vp, vp]
+        L.fq_fake_quant_mask.restype = ctypes.c_int
+        L.fq_fake_quant_mask.argtypes = [dp, vp, i64, i64, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.fq_ste_backward_mask.restype = ctypes.c_int
+        L.fq_ste_backward_mask.argtypes = [vp, vp, i64, i64, vp, vp]
         L.fq_ste_backward.restype = ctypes.c_int
         L.fq_qlinear_workspace_size.argtypes = [dp, dp, i64, i64, i64]
         L.fq_qlinear_workspace_size.restype = sz
@@ -235,6 +240,41 @@ def fq_fake_quant(desc: FqDesc, x, y=None, out: Quantized | None = None, ws=None
     _check(lib().fq_fake_quant(ctypes.byref(desc), _ptr(x), rows, cols, _ptr(y), _ptr(codes),
                                _ptr(scales), _ptr(outer), _ptr(ws), nbytes, _stream(stream)))
     return y
+
+
+def fq_fake_quant_mask(desc: FqDesc, x, y=None, out: Quantized | None = None, keep=None,
+                       ws=None, stream=None):
+    """fq_fake_quant that also writes the STE keep mask (uint8 [rows, cols/8],
+    layout of x, bit c mod 8 of byte (r, c/8) set where element (r, c) was
+    kept).  Returns (y, keep)."""
+    torch = _torch()
+    rows, cols = x.shape
+    if y is None:
+        y = torch.empty_like(x)
+    if keep is None:
+        keep = torch.empty((rows, cols // 8), dtype=torch.uint8, device=x.device)
+    if ws is None:
+        ws, nbytes = workspace(desc, rows, cols, x.device)
+    else:
+        nbytes = ws.numel() * ws.element_size()
+    codes = scales = outer = None
+    if out is not None:
+        codes, scales, outer = out.codes, out.scales, out.outer
+    _check(lib().fq_fake_quant_mask(ctypes.byref(desc), _ptr(x), rows, cols, _ptr(y),
+                                    _ptr(codes), _ptr(scales), _ptr(outer), _ptr(keep),
+                                    _ptr(ws), nbytes, _stream(stream)))
+    return y, keep
+
+
+def fq_ste_backward_mask(keep, dy, dx=None, stream=None):
+    """dx = dy where the keep bit is set, else +0.  Returns dx."""
+    torch = _torch()
+    rows, cols = dy.shape
+    if dx is None:
+        dx = torch.empty_like(dy)
+    _check(lib().fq_ste_backward_mask(_ptr(keep), _ptr(dy), rows, cols, _ptr(dx),
+                                      _stream(stream)))
+    return dx
 
 
 def fq_ste_backward(desc: FqDesc, x, q: Quantized, dy, dx=None, stream=None):

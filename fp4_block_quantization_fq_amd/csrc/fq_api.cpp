@@ -123,7 +123,7 @@ fq_status device_status(hipError_t e, const char *what)
 // Shared body of fq_quantize / fq_fake_quant once arguments are checked.
 fq_status run_quant(const Fmt &f, const fq_desc *d, const void *x, int64_t R, int64_t C,
                     void *y, void *codes, void *scales, float *outer, void *ws,
-                    hipStream_t st, bool cached = false)
+                    hipStream_t st, bool cached = false, void *keep = nullptr)
 {
     fqimpl::QuantArgs a;
     a.fmt = f.fmt;
@@ -139,6 +139,7 @@ fq_status run_quant(const Fmt &f, const fq_desc *d, const void *x, int64_t R, in
     a.outer = (f.fmt == fqimpl::FMT_MX) ? nullptr : outer;
     a.yt = nullptr;
     a.partials = (uint32_t *)ws;
+    a.keep = keep;
     a.cached_outputs = cached;
     uint32_t npart = 0;
     if (f.fmt == fqimpl::FMT_NVT) {
@@ -244,6 +245,49 @@ fq_status fq_fake_quant(const fq_desc *desc, const void *x_bf16, int64_t rows, i
     }
     return run_quant(f, desc, x_bf16, rows, cols, y_bf16, codes, scales, outer, ws,
                      (hipStream_t)stream);
+}
+
+fq_status fq_fake_quant_mask(const fq_desc *desc, const void *x_bf16, int64_t rows,
+                             int64_t cols, void *y_bf16, void *codes, void *scales,
+                             float *outer, void *keep, void *ws, size_t ws_bytes, void *stream)
+{
+    Fmt f;
+    FQ_TRY(check_desc(desc, &f, "desc"));
+    FQ_TRY(check_shape(f, desc->axis, rows, cols));
+    if (cols % 8 != 0)
+        return fail(FQ_ERR_SHAPE, "cols=%lld must be a multiple of 8 for the keep mask",
+                    (long long)cols);
+    FQ_TRY(check_ptr(x_bf16, "x", true));
+    FQ_TRY(check_ptr(y_bf16, "y", true));
+    FQ_TRY(check_ptr(codes, "codes", false));
+    FQ_TRY(check_ptr(scales, "scales", false));
+    FQ_TRY(check_ptr(outer, "outer", false, 4));
+    FQ_TRY(check_ptr(keep, "keep", true));
+    const size_t need = quant_ws(f);
+    if (need) {
+        FQ_TRY(check_ptr(ws, "ws", true));
+        if (ws_bytes < need)
+            return fail(FQ_ERR_WORKSPACE, "workspace %zu bytes < %zu required", ws_bytes, need);
+    }
+    return run_quant(f, desc, x_bf16, rows, cols, y_bf16, codes, scales, outer, ws,
+                     (hipStream_t)stream, false, keep);
+}
+
+fq_status fq_ste_backward_mask(const void *keep, const void *dy_bf16, int64_t rows,
+                               int64_t cols, void *dx_bf16, void *stream)
+{
+    if (rows < 1 || cols < 8 || cols % 8 != 0)
+        return fail(FQ_ERR_SHAPE, "rows=%lld must be >= 1 and cols=%lld a positive multiple of 8",
+                    (long long)rows, (long long)cols);
+    if (rows > kMaxElems || cols > kMaxElems || rows * cols > kMaxElems)
+        return fail(FQ_ERR_SHAPE, "rows*cols=%lld*%lld exceeds 2^34 elements", (long long)rows,
+                    (long long)cols);
+    FQ_TRY(check_ptr(keep, "keep", true));
+    FQ_TRY(check_ptr(dy_bf16, "dy", true));
+    FQ_TRY(check_ptr(dx_bf16, "dx", true));
+    return device_status(fqimpl::launch_ste_mask(keep, dy_bf16, rows, cols, dx_bf16,
+                                                 (hipStream_t)stream),
+                         "ste mask launch");
 }
 
 fq_status fq_ste_backward(const fq_desc *desc, const void *x_bf16, const void *scales,

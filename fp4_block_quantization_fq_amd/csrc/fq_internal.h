@@ -26,6 +26,7 @@ struct QuantArgs {
     void *codes;          // or null
     void *scales;         // or null
     float *outer;         // or null
+    void *keep = nullptr; // uint8 [R, C/8] STE keep mask in the layout of x, or null
     uint32_t *partials;   // kAbsmaxPartials words (NV per-tensor only)
     bool cached_outputs;  // ordinary stores (outputs re-read right away) instead of streaming
 };
@@ -36,6 +37,9 @@ hipError_t launch_quant(const QuantArgs &a, uint32_t npart, hipStream_t stream);
 hipError_t launch_dequant(int fmt, int col, const void *codes, const void *scales,
                           const float *outer, int64_t R, int64_t C, void *y,
                           hipStream_t stream);
+// dx = dy where the keep bit (bit c mod 8 of byte (r, c / 8)) is set, else +0.
+hipError_t launch_ste_mask(const void *keep, const void *dy, int64_t R, int64_t C, void *dx,
+                           hipStream_t stream);
 hipError_t launch_ste(int fmt, int col, const void *x, const void *scales,
                       const float *outer, const void *dy, int64_t R, int64_t C,
                       void *dx, hipStream_t stream);

@@ -142,7 +142,8 @@ __device__ __forceinline__ void quant_row_seg(uint32_t seg, const uint4 &v0, con
                                               const OuterScale &ot, uint4 *__restrict__ y,
                                               uint2 *__restrict__ codes,
                                               uint8_t *__restrict__ scales,
-                                              float *__restrict__ outer, uint32_t seed_lo,
+                                              float *__restrict__ outer,
+                                              uint16_t *__restrict__ keep, uint32_t seed_lo,
                                               uint32_t seed_hi)
 {
     const uint32_t lane = threadIdx.x & 63;
@@ -164,6 +165,7 @@ __device__ __forceinline__ void quant_row_seg(uint32_t seg, const uint4 &v0, con
     }
     uint32_t cw[2], yp[8];
     encode_pairs<FMT, RND, 8>(xp, b, rnd, cw, yp);
+    if (keep) keep[seg] = (uint16_t)keep_mask<FMT, 8>(xp, b);
     if (codes) st_stream<NT>(&codes[seg], make_uint2(cw[0], cw[1]));
     if (y) {
         st_stream<NT>(&y[2 * seg], make_uint4(yp[0], yp[1], yp[2], yp[3]));
@@ -191,7 +193,8 @@ __device__ __forceinline__ void quant_row_chunk(uint32_t c, const uint4 &v, cons
                                                 uint4 *__restrict__ y,
                                                 uint32_t *__restrict__ codes,
                                                 uint8_t *__restrict__ scales,
-                                                float *__restrict__ outer, uint32_t seed_lo,
+                                                float *__restrict__ outer,
+                                                uint8_t *__restrict__ keep, uint32_t seed_lo,
                                                 uint32_t seed_hi)
 {
     const uint32_t lane = threadIdx.x & 63;
@@ -210,6 +213,7 @@ __device__ __forceinline__ void quant_row_chunk(uint32_t c, const uint4 &v, cons
     if (RND == RND_SR) rnd[0] = philox4x32_10(c, 0u, 0u, 0u, seed_lo, seed_hi);
     uint32_t cw[1], yp[4];
     encode_pairs<FMT, RND, 4>(xp, b, rnd, cw, yp);
+    if (keep) keep[c] = (uint8_t)keep_mask<FMT, 4>(xp, b);
     if (codes) st_stream<NT>(&codes[c], cw[0]);
     if (y) st_stream<NT>(&y[c], make_uint4(yp[0], yp[1], yp[2], yp[3]));
 }
@@ -220,8 +224,8 @@ template <int FMT, int RND, int MAP, bool NT>
 __global__ __launch_bounds__(kThreads) void k_quant_row(
     const uint4 *__restrict__ x, uint32_t nunits, uint4 *__restrict__ y,
     void *__restrict__ codes, uint8_t *__restrict__ scales, float *__restrict__ outer,
-    const uint32_t *__restrict__ partials, uint32_t npart, uint32_t seed_lo,
-    uint32_t seed_hi)
+    void *__restrict__ keep, const uint32_t *__restrict__ partials, uint32_t npart,
+    uint32_t seed_lo, uint32_t seed_hi)
 {
     OuterScale ot = {0.0f, 0.0f};
     if (FMT == FMT_NVT) {
@@ -233,11 +237,11 @@ __global__ __launch_bounds__(kThreads) void k_quant_row(
         if (MAP == 1) {
             const uint4 v = x[u];
             quant_row_chunk<FMT, RND, NT>(u, v, ot, y, (uint32_t *)codes, scales, outer,
-                                          seed_lo, seed_hi);
+                                          (uint8_t *)keep, seed_lo, seed_hi);
         } else {
             const uint4 v0 = x[2 * u], v1 = x[2 * u + 1];
             quant_row_seg<FMT, RND, NT>(u, v0, v1, ot, y, (uint2 *)codes, scales, outer,
-                                        seed_lo, seed_hi);
+                                        (uint16_t *)keep, seed_lo, seed_hi);
         }
     }
 }
@@ -318,11 +322,15 @@ template <int FMT, int RND, bool NT>
 __global__ __launch_bounds__(kThreads) void k_quant_col(
     const uint4 *__restrict__ x, uint32_t R, uint32_t C, uint4 *__restrict__ y,
     uint4 *__restrict__ yt, uint8_t *__restrict__ codes, uint8_t *__restrict__ scales,
-    float *__restrict__ outer, const uint32_t *__restrict__ partials, uint32_t npart,
-    uint32_t seed_lo, uint32_t seed_hi)
+    float *__restrict__ outer, uint8_t *__restrict__ keep,
+    const uint32_t *__restrict__ partials, uint32_t npart, uint32_t seed_lo, uint32_t seed_hi)
 {
     constexpr uint32_t B = (FMT == FMT_MX) ? 32 : 16;
     __shared__ __attribute__((aligned(1024))) uint8_t s_tile[kQcRows / 8 * kQcBlockBytes];
+    // clip bits of the tile for the keep mask: row r, columns 32h .. 32h + 31
+    // in word 2r + h (clipped elements are rare, so they are the ones set)
+    __shared__ uint32_t s_clip[kQcRows * (kQcCols / 32)];
+    static_assert(kQcRows * (kQcCols / 32) == kThreads, "one clip word per thread");
 
     OuterScale ot = {0.0f, 0.0f};
     if (FMT == FMT_NVT) {
@@ -347,6 +355,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_col(
         __builtin_amdgcn_global_load_lds((const void *)(x + (size_t)row * ldx + chunk),
                                          (lds_void *)(s_tile + blk * kQcBlockBytes), 16, 0, 0);
     }
+    if (keep) s_clip[threadIdx.x] = 0u;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
@@ -386,6 +395,13 @@ __global__ __launch_bounds__(kThreads) void k_quant_col(
         }
         uint32_t cw[2], yq[8];
         encode_pairs<FMT, RND, 8>(xp, b, rnd, cw, yq);
+        if (keep) {
+            // element i of the segment is row 16 rb + i of the tile
+            for (uint32_t clip = ~keep_mask<FMT, 8>(xp, b) & 0xFFFFu; clip; clip &= clip - 1) {
+                const uint32_t i = __builtin_ctz(clip);
+                atomicOr(&s_clip[(rb * 16 + i) * (kQcCols / 32) + (lc >> 5)], 1u << (lc & 31));
+            }
+        }
         if (codes)
             st_stream<NT>(reinterpret_cast<uint2 *>(codes + (size_t)col * (R >> 1) + (row0 >> 1)),
                           make_uint2(cw[0], cw[1]));
@@ -405,8 +421,24 @@ __global__ __launch_bounds__(kThreads) void k_quant_col(
             }
         }
     }
-    if (!y) return;
+    if (!y && !keep) return;
     __syncthreads();
+    if (keep) {
+        // thread t: tile row t / 2, columns 32 (t % 2) .. + 31 of the keep mask
+        const uint32_t r = threadIdx.x / (kQcCols / 32), h = threadIdx.x % (kQcCols / 32);
+        const uint32_t c0 = tc0 + 32 * h;
+        if (tr0 + r < R && c0 < C) {
+            const uint32_t kw = ~s_clip[threadIdx.x];
+            uint8_t *dst = keep + ((size_t)(tr0 + r) * C + c0) / 8;
+            if (c0 + 32 <= C && (((uintptr_t)dst) & 3) == 0) {
+                *reinterpret_cast<uint32_t *>(dst) = kw;
+            } else {
+                const uint32_t nb = min(4u, (C - c0) / 8);
+                for (uint32_t j = 0; j < nb; ++j) dst[j] = (uint8_t)(kw >> (8 * j));
+            }
+        }
+    }
+    if (!y) return;
     // the fake-quantized tile back to [R, C] as full 128-byte row pieces
 #pragma unroll
     for (uint32_t i = 0; i < 4; ++i) {
@@ -542,6 +574,22 @@ __global__ __launch_bounds__(kThreads) void k_ste_col(
     }
 }
 
+// Clipped STE from a keep mask: chunk c (8 elements) of dy and byte c of the
+// mask.  dy and dx may be the same buffer (each lane reads its chunk before
+// writing it), so they are not restrict-qualified.
+__global__ __launch_bounds__(kThreads) void k_ste_mask(const uint8_t *__restrict__ keep,
+                                                       const uint4 *dy, uint32_t nchunks,
+                                                       uint4 *dx)
+{
+    for (uint32_t c = blockIdx.x * kThreads + threadIdx.x; c < nchunks;
+         c += gridDim.x * kThreads) {
+        const uint4 d = dy[c];
+        const uint32_t k = keep[c];
+        st_stream<true>(&dx[c], make_uint4(ste_word(d.x, k, 0), ste_word(d.y, k, 2),
+                                           ste_word(d.z, k, 4), ste_word(d.w, k, 6)));
+    }
+}
+
 // ---------------------------------------------------------------------------
 // launch helpers
 // ---------------------------------------------------------------------------
@@ -579,13 +627,13 @@ hipError_t quant_dispatch_nt(const fqimpl::QuantArgs &a, uint32_t npart, hipStre
         const uint64_t nunits = (uint64_t)a.R * a.C / (MAP == 1 ? 8 : 16);
         hipLaunchKernelGGL((k_quant_row<FMT, RND, MAP, NT>), dim3(row_grid(nunits, kThreads)),
                            dim3(kThreads), 0, st, (const uint4 *)a.x, (uint32_t)nunits,
-                           (uint4 *)a.y, a.codes, (uint8_t *)a.scales, a.outer, parts, npart,
-                           slo, shi);
+                           (uint4 *)a.y, a.codes, (uint8_t *)a.scales, a.outer, a.keep, parts,
+                           npart, slo, shi);
     } else {
         hipLaunchKernelGGL((k_quant_col<FMT, RND, NT>), quant_col_grid(a.R, a.C), dim3(kThreads), 0,
                            st, (const uint4 *)a.x, (uint32_t)a.R, (uint32_t)a.C, (uint4 *)a.y,
                            (uint4 *)a.yt, (uint8_t *)a.codes, (uint8_t *)a.scales, a.outer,
-                           parts, npart, slo, shi);
+                           (uint8_t *)a.keep, parts, npart, slo, shi);
     }
     return hipGetLastError();
 }
@@ -672,6 +720,15 @@ static hipError_t ste_dispatch(int col, const void *x, const void *scales, const
                            (const uint4 *)x, (const uint8_t *)scales, outer, (const uint4 *)dy,
                            (uint32_t)R, (uint32_t)C, (uint4 *)dx);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_ste_mask(const void *keep, const void *dy, int64_t R, int64_t C, void *dx,
+                           hipStream_t stream)
+{
+    const uint64_t nchunks = (uint64_t)R * C / 8;
+    hipLaunchKernelGGL(k_ste_mask, dim3(row_grid(nchunks, kThreads)), dim3(kThreads), 0, stream,
+                       (const uint8_t *)keep, (const uint4 *)dy, (uint32_t)nchunks, (uint4 *)dx);
     return hipGetLastError();
 }
 

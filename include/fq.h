@@ -162,6 +162,30 @@ fq_status fq_ste_backward(const fq_desc *desc, const void *x_bf16,
                           const void *dy_bf16, int64_t rows, int64_t cols,
                           void *dx_bf16, void *stream);
 
+/* Fake quantization that also writes the STE keep mask: as fq_fake_quant,
+ * plus keep [rows, cols / 8] uint8 in the layout of x (row-major, whatever
+ * desc->axis is): bit (c mod 8) of byte (r, c / 8) is 1 where element (r, c)
+ * was kept (a = RN(|x| / s_eff) <= 6) and 0 where the forward clipped it.
+ * The backward then needs neither x nor the scales (fq_ste_backward_mask):
+ * the clipped STE reads 2 B of dy and 1/8 B of mask per element instead of
+ * 2 B of x plus the scales.  cols must be a multiple of 8; keep must be
+ * non-NULL, 16-byte aligned, and must not overlap the other buffers.  Errors
+ * as fq_fake_quant.  Source: TetraJet-v2 sec. 2.A (the backward passes
+ * gradients through the quantizer where it did not clip); "Como o
+ * Treinamento ...", "Detalhes tecnicos" (STE, clipping effects). */
+fq_status fq_fake_quant_mask(const fq_desc *desc, const void *x_bf16, int64_t rows,
+                             int64_t cols, void *y_bf16, void *codes, void *scales,
+                             float *outer, void *keep, void *ws, size_t ws_bytes,
+                             void *stream);
+
+/* Clipped straight-through estimator from a keep mask written by
+ * fq_fake_quant_mask: dx = dy where the element's keep bit is set, else +0.
+ * keep [rows, cols / 8] (layout above), dy and dx [rows, cols] BF16, all
+ * device pointers, 16-byte aligned; dx may alias dy.  rows >= 1, cols >= 8,
+ * cols a multiple of 8.  Format independent.  Source: as fq_ste_backward. */
+fq_status fq_ste_backward_mask(const void *keep, const void *dy_bf16, int64_t rows,
+                               int64_t cols, void *dx_bf16, void *stream);
+
 /* Workspace for fq_qlinear_fwd: the dequantized X_hat [M, K] BF16 at offset
  * 0, the dequantized and transposed W_hat^T [N, K] BF16 at offset
  * round_up(M * K * 2, 256), then 8192 bytes of reduction scratch.  When both

@@ -129,6 +129,34 @@ def test_other_entry_points_validate(L):
                             fake(), fake(), 1024, None) == fq.FQ_ERR_WORKSPACE
 
 
+def test_mask_entry_points_validate(L):
+    mx = fq.fq_desc_mxfp4()
+    nv = fq.fq_desc_nvfp4()
+
+    def fqm(d, keep, rows=64, cols=64, y=fake(), ws=None, nbytes=0):
+        return L.fq_fake_quant_mask(ctypes.byref(d), fake(), rows, cols, y, None, None, None,
+                                    keep, ws, nbytes, None)
+    assert fqm(mx, None) == fq.FQ_ERR_NULL                     # keep is required
+    assert fqm(mx, fake(0x10004)) == fq.FQ_ERR_ALIGN
+    assert fqm(mx, fake(), y=None) == fq.FQ_ERR_NULL
+    assert fqm(mx, fake(), cols=48) == fq.FQ_ERR_SHAPE         # not a multiple of 32
+    assert fqm(nv, fake()) == fq.FQ_ERR_NULL                   # per-tensor needs ws
+    assert fqm(nv, fake(), ws=fake(), nbytes=100) == fq.FQ_ERR_WORKSPACE
+    col = fq.fq_desc_mxfp4(axis=fq.FQ_AXIS_COL)
+    assert fqm(col, fake(), rows=32, cols=20) == fq.FQ_ERR_SHAPE
+
+    def stm(keep=fake(), dy=fake(), rows=64, cols=64, dx=fake()):
+        return L.fq_ste_backward_mask(keep, dy, rows, cols, dx, None)
+    assert stm(keep=None) == fq.FQ_ERR_NULL
+    assert stm(dy=None) == fq.FQ_ERR_NULL
+    assert stm(dx=None) == fq.FQ_ERR_NULL
+    assert stm(keep=fake(0x10008)) == fq.FQ_ERR_ALIGN
+    assert stm(cols=12) == fq.FQ_ERR_SHAPE
+    assert stm(cols=0) == fq.FQ_ERR_SHAPE
+    assert stm(rows=0) == fq.FQ_ERR_SHAPE
+    assert stm(rows=1 << 20, cols=1 << 15) == fq.FQ_ERR_SHAPE   # > 2^34 elements
+
+
 def test_qlinear_bwd_validates(L):
     nv = fq.fq_desc_nvfp4()
     col = fq.fq_desc_nvfp4(axis=fq.FQ_AXIS_COL)
