@@ -337,6 +337,51 @@ def main():
                              "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                              "frac": round(tfb / BF16_PEAK_TFLOPS, 4)}}
 
+    # ---------------- the backward with MXFP4 everywhere (FP4 matrix cores) ----------------
+    qbwd_mx = None
+    if not args.only:
+        log("bench: qlinear backward mxfp4")
+        mxd_x, mxd_w = fq.fq_desc_mxfp4(), fq.fq_desc_mxfp4(axis=fq.FQ_AXIS_COL)
+        mxd_g = fq.fq_desc_mxfp4(rounding=fq.FQ_ROUND_SR, seed=1234)
+        bws_mx = fq.qlinear_bwd_workspace(mxd_x, mxd_w, mxd_g, M, Kd, N, dev)
+        for _ in range(3):
+            fq.fq_qlinear_bwd(mxd_x, mxd_w, mxd_g, xq, wq, dyq, dx=gx, dw=gw, ws=bws_mx)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.qlinear_iters):
+            fq.fq_qlinear_bwd(mxd_x, mxd_w, mxd_g, xq, wq, dyq, dx=gx, dw=gw, ws=bws_mx)
+        e1.record()
+        torch.cuda.synchronize()
+        bmx = e0.elapsed_time(e1) / args.qlinear_iters
+        tfx = 4.0 * M * Kd * N / (bmx * 1e-3) / 1e12
+        qbwd_mx = {"workload": "the same backward with MXFP4 forward operands and MXFP4 SR "
+                               "gradient operands (seed 1234): both products on the scaled "
+                               "FP4 matrix cores",
+                   "ms": round(bmx, 4), "TFLOPs": round(tfx, 1),
+                   "roofline": {"bound": "mfma", "achieved": round(tfx, 1),
+                                "peak": FP4_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                "frac": round(tfx / FP4_PEAK_TFLOPS, 4)}}
+
+    # ---------------- STE from the bit-packed keep mask ----------------
+    ste_mask = None
+    if not args.only:
+        log("bench: ste from keep mask")
+        keeps = [fq.fq_fake_quant_mask(d_nv128, xs[i], y=ys[i])[1] for i in range(NBUF)]
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for s in range(K):
+            fq.fq_ste_backward_mask(keeps[s % NBUF], dys[s % NBUF], dx=dxs[s % NBUF])
+        e1.record()
+        torch.cuda.synchronize()
+        sms = e0.elapsed_time(e1) / K
+        sb = 2 * n + n // 8 + 2 * n
+        ste_mask = {"op": "dx = keep ? dy : 0 on 16384x4096 (dy, 1-bit mask -> dx)",
+                    "ms": round(sms, 5), "bytes": sb,
+                    "GBps": round(sb / (sms * 1e-3) / 1e9, 1),
+                    "frac_hbm": round(sb / (sms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+
     # ---------------- random Hadamard transform ----------------
     rht = None
     if not args.only:
@@ -416,6 +461,8 @@ def main():
         "qlinear": qlin,
         "qlinear_mxfp4": qmx,
         "qlinear_bwd": qbwd,
+        "qlinear_bwd_mxfp4": qbwd_mx,
+        "ste_mask": ste_mask,
         "hadamard": rht,
     }
     print(json.dumps(out), flush=True)

@@ -442,12 +442,17 @@ fq_status fq_qlinear_fwd(const fq_desc *desc_x, const fq_desc *desc_w, const voi
 
 // qlinear backward workspace regions, in order (each rounded up to 256 B).
 struct BwdLayout {
-    size_t xhat, xsc, xout, what, wsc, wout, dyq_n, wq_n, xq_mt, dyq_mt, dx_raw, dw_raw, parts,
-        rdy_n, rw_n, rx_m, rdy_m, total;
+    size_t xhat, xkeep, what, wkeep, dyq_n, wq_n, xq_mt, dyq_mt, parts, rdy_n, rw_n, rx_m, rdy_m,
+        total;
 };
 
-static BwdLayout bwd_layout(const Fmt &fx, const Fmt &fw, bool rht, int64_t M, int64_t K,
-                            int64_t N)
+// Backward workspace.  X_hat and W_hat are the forward's operands (BF16),
+// xkeep / wkeep their STE keep masks (1 bit per element, layout of X and W);
+// dyq_n, wq_n, xq_mt, dyq_mt hold the four quantized gradient-product
+// operands: BF16 [M, N], [K, N], [K, M], [N, M] (transposed for the last
+// two), or, for MXFP4 gradient operands, their codes followed by their E8M0
+// scales in the same place (0.53 B instead of 2 B per element).
+static BwdLayout bwd_layout(bool rht, int64_t M, int64_t K, int64_t N)
 {
     BwdLayout L;
     size_t off = 0;
@@ -458,17 +463,13 @@ static BwdLayout bwd_layout(const Fmt &fx, const Fmt &fw, bool rht, int64_t M, i
     };
     const size_t mk = (size_t)M * K, kn = (size_t)K * N, mn = (size_t)M * N;
     L.xhat = take(mk * 2);
-    L.xsc = take(mk / fx.B);
-    L.xout = take(fx.fmt == fqimpl::FMT_NV128 ? mk / 128 * 4 : 4);
+    L.xkeep = take(mk / 8);
     L.what = take(kn * 2);
-    L.wsc = take(kn / fw.B);
-    L.wout = take(fw.fmt == fqimpl::FMT_NV128 ? kn / 128 * 4 : 4);
+    L.wkeep = take(kn / 8);
     L.dyq_n = take(mn * 2);
     L.wq_n = take(kn * 2);
     L.xq_mt = take(mk * 2);
     L.dyq_mt = take(mn * 2);
-    L.dx_raw = take(mk * 2);
-    L.dw_raw = take(kn * 2);
     L.parts = take(fqimpl::kAbsmaxPartials * sizeof(uint32_t));
     // rotated operands (random Hadamard transform), only when requested
     L.rdy_n = take(rht ? mn * 2 : 0);
@@ -489,7 +490,7 @@ size_t fq_qlinear_bwd_workspace_size(const fq_desc *desc_x, const fq_desc *desc_
         return 0;
     if (rht_block != 0 && rht_block != 16 && rht_block != 128) return 0;
     if (M < 1 || K < 1 || N < 1 || M > kMaxElems || K > kMaxElems || N > kMaxElems) return 0;
-    return bwd_layout(fx, fw, rht_block != 0, M, K, N).total;
+    return bwd_layout(rht_block != 0, M, K, N).total;
 }
 
 fq_status fq_hadamard(const void *x_bf16, int64_t rows, int64_t cols, int32_t axis,
@@ -521,10 +522,12 @@ fq_status fq_hadamard(const void *x_bf16, int64_t rows, int64_t cols, int32_t ax
 
 // One quantizer pass of the backward: src [R, C] along rows (col = false,
 // output y [R, C]) or along columns (col = true, output the transpose
-// yt [C, R]); optional scales/outer in the pass's own layout.
+// yt [C, R]); optional codes/scales in the pass's own layout and an optional
+// keep mask in the layout of src.
 static fq_status bwd_quant(const Fmt &f, const fq_desc *d, uint64_t seed, bool col,
                            const void *src, int64_t R, int64_t C, void *y, void *yt,
-                           void *scales, float *outer, uint32_t *parts, hipStream_t st)
+                           void *codes, void *scales, void *keep, uint32_t *parts,
+                           hipStream_t st)
 {
     fqimpl::QuantArgs a;
     a.fmt = f.fmt;
@@ -536,9 +539,10 @@ static fq_status bwd_quant(const Fmt &f, const fq_desc *d, uint64_t seed, bool c
     a.C = C;
     a.y = y;
     a.yt = yt;
-    a.codes = nullptr;
+    a.codes = codes;
     a.scales = scales;
-    a.outer = (f.fmt == fqimpl::FMT_MX) ? nullptr : outer;
+    a.outer = nullptr;
+    a.keep = keep;
     a.partials = parts;
     a.cached_outputs = true;
     uint32_t npart = 0;
@@ -589,7 +593,7 @@ fq_status fq_qlinear_bwd(const fq_desc *desc_x, const fq_desc *desc_w, const fq_
     FQ_TRY(check_ptr(dw_bf16, "dw", true));
     FQ_TRY(check_ptr(ws, "ws", true));
     const bool rht = rht_block != 0;
-    const BwdLayout L = bwd_layout(fx, fw, rht, M, K, N);
+    const BwdLayout L = bwd_layout(rht, M, K, N);
     if (ws_bytes < L.total)
         return fail(FQ_ERR_WORKSPACE, "workspace %zu bytes < %zu required", ws_bytes, L.total);
 
@@ -598,11 +602,11 @@ fq_status fq_qlinear_bwd(const fq_desc *desc_x, const fq_desc *desc_w, const fq_
     hipStream_t st = (hipStream_t)stream;
     const uint64_t sg = desc_g->seed;
 
-    // the forward's operands and their scales: X_hat [M, K], W_hat [K, N]
+    // the forward's operands and their STE keep masks: X_hat [M, K], W_hat [K, N]
     FQ_TRY(bwd_quant(fx, desc_x, desc_x->seed, false, x_bf16, M, K, b + L.xhat, nullptr,
-                     b + L.xsc, (float *)(b + L.xout), parts, st));
+                     nullptr, nullptr, b + L.xkeep, parts, st));
     FQ_TRY(bwd_quant(fw, desc_w, desc_w->seed, true, w_bf16, K, N, b + L.what, nullptr,
-                     b + L.wsc, (float *)(b + L.wout), parts, st));
+                     nullptr, nullptr, b + L.wkeep, parts, st));
     // the operands before quantization, rotated along each contraction axis
     const void *op_dy_n = dy_bf16, *op_w_n = b + L.what, *op_x_m = b + L.xhat, *op_dy_m = dy_bf16;
     if (rht) {
@@ -619,30 +623,44 @@ fq_status fq_qlinear_bwd(const fq_desc *desc_x, const fq_desc *desc_w, const fq_
         op_x_m = b + L.rx_m;
         op_dy_m = b + L.rdy_m;
     }
-    // operands of dX = STE_X(Q(dY) . Q(W_hat)^T), both quantized along N
-    FQ_TRY(bwd_quant(fg, desc_g, sg + 0, false, op_dy_n, M, N, b + L.dyq_n, nullptr, nullptr,
-                     nullptr, parts, st));
-    FQ_TRY(bwd_quant(fg, desc_g, sg + 1, false, op_w_n, K, N, b + L.wq_n, nullptr, nullptr,
-                     nullptr, parts, st));
-    // operands of dW = STE_W(Q(X_hat)^T . Q(dY)), both quantized along M,
-    // written transposed
-    FQ_TRY(bwd_quant(fg, desc_g, sg + 2, true, op_x_m, M, K, nullptr, b + L.xq_mt, nullptr,
-                     nullptr, parts, st));
-    FQ_TRY(bwd_quant(fg, desc_g, sg + 3, true, op_dy_m, M, N, nullptr, b + L.dyq_mt, nullptr,
-                     nullptr, parts, st));
-    // both products in one launch, then the two STE masks
-    hipError_t e = fqimpl::launch_gemm_bf16_nt_pair(b + L.dyq_n, b + L.wq_n, b + L.dx_raw, M, K, N,
-                                                    b + L.xq_mt, b + L.dyq_mt, b + L.dw_raw, K, N,
-                                                    M, st);
-    if (e != hipSuccess) return device_status(e, "gemm launch");
-    e = fqimpl::launch_ste(fx.fmt, 0, x_bf16, b + L.xsc,
-                           fx.fmt == fqimpl::FMT_MX ? nullptr : (const float *)(b + L.xout),
-                           b + L.dx_raw, M, K, dx_bf16, st);
-    if (e != hipSuccess) return device_status(e, "ste launch");
-    e = fqimpl::launch_ste(fw.fmt, 1, w_bf16, b + L.wsc,
-                           fw.fmt == fqimpl::FMT_MX ? nullptr : (const float *)(b + L.wout),
-                           b + L.dw_raw, K, N, dw_bf16, st);
-    return device_status(e, "ste launch");
+    // The four gradient-product operands: dY and W_hat along N (dX = Q(dY) .
+    // Q(W_hat)^T), X_hat and dY along M (dW = Q(X_hat)^T . Q(dY)), Philox keys
+    // seed + 0 .. 3.  Both products run in one grouped launch whose epilogue
+    // applies the STE keep masks (clipped entries of dX and dW are +0).
+    struct Op { const void *src; int64_t R, C; bool col; size_t at; };
+    const Op ops[4] = {{op_dy_n, M, N, false, L.dyq_n}, {op_w_n, K, N, false, L.wq_n},
+                       {op_x_m, M, K, true, L.xq_mt}, {op_dy_m, M, N, true, L.dyq_mt}};
+    hipError_t e;
+    if (fg.fmt == fqimpl::FMT_MX) {
+        // MXFP4 operands go to the scaled FP4 matrix cores as codes + scales
+        // (quantized along the contraction axis, which is what the product
+        // needs): [rows, red/2] codes then [rows, red/32] scales
+        fqimpl::Fp4Operands o[2];
+        const void *cd[4], *sc[4];
+        for (int i = 0; i < 4; ++i) {
+            const Op &p = ops[i];
+            const size_t elems = (size_t)p.R * p.C;
+            void *codes = b + p.at, *scales = b + p.at + round256(elems / 2);
+            FQ_TRY(bwd_quant(fg, desc_g, sg + i, p.col, p.src, p.R, p.C, nullptr, nullptr, codes,
+                             scales, nullptr, parts, st));
+            cd[i] = codes;
+            sc[i] = scales;
+        }
+        o[0] = {cd[0], sc[0], cd[1], sc[1], dx_bf16, M, K, N, b + L.xkeep};
+        o[1] = {cd[2], sc[2], cd[3], sc[3], dw_bf16, K, N, M, b + L.wkeep};
+        e = fqimpl::launch_gemm_mxfp4_nt_pair(o[0], o[1], 2, st);
+    } else {
+        // BF16 operands: row passes write y, column passes write y transposed
+        for (int i = 0; i < 4; ++i) {
+            const Op &p = ops[i];
+            FQ_TRY(bwd_quant(fg, desc_g, sg + i, p.col, p.src, p.R, p.C, p.col ? nullptr : b + p.at,
+                             p.col ? b + p.at : nullptr, nullptr, nullptr, nullptr, parts, st));
+        }
+        e = fqimpl::launch_gemm_bf16_nt_pair(b + L.dyq_n, b + L.wq_n, dx_bf16, M, K, N,
+                                             b + L.xq_mt, b + L.dyq_mt, dw_bf16, K, N, M, st,
+                                             b + L.xkeep, b + L.wkeep);
+    }
+    return device_status(e, "gemm launch");
 }
 
 const char *fq_status_string(fq_status s)

@@ -60,9 +60,22 @@ struct Problem {
     const uint16_t *A;
     const uint16_t *Bt;
     uint16_t *C;
+    const uint8_t *keep;   // STE keep mask of C (bit n mod 8 of byte n / 8), or null
     int M, N, K;
     int tiles;     // workgroups of this problem in the grid
 };
+
+// Output element (row, col) of C [M, N], zeroed where the keep mask clears it
+// (the straight-through gradient of a clipped element is +0).
+__device__ __forceinline__ void store_out(uint16_t *__restrict__ C,
+                                          const uint8_t *__restrict__ keep, int row, int col,
+                                          int N, float v)
+{
+    const size_t n = (size_t)row * N + col;
+    uint16_t bits = __builtin_bit_cast(uint16_t, (__bf16)v);
+    if (keep && !((keep[n >> 3] >> (n & 7)) & 1u)) bits = 0;
+    C[n] = bits;
+}
 
 __device__ __forceinline__ int swz(int row, int chunk)
 {
@@ -103,6 +116,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_nt(Problem p0, Problem p1)
     const uint16_t *__restrict__ A = second ? p1.A : p0.A;
     const uint16_t *__restrict__ Bt = second ? p1.Bt : p0.Bt;
     uint16_t *__restrict__ C = second ? p1.C : p0.C;
+    const uint8_t *__restrict__ keep = second ? p1.keep : p0.keep;
     const int M = second ? p1.M : p0.M, N = second ? p1.N : p0.N, K = second ? p1.K : p0.K;
     const int b = second ? (int)blockIdx.x - p0.tiles : (int)blockIdx.x;
 
@@ -188,10 +202,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_nt(Problem p0, Problem p1)
             for (int v = 0; v < 16; ++v) {
                 const int row = tm * BM + wm * WTM + i * 32 + (v >> 2) * 8 +
                                 (lane >> 5) * 4 + (v & 3);
-                if (row < M) {
-                    __bf16 h = (__bf16)acc[i][j][v];
-                    C[(size_t)row * N + col] = __builtin_bit_cast(uint16_t, h);
-                }
+                if (row < M) store_out(C, keep, row, col, N, acc[i][j][v]);
             }
         }
 }
@@ -207,6 +218,7 @@ struct Fp4Problem {
     const uint8_t *B;    // codes [N, K/2]
     const uint8_t *Bs;   // scales [N, K/32]
     uint16_t *C;         // BF16 [M, N]
+    const uint8_t *keep; // STE keep mask of C, or null
     int M, N, K;
     int tiles;
 };
@@ -258,6 +270,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mxfp4_nt(Fp4Problem p0, Fp
     const uint8_t *__restrict__ Bc = second ? p1.B : p0.B;
     const uint8_t *__restrict__ Bs = second ? p1.Bs : p0.Bs;
     uint16_t *__restrict__ C = second ? p1.C : p0.C;
+    const uint8_t *__restrict__ keep = second ? p1.keep : p0.keep;
     const int M = second ? p1.M : p0.M, N = second ? p1.N : p0.N, K = second ? p1.K : p0.K;
     const int b = second ? (int)blockIdx.x - p0.tiles : (int)blockIdx.x;
 
@@ -386,10 +399,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mxfp4_nt(Fp4Problem p0, Fp
             for (int v = 0; v < 16; ++v) {
                 const int row = tm * BM + wm * WTM + i * 32 + (v >> 2) * 8 +
                                 (lane >> 5) * 4 + (v & 3);
-                if (row < M) {
-                    __bf16 h = (__bf16)acc[i][j][v];
-                    C[(size_t)row * N + col] = __builtin_bit_cast(uint16_t, h);
-                }
+                if (row < M) store_out(C, keep, row, col, N, acc[i][j][v]);
             }
         }
 }
@@ -402,6 +412,7 @@ Problem make_problem(const void *a, const void *bt, void *c, int64_t M, int64_t 
     p.A = (const uint16_t *)a;
     p.Bt = (const uint16_t *)bt;
     p.C = (uint16_t *)c;
+    p.keep = nullptr;
     p.M = (int)M;
     p.N = (int)N;
     p.K = (int)K;
@@ -425,10 +436,12 @@ hipError_t launch_gemm_bf16_nt(const void *a, const void *bt, void *c, int64_t M
 hipError_t launch_gemm_bf16_nt_pair(const void *a0, const void *bt0, void *c0, int64_t M0,
                                     int64_t N0, int64_t K0, const void *a1, const void *bt1,
                                     void *c1, int64_t M1, int64_t N1, int64_t K1,
-                                    hipStream_t stream)
+                                    hipStream_t stream, const void *keep0, const void *keep1)
 {
     Problem p0 = make_problem(a0, bt0, c0, M0, N0, K0);
     Problem p1 = make_problem(a1, bt1, c1, M1, N1, K1);
+    p0.keep = (const uint8_t *)keep0;
+    p1.keep = (const uint8_t *)keep1;
     // longer per-tile contraction first; the first problem's share of the
     // grid is padded to a multiple of the XCD count so that the second keeps
     // its XCD-contiguous tile order
@@ -453,6 +466,7 @@ hipError_t launch_gemm_mxfp4_nt_pair(const Fp4Operands &o0, const Fp4Operands &o
         p.B = (const uint8_t *)o.b_codes;
         p.Bs = (const uint8_t *)o.b_scales;
         p.C = (uint16_t *)o.c;
+        p.keep = (const uint8_t *)o.keep;
         p.M = (int)o.M;
         p.N = (int)o.N;
         p.K = (int)o.K;

@@ -50,6 +50,7 @@ struct Fp4Operands {
     const void *a_codes, *a_scales, *b_codes, *b_scales;
     void *c;
     int64_t M, N, K;
+    const void *keep = nullptr;   // optional STE keep mask of c (elements zeroed where clear)
 };
 hipError_t launch_gemm_mxfp4_nt_pair(const Fp4Operands &o0, const Fp4Operands &o1, int count,
                                      hipStream_t stream);
@@ -61,9 +62,12 @@ hipError_t launch_hadamard(const void *x, int64_t R, int64_t C, int col, int n, 
 hipError_t launch_gemm_bf16_nt(const void *a, const void *bt, void *c, int64_t M,
                                int64_t N, int64_t K, hipStream_t stream);
 // Two independent products C0 = A0 * Bt0^T and C1 = A1 * Bt1^T in one launch.
+// keep0 / keep1: optional STE keep masks of c0 / c1 (bit n mod 8 of byte n / 8
+// for element n of C in row-major order); clear bits store +0.
 hipError_t launch_gemm_bf16_nt_pair(const void *a0, const void *bt0, void *c0, int64_t M0,
                                     int64_t N0, int64_t K0, const void *a1, const void *bt1,
                                     void *c1, int64_t M1, int64_t N1, int64_t K1,
-                                    hipStream_t stream);
+                                    hipStream_t stream, const void *keep0 = nullptr,
+                                    const void *keep1 = nullptr);
 
 }  // namespace fqimpl

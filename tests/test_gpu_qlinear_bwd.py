@@ -57,3 +57,9 @@ def test_qlinear_bwd_rne_gradient_quantizer():
 def test_workload_qlinear_bwd():
     errs = _bwd_check(8192, 2880, 5760, "nv_tensor", "nv_tensor", "nv_128")
     assert max(errs.values()) < 4e-3
+
+
+def test_workload_qlinear_bwd_mxfp4():
+    # MXFP4 gradient operands: both products run on the scaled FP4 matrix cores
+    errs = _bwd_check(8192, 2880, 5760, "mx", "mx", "mx")
+    assert max(errs.values()) < 4e-3
