@@ -84,6 +84,10 @@ def lib() -> ctypes.CDLL:
         L.fqo_hadamard_rows.argtypes = [u16p, i64, i64, ctypes.c_int, ctypes.c_uint64,
                                         ctypes.c_float, u16p, ctypes.c_int]
         L.fqo_hadamard_rows.restype = ctypes.c_int
+        L.fqo_quantize_rows_retain.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_uint64,
+                                               u16p, i64, i64, u8p, f32p, u8p, u8p, f32p,
+                                               u16p, ctypes.c_int]
+        L.fqo_quantize_rows_retain.restype = ctypes.c_int
         L.fqo_max_threads.argtypes = []
         L.fqo_max_threads.restype = ctypes.c_int
         _lib = L
@@ -277,6 +281,112 @@ def ste_backward_mask(keep: np.ndarray, dy: np.ndarray) -> np.ndarray:
                          bitorder="little")
     assert bits.shape == dy.shape
     return np.where(bits == 1, dy, np.uint16(0)).astype(np.uint16)
+
+
+# --------------------------------------------------------------------------
+# TetraJet-v2 sec. 2.B (OsciReset) and sec. 2.C (static outlier retention)
+# --------------------------------------------------------------------------
+
+def osci_state(n: int) -> dict:
+    """Per-element OsciReset state for n weights: previous master weight
+    (FP32), previous quantized value (BF16 bits) and the two distances (FP32)."""
+    return {"w_prev": np.zeros(n, np.float32), "q_prev": np.zeros(n, np.uint16),
+            "dist_m": np.zeros(n, np.float32), "dist_q": np.zeros(n, np.float32)}
+
+
+def osci_track(w: np.ndarray, q: np.ndarray, st: dict, first: bool) -> None:
+    """One training step of the oscillation tracker ("Resumo Tecnico:
+    TetraJet-v2", sec. 2.B, detection): the distance the master weight w
+    (FP32) and its quantized value q (BF16 bits, the fake-quantized weight the
+    forward used) travelled since the previous step is added to dist_m and
+    dist_q.  Every difference and every sum is one FP32 operation (numpy
+    float32 arithmetic rounds each to nearest).  first=True starts the
+    trajectory: it records w and q and clears the distances."""
+    w = np.asarray(w, np.float32).reshape(-1)
+    q = np.asarray(q, np.uint16).reshape(-1)
+    if first:
+        st["dist_m"][:] = 0
+        st["dist_q"][:] = 0
+    else:
+        qf = bf16_bits_to_f64(q).astype(np.float32)
+        qp = bf16_bits_to_f64(st["q_prev"]).astype(np.float32)
+        st["dist_m"][:] = st["dist_m"] + np.abs(w - st["w_prev"])
+        st["dist_q"][:] = st["dist_q"] + np.abs(qf - qp)
+    st["w_prev"][:] = w
+    st["q_prev"][:] = q
+
+
+def osci_reset(w: np.ndarray, q: np.ndarray, st: dict, tau: float) -> np.ndarray:
+    """The OsciReset check (sec. 2.B, mechanism), called by the training loop
+    when the learning rate is low.  The oscillation risk is dist_q / dist_m;
+    READING: an element oscillates when dist_q > RN32(tau * dist_m) (so a
+    quantized value that moved while the master weight did not counts, and
+    one that never moved does not), and its master weight is reset to its
+    current quantized value, the representative of its quantization bin.  A
+    check starts a new window: the distances restart at 0 and the trajectory
+    continues from the (reset) weights.  Returns the new w and the boolean
+    mask of reset elements."""
+    w = np.array(w, np.float32).reshape(-1)
+    q = np.asarray(q, np.uint16).reshape(-1)
+    osc = st["dist_q"] > (np.float32(tau) * st["dist_m"])
+    w[osc] = bf16_bits_to_f64(q[osc]).astype(np.float32)
+    st["w_prev"][:] = w
+    st["q_prev"][:] = q
+    st["dist_m"][:] = 0
+    st["dist_q"][:] = 0
+    return w, osc
+
+
+def channel_absmax(x: np.ndarray, running: np.ndarray | None = None) -> np.ndarray:
+    """Per-channel (per-column) maximum |x| of a BF16 [R, C] tensor, as BF16
+    magnitude bits (uint32), folded into `running` if given ("Resumo Tecnico:
+    TetraJet-v2", sec. 2.C: outlier channels are identified by their norms over
+    a calibration window; READING: the norm is the maximum magnitude, which is
+    exact and independent of summation order)."""
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    m = (x & np.uint16(0x7FFF)).max(axis=0).astype(np.uint32)
+    return m if running is None else np.maximum(running, m)
+
+
+def select_channels(amax_bits: np.ndarray, k: int):
+    """The k channels with the largest calibration magnitude (ties: lower
+    channel index first) and their FP8 scales s_c = RN32(amax_c / 448)
+    (sec. 2.C: the top p% channels stay in FP8, E4M3's largest value 448).
+    Returns (retain [C] bool, chan_scale [C] float32, 0 where not retained)."""
+    a = np.asarray(amax_bits, np.uint32)
+    C = a.size
+    order = sorted(range(C), key=lambda c: (-int(a[c]), c))
+    retain = np.zeros(C, bool)
+    retain[order[:k]] = True
+    amax = bf16_bits_to_f64(a.astype(np.uint16)).astype(np.float32)
+    scale = np.where(retain, amax / np.float32(448.0), np.float32(0)).astype(np.float32)
+    return retain, scale
+
+
+def fake_quant_retain(x: np.ndarray, fmt: str, retain: np.ndarray, chan_scale: np.ndarray,
+                      rounding: str = "rne", seed: int = 0,
+                      nthreads: int | None = None) -> dict:
+    """Row-axis fake quantization in which the retained channels (columns)
+    are FP8 E4M3 with their own scale and the rest FP4 (fqo_quantize_rows_retain).
+    fmt "mx" or "nv_128"."""
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    R, C = x.shape
+    B = BLOCK[fmt]
+    ret = np.ascontiguousarray(np.asarray(retain).astype(np.uint8))
+    sc = np.ascontiguousarray(chan_scale, dtype=np.float32)
+    codes = np.zeros((R, C // 2), np.uint8)
+    scales = np.zeros((R, C // B), np.uint8)
+    outer = np.zeros((R, C // 128), np.float32) if fmt == "nv_128" else None
+    y = np.zeros((R, C), np.uint16)
+    n = default_threads() if nthreads is None else nthreads
+    rc = lib().fqo_quantize_rows_retain(FORMATS[fmt], ROUNDINGS[rounding], seed,
+                                        _ptr(x, ctypes.c_uint16), R, C,
+                                        _ptr(ret, ctypes.c_uint8), _ptr(sc, ctypes.c_float),
+                                        _ptr(codes, ctypes.c_uint8), _ptr(scales, ctypes.c_uint8),
+                                        _ptr(outer, ctypes.c_float), _ptr(y, ctypes.c_uint16), n)
+    if rc != 0:
+        raise ValueError(f"oracle: {fmt} {x.shape} cannot be quantized with retained channels")
+    return {"codes": codes, "scales": scales, "outer": outer, "y": y}
 
 
 def bf16_bits_to_f64(a: np.ndarray) -> np.ndarray:

@@ -391,6 +391,103 @@ int fqo_quantize_rows(int fmt, int rounding, uint64_t seed,
     return 0;
 }
 
+/* ------------------------------------------------------------------ */
+/* Static outlier-channel retention ([TJ2] sec. 2.C, "Retencao Estatica */
+/* de Outliers"): a fixed set of channels stays in FP8 in the forward   */
+/* pass while the rest is FP4.                                          */
+/* ------------------------------------------------------------------ */
+
+/* FP8 E4M3 fake quantization of one element under its channel's FP32 scale.
+ * READING: a = |x| / s in FP32, E4M3 round-to-nearest-even saturating at 448
+ * ([OFP8]; the same encoder as the NVFP4 block scale), value = dec(e) * s in
+ * FP32, sign of x kept, then BF16; a zero channel scale gives +-0. */
+static uint16_t fp8_fake_quant(float xv, float s)
+{
+    float mag = 0.0f;
+    if (s != 0.0f) {
+        float a = fabsf(xv) / s;
+        mag = (float)fqo_e4m3_decode(fqo_e4m3_encode(a)) * s;
+    }
+    return fqo_f32_to_bf16(signbit(xv) ? -mag : mag);
+}
+
+/* Row-axis fake quantization with retained channels.  retain[c] != 0 marks
+ * column c as an FP8 channel with scale chan_scale[c].  READING: retained
+ * elements take no part in the FP4 scales (block and 128-element outer
+ * maxima are taken over the other elements), carry FP4 code 0, and their y is
+ * the FP8 fake quantization above.  Only the MXFP4 and double-block NVFP4
+ * formats (no tensor-wide FP4 scale to redefine).  The stochastic-rounding
+ * index of an FP4 element is r * C + c as in fqo_quantize_rows. */
+int fqo_quantize_rows_retain(int fmt, int rounding, uint64_t seed,
+                             const uint16_t *x, int64_t R, int64_t C,
+                             const uint8_t *retain, const float *chan_scale,
+                             uint8_t *codes, uint8_t *scales, float *outer,
+                             uint16_t *y, int nthreads)
+{
+    const int B = block_size_of(fmt);
+    if (fmt == FQO_NV_TENSOR) return -1;
+    if (R <= 0 || C <= 0 || C % B != 0) return -1;
+    if (fmt == FQO_NV_BLOCK128 && C % 128 != 0) return -1;
+    (void)nthreads;
+
+#ifdef _OPENMP
+#pragma omp parallel for schedule(static) num_threads(nthreads > 0 ? nthreads : 1)
+#endif
+    for (int64_t r = 0; r < R; ++r) {
+        const uint16_t *xr = x + r * C;
+        float s_outer = 0.0f;
+        for (int64_t b0 = 0; b0 < C; b0 += B) {
+            if (fmt == FQO_NV_BLOCK128 && b0 % 128 == 0) {
+                float amax128 = 0.0f;
+                for (int64_t c = b0; c < b0 + 128; ++c) {
+                    if (retain[c]) continue;
+                    float v = fabsf(fqo_bf16_to_f32(xr[c]));
+                    if (v > amax128) amax128 = v;
+                }
+                s_outer = fqo_nv_outer_scale(amax128);
+                if (outer) outer[r * (C / 128) + b0 / 128] = s_outer;
+            }
+            float amax_b = 0.0f;
+            for (int64_t c = b0; c < b0 + B; ++c) {
+                if (retain[c]) continue;
+                float v = fabsf(fqo_bf16_to_f32(xr[c]));
+                if (v > amax_b) amax_b = v;
+            }
+            uint8_t scode;
+            float s_eff;
+            if (fmt == FQO_MX) {
+                scode = fqo_mx_scale_code(amax_b);
+                s_eff = fqo_e8m0_decode(scode);
+            } else {
+                nv_block_scale(amax_b, s_outer, &scode, &s_eff);
+            }
+            if (scales) scales[r * (C / B) + b0 / B] = scode;
+            for (int64_t c = b0; c < b0 + B; ++c) {
+                float xv = fqo_bf16_to_f32(xr[c]);
+                int code = 0;
+                uint16_t yv;
+                if (retain[c]) {
+                    yv = fp8_fake_quant(xv, chan_scale[c]);
+                } else {
+                    float a = scaled_magnitude(xv, s_eff);
+                    int m = (rounding == FQO_SR)
+                                ? fqo_e2m1_sr(a, fqo_r16(seed, (uint64_t)(r * C + c)))
+                                : fqo_e2m1_rne(a);
+                    code = (signbit(xv) ? 8 : 0) | m;
+                    yv = dequant_element(code, s_eff);
+                }
+                if (codes) {
+                    uint8_t *p = &codes[r * (C / 2) + c / 2];
+                    if ((c & 1) == 0) *p = (uint8_t)((*p & 0xF0) | code);
+                    else *p = (uint8_t)((*p & 0x0F) | (code << 4));
+                }
+                if (y) y[r * C + c] = yv;
+            }
+        }
+    }
+    return 0;
+}
+
 /* Effective scale of one block from stored scale codes (and outer scales). */
 static float stored_block_scale(int fmt, const uint8_t *scales, const float *outer,
                                 int64_t r, int64_t c, int64_t C)

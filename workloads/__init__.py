@@ -53,11 +53,17 @@ def activation_with_outlier_channels(shape, sigma: float, n_channels: int,
                                      factor: float, seed: int) -> np.ndarray:
     """N(0, sigma^2) with `n_channels` columns (chosen without replacement)
     multiplied by `factor`."""
+    return activation_and_outlier_channels(shape, sigma, n_channels, factor, seed)[0]
+
+
+def activation_and_outlier_channels(shape, sigma: float, n_channels: int, factor: float,
+                                    seed: int):
+    """activation_with_outlier_channels and the indices of the scaled columns."""
     rng = np.random.default_rng(seed)
     a = rng.standard_normal(shape, dtype=np.float32) * np.float32(sigma)
     cols = rng.choice(shape[1], size=n_channels, replace=False)
     a[:, cols] *= np.float32(factor)
-    return f32_to_bf16_bits(a)
+    return f32_to_bf16_bits(a), np.sort(cols)
 
 
 # --------------------------------------------------------------------------
