@@ -28,7 +28,8 @@ FQ_AXIS_ROW, FQ_AXIS_COL = 0, 1
 EXPORTED = (
     "fq_desc_mxfp4", "fq_desc_nvfp4", "fq_workspace_size", "fq_quantize",
     "fq_dequantize", "fq_fake_quant", "fq_fake_quant_mask", "fq_ste_backward",
-    "fq_ste_backward_mask",
+    "fq_ste_backward_mask", "fq_osci_track", "fq_osci_reset", "fq_channel_absmax",
+    "fq_select_channels", "fq_fake_quant_retain",
     "fq_qlinear_workspace_size", "fq_qlinear_fwd", "fq_hadamard",
     "fq_qlinear_bwd_workspace_size", "fq_qlinear_bwd", "fq_status_string",
     "fq_last_error", "fq_version",
@@ -88,6 +89,17 @@ def lib() -> ctypes.CDLL:
         L.fq_fake_quant_mask.restype = ctypes.c_int
         L.fq_fake_quant_mask.argtypes = [dp, vp, i64, i64, vp, vp, vp, vp, vp, vp, sz, vp]
         L.fq_ste_backward_mask.restype = ctypes.c_int
+        f32 = ctypes.c_float
+        L.fq_osci_track.argtypes = [vp, vp, vp, vp, vp, vp, i64, ctypes.c_int32, vp]
+        L.fq_osci_track.restype = ctypes.c_int
+        L.fq_osci_reset.argtypes = [vp, vp, vp, vp, vp, vp, i64, f32, vp]
+        L.fq_osci_reset.restype = ctypes.c_int
+        L.fq_channel_absmax.argtypes = [vp, i64, i64, vp, vp]
+        L.fq_channel_absmax.restype = ctypes.c_int
+        L.fq_select_channels.argtypes = [vp, i64, i64, vp, vp, vp]
+        L.fq_select_channels.restype = ctypes.c_int
+        L.fq_fake_quant_retain.argtypes = [dp, vp, i64, i64, vp, vp, vp, vp, vp, vp, vp]
+        L.fq_fake_quant_retain.restype = ctypes.c_int
         L.fq_ste_backward_mask.argtypes = [vp, vp, i64, i64, vp, vp]
         L.fq_ste_backward.restype = ctypes.c_int
         L.fq_qlinear_workspace_size.argtypes = [dp, dp, i64, i64, i64]
@@ -275,6 +287,69 @@ def fq_ste_backward_mask(keep, dy, dx=None, stream=None):
     _check(lib().fq_ste_backward_mask(_ptr(keep), _ptr(dy), rows, cols, _ptr(dx),
                                       _stream(stream)))
     return dx
+
+
+def osci_state(n: int, device):
+    """OsciReset state for n weights: w_prev, dist_m, dist_q FP32 and q_prev BF16."""
+    torch = _torch()
+    return {"w_prev": torch.zeros(n, dtype=torch.float32, device=device),
+            "q_prev": torch.zeros(n, dtype=torch.bfloat16, device=device),
+            "dist_m": torch.zeros(n, dtype=torch.float32, device=device),
+            "dist_q": torch.zeros(n, dtype=torch.float32, device=device)}
+
+
+def fq_osci_track(w, q, st: dict, first: bool = False, stream=None):
+    """One step of the oscillation tracker (w FP32 master, q BF16 quantized)."""
+    _check(lib().fq_osci_track(_ptr(w), _ptr(q), _ptr(st["w_prev"]), _ptr(st["q_prev"]),
+                               _ptr(st["dist_m"]), _ptr(st["dist_q"]), w.numel(),
+                               1 if first else 0, _stream(stream)))
+
+
+def fq_osci_reset(w, q, st: dict, tau: float, stream=None):
+    """The OsciReset check: oscillating master weights (in place in w) take
+    their quantized value; every element starts a new window."""
+    _check(lib().fq_osci_reset(_ptr(w), _ptr(q), _ptr(st["w_prev"]), _ptr(st["q_prev"]),
+                               _ptr(st["dist_m"]), _ptr(st["dist_q"]), w.numel(),
+                               ctypes.c_float(tau), _stream(stream)))
+
+
+def fq_channel_absmax(x, amax=None, stream=None):
+    """Fold max |x[:, c]| (BF16 magnitude bits) into amax [cols] (int32
+    tensor, zeros if not given).  Returns amax."""
+    torch = _torch()
+    rows, cols = x.shape
+    if amax is None:
+        amax = torch.zeros(cols, dtype=torch.int32, device=x.device)
+    _check(lib().fq_channel_absmax(_ptr(x), rows, cols, _ptr(amax), _stream(stream)))
+    return amax
+
+
+def fq_select_channels(amax, k: int, stream=None):
+    """The k largest channels: (retain uint8 [cols/8] bit mask, chan_scale
+    float32 [cols])."""
+    torch = _torch()
+    cols = amax.numel()
+    retain = torch.empty(cols // 8, dtype=torch.uint8, device=amax.device)
+    scale = torch.empty(cols, dtype=torch.float32, device=amax.device)
+    _check(lib().fq_select_channels(_ptr(amax), cols, k, _ptr(retain), _ptr(scale),
+                                    _stream(stream)))
+    return retain, scale
+
+
+def fq_fake_quant_retain(desc: FqDesc, x, retain, chan_scale, y=None,
+                         out: Quantized | None = None, stream=None):
+    """Row fake quantization with FP8 retained channels.  Returns y."""
+    torch = _torch()
+    rows, cols = x.shape
+    if y is None:
+        y = torch.empty_like(x)
+    codes = scales = outer = None
+    if out is not None:
+        codes, scales, outer = out.codes, out.scales, out.outer
+    _check(lib().fq_fake_quant_retain(ctypes.byref(desc), _ptr(x), rows, cols, _ptr(y),
+                                      _ptr(codes), _ptr(scales), _ptr(outer), _ptr(retain),
+                                      _ptr(chan_scale), _stream(stream)))
+    return y
 
 
 def fq_ste_backward(desc: FqDesc, x, q: Quantized, dy, dx=None, stream=None):

@@ -21,7 +21,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfq.so")
 
-SOURCES = ["fq_api.cpp", "fq_kernels.hip", "fq_gemm.hip", "fq_hadamard.hip"]
+SOURCES = ["fq_api.cpp", "fq_kernels.hip", "fq_gemm.hip", "fq_hadamard.hip", "fq_outcontrol.hip"]
 ARCH = "gfx950"
 
 COMMON = [

@@ -663,6 +663,110 @@ fq_status fq_qlinear_bwd(const fq_desc *desc_x, const fq_desc *desc_w, const fq_
     return device_status(e, "gemm launch");
 }
 
+static fq_status check_osci(const float *w, const void *q, const float *w_prev,
+                            const void *q_prev, const float *dm, const float *dq, int64_t n)
+{
+    if (n < 4 || n % 4 != 0 || n > kMaxElems)
+        return fail(FQ_ERR_SHAPE, "n=%lld must be a positive multiple of 4 up to 2^34",
+                    (long long)n);
+    FQ_TRY(check_ptr(w, "w", true));
+    FQ_TRY(check_ptr(q, "q", true, 8));
+    FQ_TRY(check_ptr(w_prev, "w_prev", true));
+    FQ_TRY(check_ptr(q_prev, "q_prev", true, 8));
+    FQ_TRY(check_ptr(dm, "dist_m", true));
+    FQ_TRY(check_ptr(dq, "dist_q", true));
+    return FQ_OK;
+}
+
+fq_status fq_osci_track(const float *w, const void *q_bf16, float *w_prev, void *q_prev_bf16,
+                        float *dist_m, float *dist_q, int64_t n, int32_t first, void *stream)
+{
+    FQ_TRY(check_osci(w, q_bf16, w_prev, q_prev_bf16, dist_m, dist_q, n));
+    return device_status(fqimpl::launch_osci_track(w, q_bf16, w_prev, q_prev_bf16, dist_m,
+                                                   dist_q, n, first ? 1 : 0,
+                                                   (hipStream_t)stream),
+                         "osci track launch");
+}
+
+fq_status fq_osci_reset(float *w, const void *q_bf16, float *w_prev, void *q_prev_bf16,
+                        float *dist_m, float *dist_q, int64_t n, float tau, void *stream)
+{
+    FQ_TRY(check_osci(w, q_bf16, w_prev, q_prev_bf16, dist_m, dist_q, n));
+    if (!(tau >= 0.0f) || tau > 3.4e38f)
+        return fail(FQ_ERR_DESC, "tau=%g must be finite and >= 0", (double)tau);
+    return device_status(fqimpl::launch_osci_reset(w, q_bf16, w_prev, q_prev_bf16, dist_m,
+                                                   dist_q, n, tau, (hipStream_t)stream),
+                         "osci reset launch");
+}
+
+fq_status fq_channel_absmax(const void *x_bf16, int64_t rows, int64_t cols, uint32_t *amax,
+                            void *stream)
+{
+    if (rows < 1 || cols < 8 || cols % 8 != 0)
+        return fail(FQ_ERR_SHAPE, "rows=%lld must be >= 1 and cols=%lld a positive multiple of 8",
+                    (long long)rows, (long long)cols);
+    if (rows > kMaxElems || cols > kMaxElems || rows * cols > kMaxElems)
+        return fail(FQ_ERR_SHAPE, "rows*cols exceeds 2^34 elements");
+    FQ_TRY(check_ptr(x_bf16, "x", true));
+    FQ_TRY(check_ptr(amax, "amax", true, 4));
+    return device_status(fqimpl::launch_channel_absmax(x_bf16, rows, cols, amax,
+                                                       (hipStream_t)stream),
+                         "channel absmax launch");
+}
+
+fq_status fq_select_channels(const uint32_t *amax, int64_t cols, int64_t k, void *retain,
+                             float *chan_scale, void *stream)
+{
+    if (cols < 8 || cols % 8 != 0 || cols > (int64_t(1) << 24))
+        return fail(FQ_ERR_SHAPE, "cols=%lld must be a positive multiple of 8 up to 2^24",
+                    (long long)cols);
+    if (k < 0 || k > cols)
+        return fail(FQ_ERR_SHAPE, "k=%lld must be in [0, cols=%lld]", (long long)k,
+                    (long long)cols);
+    FQ_TRY(check_ptr(amax, "amax", true, 4));
+    FQ_TRY(check_ptr(retain, "retain", true, 1));
+    FQ_TRY(check_ptr(chan_scale, "chan_scale", true, 4));
+    return device_status(fqimpl::launch_select_channels(amax, cols, k, retain, chan_scale,
+                                                        (hipStream_t)stream),
+                         "select channels launch");
+}
+
+fq_status fq_fake_quant_retain(const fq_desc *desc, const void *x_bf16, int64_t rows,
+                               int64_t cols, void *y_bf16, void *codes, void *scales,
+                               float *outer, const void *retain, const float *chan_scale,
+                               void *stream)
+{
+    Fmt f;
+    FQ_TRY(check_desc(desc, &f, "desc"));
+    if (desc->axis != FQ_AXIS_ROW)
+        return fail(FQ_ERR_DESC, "retained channels need FQ_AXIS_ROW (groups along channels)");
+    if (f.fmt == fqimpl::FMT_NVT)
+        return fail(FQ_ERR_DESC, "retained channels: MXFP4 or NVFP4 with FQ_OUTER_BLOCK128 only");
+    FQ_TRY(check_shape(f, FQ_AXIS_ROW, rows, cols));
+    FQ_TRY(check_ptr(x_bf16, "x", true));
+    FQ_TRY(check_ptr(y_bf16, "y", true));
+    FQ_TRY(check_ptr(codes, "codes", false));
+    FQ_TRY(check_ptr(scales, "scales", false));
+    FQ_TRY(check_ptr(outer, "outer", false, 4));
+    FQ_TRY(check_ptr(retain, "retain", true, 1));
+    FQ_TRY(check_ptr(chan_scale, "chan_scale", true, 4));
+    fqimpl::RetainArgs a;
+    a.fmt = f.fmt;
+    a.sr = desc->rounding == FQ_ROUND_SR;
+    a.seed = desc->seed;
+    a.x = x_bf16;
+    a.R = rows;
+    a.C = cols;
+    a.retain = retain;
+    a.chan_scale = chan_scale;
+    a.y = y_bf16;
+    a.codes = codes;
+    a.scales = scales;
+    a.outer = f.fmt == fqimpl::FMT_NV128 ? outer : nullptr;
+    return device_status(fqimpl::launch_quant_retain(a, (hipStream_t)stream),
+                         "retain quantize launch");
+}
+
 const char *fq_status_string(fq_status s)
 {
     switch (s) {

@@ -221,6 +221,21 @@ __device__ __forceinline__ BlockScale nv_block_scale(float amax, const OuterScal
     return b;
 }
 
+// Chunk mapping: lane owns 8 elements; an NVFP4 block is a lane pair, an
+// MXFP4 block a lane quad and a 128-element outer block a DPP row of 16.
+template <int FMT>
+__device__ __forceinline__ BlockScale chunk_block_scale(uint32_t amax8, const OuterScale &ot,
+                                                        float &outer_out)
+{
+    const uint32_t m = dpp_max_xor1(amax8);
+    if (FMT == FMT_MX) return mx_block_scale(dpp_max_xor2(m));
+    if (FMT == FMT_NVT) return nv_block_scale(as_f(m << 16), ot);
+    const uint32_t mo = dpp_max_ror8(dpp_max_ror4(dpp_max_xor2(m)));
+    const OuterScale o = make_outer(as_f(mo << 16));
+    outer_out = o.s;
+    return nv_block_scale(as_f(m << 16), o);
+}
+
 template <int FMT>
 __device__ __forceinline__ BlockScale scale_from_code(uint32_t code, float s)
 {

@@ -70,4 +70,28 @@ hipError_t launch_gemm_bf16_nt_pair(const void *a0, const void *bt0, void *c0, i
                                     hipStream_t stream, const void *keep0 = nullptr,
                                     const void *keep1 = nullptr);
 
+// TetraJet-v2 sec. 2.B / 2.C (fq_outcontrol.hip).  n is a multiple of 4.
+hipError_t launch_osci_track(const float *w, const void *q, float *w_prev, void *q_prev,
+                             float *dist_m, float *dist_q, int64_t n, int first,
+                             hipStream_t stream);
+hipError_t launch_osci_reset(float *w, const void *q, float *w_prev, void *q_prev,
+                             float *dist_m, float *dist_q, int64_t n, float tau,
+                             hipStream_t stream);
+hipError_t launch_channel_absmax(const void *x, int64_t R, int64_t C, uint32_t *amax,
+                                 hipStream_t stream);
+hipError_t launch_select_channels(const uint32_t *amax, int64_t C, int64_t k, void *retain,
+                                  float *chan_scale, hipStream_t stream);
+struct RetainArgs {
+    int fmt;                 // FMT_MX or FMT_NV128
+    int sr;
+    uint64_t seed;
+    const void *x;           // BF16 [R, C]
+    int64_t R, C;
+    const void *retain;      // uint8 [C/8] channel bit mask
+    const float *chan_scale; // FP32 [C]
+    void *y, *codes, *scales;
+    float *outer;
+};
+hipError_t launch_quant_retain(const RetainArgs &a, hipStream_t stream);
+
 }  // namespace fqimpl

@@ -1,0 +1,336 @@
+// fq_outcontrol.hip -- TetraJet-v2's two training-time controls on gfx950.
+//
+// "Resumo Tecnico: TetraJet-v2", sec. 2.B (OsciReset): a weight oscillates
+// when its quantized value keeps travelling between bins while the master
+// weight barely moves; the risk is the ratio of the two distances travelled,
+// and at a low learning rate an oscillating master weight is reset to its
+// quantization bin.  Sec. 2.C (OutControl, static outlier retention): the few
+// channels with large norms, found once during a calibration window, stay in
+// FP8 in the forward and backward passes while the rest is FP4.
+//
+// All of it is elementwise or per-channel streaming work:
+//  * k_osci_track / k_osci_reset: four weights per lane (16-byte FP32 and
+//    8-byte BF16 accesses), FP32 distances, one rounding per operation.
+//  * k_channel_absmax: the calibration statistic, the maximum magnitude of
+//    each column, folded into a running per-channel maximum with integer
+//    atomicMax on the BF16 magnitude bits (exact, independent of order).
+//  * k_select_channels: the k largest channels (ties to the lower index) as a
+//    bit mask, and their FP8 scales amax / 448.
+//  * k_quant_row_retain: the row-axis fake quantizer's chunk mapping (8
+//    elements per lane, blocks and the 128-element outer block by DPP), with
+//    the retained columns masked out of every FP4 maximum and encoded to FP8
+//    E4M3 under their channel scale.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fq_device.hpp"
+#include "fq_internal.h"
+
+using namespace fqdev;
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr uint32_t kGridCap = 1u << 20;
+
+uint32_t grid_for(uint64_t units)
+{
+    uint64_t g = (units + kThreads - 1) / kThreads;
+    if (g > kGridCap) g = kGridCap;
+    return (uint32_t)(g ? g : 1);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return as_f(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return as_f(w & 0xFFFF0000u); }
+
+// ---------------------------------------------------------------------------
+// OsciReset
+// ---------------------------------------------------------------------------
+// One training step: dist_m += |w - w_prev|, dist_q += |q - q_prev| (FP32,
+// each operation rounded once), then w_prev = w, q_prev = q; first = 1 only
+// records w and q and clears the distances.
+__global__ __launch_bounds__(kThreads) void k_osci_track(const float4 *__restrict__ w,
+                                                         const uint2 *__restrict__ q,
+                                                         float4 *__restrict__ w_prev,
+                                                         uint2 *__restrict__ q_prev,
+                                                         float4 *__restrict__ dm,
+                                                         float4 *__restrict__ dq, uint32_t n4,
+                                                         int first)
+{
+    for (uint32_t i = blockIdx.x * kThreads + threadIdx.x; i < n4; i += gridDim.x * kThreads) {
+        const float4 wv = w[i];
+        const uint2 qv = q[i];
+        if (first) {
+            dm[i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            dq[i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        } else {
+            const float4 wp = w_prev[i];
+            const uint2 qp = q_prev[i];
+            float4 m = dm[i], d = dq[i];
+            m.x = m.x + __builtin_fabsf(wv.x - wp.x);
+            m.y = m.y + __builtin_fabsf(wv.y - wp.y);
+            m.z = m.z + __builtin_fabsf(wv.z - wp.z);
+            m.w = m.w + __builtin_fabsf(wv.w - wp.w);
+            d.x = d.x + __builtin_fabsf(bf16_lo(qv.x) - bf16_lo(qp.x));
+            d.y = d.y + __builtin_fabsf(bf16_hi(qv.x) - bf16_hi(qp.x));
+            d.z = d.z + __builtin_fabsf(bf16_lo(qv.y) - bf16_lo(qp.y));
+            d.w = d.w + __builtin_fabsf(bf16_hi(qv.y) - bf16_hi(qp.y));
+            dm[i] = m;
+            dq[i] = d;
+        }
+        w_prev[i] = wv;
+        q_prev[i] = qv;
+    }
+}
+
+// The check: an element whose dist_q exceeds RN(tau * dist_m) takes its
+// quantized value as its master weight; then every element starts a new
+// window (distances 0, trajectory continuing from the possibly reset w).
+__device__ __forceinline__ float osci_one(float w, float q, float m, float d, float tau)
+{
+    return d > tau * m ? q : w;
+}
+
+__global__ __launch_bounds__(kThreads) void k_osci_reset(float4 *__restrict__ w,
+                                                         const uint2 *__restrict__ q,
+                                                         float4 *__restrict__ w_prev,
+                                                         uint2 *__restrict__ q_prev,
+                                                         float4 *__restrict__ dm,
+                                                         float4 *__restrict__ dq, uint32_t n4,
+                                                         float tau)
+{
+    for (uint32_t i = blockIdx.x * kThreads + threadIdx.x; i < n4; i += gridDim.x * kThreads) {
+        float4 wv = w[i];
+        const uint2 qv = q[i];
+        const float4 m = dm[i], d = dq[i];
+        wv.x = osci_one(wv.x, bf16_lo(qv.x), m.x, d.x, tau);
+        wv.y = osci_one(wv.y, bf16_hi(qv.x), m.y, d.y, tau);
+        wv.z = osci_one(wv.z, bf16_lo(qv.y), m.z, d.z, tau);
+        wv.w = osci_one(wv.w, bf16_hi(qv.y), m.w, d.w, tau);
+        w[i] = wv;
+        w_prev[i] = wv;
+        q_prev[i] = qv;
+        dm[i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        dq[i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Outlier channels
+// ---------------------------------------------------------------------------
+constexpr uint32_t kAmaxRows = 64;     // rows per thread
+
+// Thread t: 8-column chunk t mod (C/8) of rows (t / (C/8)) * 64 .. + 63.
+__global__ __launch_bounds__(kThreads) void k_channel_absmax(const uint4 *__restrict__ x,
+                                                             uint32_t R, uint32_t C,
+                                                             uint32_t *__restrict__ amax)
+{
+    const uint32_t nchunk = C >> 3;
+    const uint64_t t = (uint64_t)blockIdx.x * kThreads + threadIdx.x;
+    const uint32_t chunk = (uint32_t)(t % nchunk);
+    const uint64_t r0 = (t / nchunk) * kAmaxRows;
+    if (r0 >= R) return;
+    const uint32_t r1 = (uint32_t)min<uint64_t>(r0 + kAmaxRows, R);
+    uint32_t m[4] = {0u, 0u, 0u, 0u};
+    for (uint32_t r = (uint32_t)r0; r < r1; ++r) {
+        const uint4 v = x[(size_t)r * nchunk + chunk];
+        m[0] = pkmax_u16(m[0], v.x & 0x7FFF7FFFu);
+        m[1] = pkmax_u16(m[1], v.y & 0x7FFF7FFFu);
+        m[2] = pkmax_u16(m[2], v.z & 0x7FFF7FFFu);
+        m[3] = pkmax_u16(m[3], v.w & 0x7FFF7FFFu);
+    }
+    uint32_t *dst = amax + (size_t)chunk * 8;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        atomicMax(&dst[2 * j], m[j] & 0xFFFFu);
+        atomicMax(&dst[2 * j + 1], m[j] >> 16);
+    }
+}
+
+// Thread c: the rank of channel c among all (larger magnitude first, the
+// lower index first among equals); retained when rank < k.  The magnitudes
+// pass through LDS in tiles of 1024.
+constexpr uint32_t kSelTile = 1024;
+
+__global__ __launch_bounds__(kThreads) void k_select_channels(const uint32_t *__restrict__ amax,
+                                                              uint32_t C, uint32_t k,
+                                                              uint8_t *__restrict__ retain,
+                                                              float *__restrict__ chan_scale)
+{
+    __shared__ uint32_t s_a[kSelTile];
+    const uint32_t c = blockIdx.x * kThreads + threadIdx.x;
+    const uint32_t mine = c < C ? amax[c] : 0u;
+    uint32_t rank = 0;
+    for (uint32_t base = 0; base < C; base += kSelTile) {
+        const uint32_t nt = min(kSelTile, C - base);
+        __syncthreads();
+        for (uint32_t i = threadIdx.x; i < nt; i += kThreads) s_a[i] = amax[base + i];
+        __syncthreads();
+        for (uint32_t i = 0; i < nt; ++i) {
+            const uint32_t o = s_a[i];
+            rank += (o > mine || (o == mine && base + i < c)) ? 1u : 0u;
+        }
+    }
+    const bool keep = c < C && rank < k;
+    if (c < C) chan_scale[c] = keep ? as_f(mine << 16) / 448.0f : 0.0f;
+    // bits of 64 consecutive channels -> 8 bytes, written by lane 0
+    const uint64_t bits = __ballot(keep);
+    const uint32_t c0 = c & ~63u;
+    if ((threadIdx.x & 63) == 0 && c0 < C) {
+        const uint32_t nbytes = min(8u, (C - c0) / 8);
+        for (uint32_t j = 0; j < nbytes; ++j) retain[c0 / 8 + j] = (uint8_t)(bits >> (8 * j));
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Row fake quantization with retained (FP8) channels
+// ---------------------------------------------------------------------------
+// FP8 E4M3 fake quantization under the channel scale s: a = |x| / s (IEEE
+// division), E4M3 nearest-even saturating at 448, value * s, sign kept; a
+// zero scale gives +-0.
+__device__ __forceinline__ float fp8_fake(float x, float s)
+{
+    float mag = 0.0f;
+    if (s != 0.0f) mag = e4m3_value(e4m3_encode_sat(__builtin_fabsf(x) / s)) * s;
+    return as_f(as_u(mag) | (as_u(x) & 0x80000000u));
+}
+
+template <int FMT, int RND, bool NT>
+__global__ __launch_bounds__(kThreads) void k_quant_row_retain(
+    const uint4 *__restrict__ x, uint32_t nchunks, uint32_t C, const uint8_t *__restrict__ retain,
+    const float *__restrict__ chan_scale, uint4 *__restrict__ y, uint32_t *__restrict__ codes,
+    uint8_t *__restrict__ scales, float *__restrict__ outer, uint32_t seed_lo, uint32_t seed_hi)
+{
+    const uint32_t lane = threadIdx.x & 63;
+    const OuterScale ot = {0.0f, 0.0f};
+    for (uint32_t c = blockIdx.x * kThreads + threadIdx.x; c < nchunks;
+         c += gridDim.x * kThreads) {
+        const uint4 v = x[c];
+        const uint32_t xp[4] = {v.x, v.y, v.z, v.w};
+        const uint32_t col0 = (uint32_t)(((uint64_t)c * 8) % C);
+        const uint32_t rbits = retain[col0 >> 3];      // bit j: element j is an FP8 channel
+        // FP4 maxima over the other elements only
+        uint32_t mp[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t keep_lo = ((rbits >> (2 * i)) & 1u) ? 0u : 0x7FFFu;
+            const uint32_t keep_hi = ((rbits >> (2 * i + 1)) & 1u) ? 0u : 0x7FFF0000u;
+            mp[i] = xp[i] & (keep_lo | keep_hi);
+        }
+        const uint32_t m = pkmax_u16(pkmax_u16(mp[0], mp[1]), pkmax_u16(mp[2], mp[3]));
+        float so = 0.0f;
+        const BlockScale b = chunk_block_scale<FMT>(max(m & 0xFFFFu, m >> 16), ot, so);
+        if (FMT == FMT_NV128 && outer && (lane & 15) == 0) outer[c >> 4] = so;
+        if (scales) {
+            if (FMT == FMT_MX) {
+                if ((lane & 3) == 0) scales[c >> 2] = (uint8_t)b.code;
+            } else {
+                if ((lane & 1) == 0) scales[c >> 1] = (uint8_t)b.code;
+            }
+        }
+        u32x4 rnd[1];
+        if (RND == RND_SR) rnd[0] = philox4x32_10(c, 0u, 0u, 0u, seed_lo, seed_hi);
+        uint32_t cw[1], yp[4];
+        encode_pairs<FMT, RND, 4>(xp, b, rnd, cw, yp);
+        if (rbits) {
+            uint32_t nib = 0;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) nib |= ((rbits >> j) & 1u) * (0xFu << (4 * j));
+            cw[0] &= ~nib;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                if ((rbits >> (2 * i)) & 1u) {
+                    const float f = fp8_fake(bf16_lo(xp[i]), chan_scale[col0 + 2 * i]);
+                    yp[i] = (yp[i] & 0xFFFF0000u) | (bf16_pair_rne(f, 0.0f) & 0xFFFFu);
+                }
+                if ((rbits >> (2 * i + 1)) & 1u) {
+                    const float f = fp8_fake(bf16_hi(xp[i]), chan_scale[col0 + 2 * i + 1]);
+                    yp[i] = (yp[i] & 0xFFFFu) | (bf16_pair_rne(0.0f, f) & 0xFFFF0000u);
+                }
+            }
+        }
+        if (codes) {
+            if (NT) __builtin_nontemporal_store(cw[0], &codes[c]);
+            else codes[c] = cw[0];
+        }
+        if (y) {
+            const uint4 o = make_uint4(yp[0], yp[1], yp[2], yp[3]);
+            if (NT) {
+                typedef uint32_t u32v4 __attribute__((ext_vector_type(4)));
+                __builtin_nontemporal_store((u32v4){o.x, o.y, o.z, o.w},
+                                            reinterpret_cast<u32v4 *>(&y[c]));
+            } else {
+                y[c] = o;
+            }
+        }
+    }
+}
+
+template <int FMT, int RND>
+hipError_t retain_dispatch(const fqimpl::RetainArgs &a, hipStream_t st)
+{
+    const uint64_t nchunks = (uint64_t)a.R * a.C / 8;
+    const uint32_t slo = (uint32_t)a.seed, shi = (uint32_t)(a.seed >> 32);
+    hipLaunchKernelGGL((k_quant_row_retain<FMT, RND, true>), dim3(grid_for(nchunks)),
+                       dim3(kThreads), 0, st, (const uint4 *)a.x, (uint32_t)nchunks,
+                       (uint32_t)a.C, (const uint8_t *)a.retain, a.chan_scale, (uint4 *)a.y,
+                       (uint32_t *)a.codes, (uint8_t *)a.scales, a.outer, slo, shi);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+namespace fqimpl {
+
+hipError_t launch_osci_track(const float *w, const void *q, float *w_prev, void *q_prev,
+                             float *dist_m, float *dist_q, int64_t n, int first,
+                             hipStream_t st)
+{
+    const uint64_t n4 = (uint64_t)n / 4;
+    hipLaunchKernelGGL(k_osci_track, dim3(grid_for(n4)), dim3(kThreads), 0, st,
+                       (const float4 *)w, (const uint2 *)q, (float4 *)w_prev, (uint2 *)q_prev,
+                       (float4 *)dist_m, (float4 *)dist_q, (uint32_t)n4, first);
+    return hipGetLastError();
+}
+
+hipError_t launch_osci_reset(float *w, const void *q, float *w_prev, void *q_prev,
+                             float *dist_m, float *dist_q, int64_t n, float tau, hipStream_t st)
+{
+    const uint64_t n4 = (uint64_t)n / 4;
+    hipLaunchKernelGGL(k_osci_reset, dim3(grid_for(n4)), dim3(kThreads), 0, st, (float4 *)w,
+                       (const uint2 *)q, (float4 *)w_prev, (uint2 *)q_prev, (float4 *)dist_m,
+                       (float4 *)dist_q, (uint32_t)n4, tau);
+    return hipGetLastError();
+}
+
+hipError_t launch_channel_absmax(const void *x, int64_t R, int64_t C, uint32_t *amax,
+                                 hipStream_t st)
+{
+    const uint64_t threads = (uint64_t)(C / 8) * (uint64_t)((R + kAmaxRows - 1) / kAmaxRows);
+    const uint64_t g = (threads + kThreads - 1) / kThreads;
+    hipLaunchKernelGGL(k_channel_absmax, dim3((uint32_t)g), dim3(kThreads), 0, st,
+                       (const uint4 *)x, (uint32_t)R, (uint32_t)C, amax);
+    return hipGetLastError();
+}
+
+hipError_t launch_select_channels(const uint32_t *amax, int64_t C, int64_t k, void *retain,
+                                  float *chan_scale, hipStream_t st)
+{
+    const uint32_t g = (uint32_t)((C + kThreads - 1) / kThreads);
+    hipLaunchKernelGGL(k_select_channels, dim3(g), dim3(kThreads), 0, st, amax, (uint32_t)C,
+                       (uint32_t)k, (uint8_t *)retain, chan_scale);
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_retain(const RetainArgs &a, hipStream_t st)
+{
+    switch (a.fmt * 2 + a.sr) {
+    case FMT_MX * 2 + 0: return retain_dispatch<FMT_MX, RND_RNE>(a, st);
+    case FMT_MX * 2 + 1: return retain_dispatch<FMT_MX, RND_SR>(a, st);
+    case FMT_NV128 * 2 + 0: return retain_dispatch<FMT_NV128, RND_RNE>(a, st);
+    case FMT_NV128 * 2 + 1: return retain_dispatch<FMT_NV128, RND_SR>(a, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace fqimpl

@@ -268,6 +268,54 @@ fq_status fq_qlinear_bwd(const fq_desc *desc_x, const fq_desc *desc_w,
                          int64_t M, int64_t K, int64_t N, void *dx_bf16, void *dw_bf16,
                          void *ws, size_t ws_bytes, void *stream);
 
+/* ---- TetraJet-v2 OsciReset ("Resumo Tecnico: TetraJet-v2", sec. 2.B) ----
+ * Per-element state of n weights, all device arrays the caller owns: w_prev
+ * and dist_m, dist_q FP32 [n], q_prev BF16 [n].  w is the FP32 master weight,
+ * q the BF16 fake-quantized weight the forward pass used.  n >= 4, n a
+ * multiple of 4; every pointer 16-byte aligned (q, q_prev: 8-byte).
+ *
+ * fq_osci_track: one training step.  dist_m += |w - w_prev| and dist_q +=
+ * |q - q_prev| (FP32, one rounding per operation), then w_prev = w and
+ * q_prev = q.  first != 0 starts the trajectory: records w and q and zeroes
+ * the distances (no memset: safe inside a captured graph). */
+fq_status fq_osci_track(const float *w, const void *q_bf16, float *w_prev, void *q_prev_bf16,
+                        float *dist_m, float *dist_q, int64_t n, int32_t first, void *stream);
+
+/* fq_osci_reset: the check, called when the learning rate is low.  The
+ * oscillation risk is dist_q / dist_m; an element with dist_q > RN(tau *
+ * dist_m) gets w = q (its quantized value), all others keep w.  Then every
+ * element starts a new window: w_prev = w, q_prev = q, distances 0.  tau is
+ * the risk threshold (finite, >= 0). */
+fq_status fq_osci_reset(float *w, const void *q_bf16, float *w_prev, void *q_prev_bf16,
+                        float *dist_m, float *dist_q, int64_t n, float tau, void *stream);
+
+/* ---- TetraJet-v2 static outlier-channel retention (sec. 2.C) ----
+ * Calibration: fq_channel_absmax folds max |x[:, c]| of a BF16 [rows, cols]
+ * tensor into amax [cols] (uint32, the BF16 magnitude bits; zero it once before
+ * the first batch), by integer atomic maximum, so the result does not depend
+ * on order.  cols a multiple of 8; x 16-byte and amax 4-byte aligned. */
+fq_status fq_channel_absmax(const void *x_bf16, int64_t rows, int64_t cols, uint32_t *amax,
+                            void *stream);
+
+/* Selection: the k channels with the largest amax (ties: lower index first)
+ * are retained.  Writes retain [cols / 8] (bit c mod 8 of byte c / 8 set for a
+ * retained channel) and chan_scale [cols] FP32 = amax_c / 448 (the largest
+ * E4M3 value; 0 for other channels).  0 <= k <= cols, cols a multiple of 8. */
+fq_status fq_select_channels(const uint32_t *amax, int64_t cols, int64_t k, void *retain,
+                             float *chan_scale, void *stream);
+
+/* Row-axis fake quantization with retained channels: columns whose retain
+ * bit is set are FP8 E4M3 fake-quantized under chan_scale (|x| / s in FP32,
+ * nearest-even, saturating at 448, times s, sign kept; s = 0 gives +-0) and
+ * carry FP4 code 0; every FP4 block and 128-element outer maximum is taken
+ * over the other elements only.  desc: MXFP4 or NVFP4 double block
+ * (FQ_OUTER_BLOCK128), axis FQ_AXIS_ROW, RNE or SR; y required, codes,
+ * scales, outer optional (as fq_fake_quant). */
+fq_status fq_fake_quant_retain(const fq_desc *desc, const void *x_bf16, int64_t rows,
+                               int64_t cols, void *y_bf16, void *codes, void *scales,
+                               float *outer, const void *retain, const float *chan_scale,
+                               void *stream);
+
 /* Static description of a status code. */
 const char *fq_status_string(fq_status s);
 

@@ -157,6 +157,43 @@ def test_mask_entry_points_validate(L):
     assert stm(rows=1 << 20, cols=1 << 15) == fq.FQ_ERR_SHAPE   # > 2^34 elements
 
 
+def test_outcontrol_entry_points_validate(L):
+    f = fake
+    # OsciReset: n a positive multiple of 4, all state pointers required
+    assert L.fq_osci_track(f(), f(), f(), f(), f(), f(), 6, 0, None) == fq.FQ_ERR_SHAPE
+    assert L.fq_osci_track(f(), f(), f(), f(), f(), f(), 0, 0, None) == fq.FQ_ERR_SHAPE
+    assert L.fq_osci_track(f(), None, f(), f(), f(), f(), 64, 0, None) == fq.FQ_ERR_NULL
+    assert L.fq_osci_track(f(0x10004), f(), f(), f(), f(), f(), 64, 0, None) == fq.FQ_ERR_ALIGN
+    assert L.fq_osci_track(f(), f(0x10004), f(), f(), f(), f(), 64, 0, None) == fq.FQ_ERR_ALIGN
+    assert L.fq_osci_reset(f(), f(), f(), f(), f(), None, 64, ctypes.c_float(2.0),
+                           None) == fq.FQ_ERR_NULL
+    for bad in (-1.0, float("nan"), float("inf")):
+        assert L.fq_osci_reset(f(), f(), f(), f(), f(), f(), 64, ctypes.c_float(bad),
+                               None) == fq.FQ_ERR_DESC, bad
+    # calibration and selection
+    assert L.fq_channel_absmax(f(), 64, 12, f(), None) == fq.FQ_ERR_SHAPE
+    assert L.fq_channel_absmax(f(), 0, 64, f(), None) == fq.FQ_ERR_SHAPE
+    assert L.fq_channel_absmax(f(), 64, 64, None, None) == fq.FQ_ERR_NULL
+    assert L.fq_select_channels(f(), 64, 65, f(), f(), None) == fq.FQ_ERR_SHAPE
+    assert L.fq_select_channels(f(), 64, -1, f(), f(), None) == fq.FQ_ERR_SHAPE
+    assert L.fq_select_channels(f(), 60, 4, f(), f(), None) == fq.FQ_ERR_SHAPE
+    assert L.fq_select_channels(f(), 64, 4, None, f(), None) == fq.FQ_ERR_NULL
+    # retained-channel quantizer: row axis, MXFP4 or double-block NVFP4
+    mx, nvt = fq.fq_desc_mxfp4(), fq.fq_desc_nvfp4()
+    col = fq.fq_desc_mxfp4(axis=fq.FQ_AXIS_COL)
+
+    def fqr(d, retain=f(), scale=f(), rows=64, cols=64, y=f()):
+        return L.fq_fake_quant_retain(ctypes.byref(d), f(), rows, cols, y, None, None, None,
+                                      retain, scale, None)
+    assert fqr(nvt) == fq.FQ_ERR_DESC
+    assert fqr(col) == fq.FQ_ERR_DESC
+    assert fqr(mx, retain=None) == fq.FQ_ERR_NULL
+    assert fqr(mx, scale=None) == fq.FQ_ERR_NULL
+    assert fqr(mx, y=None) == fq.FQ_ERR_NULL
+    assert fqr(mx, cols=48) == fq.FQ_ERR_SHAPE
+    assert fqr(fq.fq_desc_nvfp4(outer=fq.FQ_OUTER_BLOCK128), cols=64) == fq.FQ_ERR_SHAPE
+
+
 def test_qlinear_bwd_validates(L):
     nv = fq.fq_desc_nvfp4()
     col = fq.fq_desc_nvfp4(axis=fq.FQ_AXIS_COL)

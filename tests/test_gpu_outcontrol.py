@@ -1,0 +1,95 @@
+"""GPU parity of TetraJet-v2's OsciReset tracker and static outlier-channel
+retention against the oracle: tracker state and reset weights bit-exact over
+a multi-step trajectory; per-channel calibration maxima, the selected
+channels and their FP8 scales bit-exact; the retained-channel fake quantizer
+bit-exact (codes, scales, outer scales, y) on both formats and roundings,
+including the 16384x4096 workload with 10 % of the channels retained."""
+import numpy as np
+import pytest
+import torch
+
+import fp4_block_quantization_fq_amd as fq
+import oracle
+import workloads as wl
+from gpu_util import assert_same, make_desc, to_bits, to_dev, to_np
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def test_osci_trajectory_matches_oracle():
+    rng = np.random.default_rng(21)
+    R, C = 256, 512                       # n = 131072 weights, MXFP4 groups along rows
+    n = R * C
+    w = (rng.standard_normal(n).astype(np.float32) * np.float32(0.02))
+    st_o = oracle.osci_state(n)
+    st_g = fq.osci_state(n, DEV)
+    tw = torch.from_numpy(w.copy()).to(DEV)
+    for t in range(6):
+        if t:
+            w = (w + rng.standard_normal(n).astype(np.float32) * np.float32(2e-4)).astype(np.float32)
+            tw.copy_(torch.from_numpy(w))
+        q = oracle.fake_quant(wl.f32_to_bf16_bits(w).reshape(R, C), "mx")["y"].reshape(-1)
+        oracle.osci_track(w, q, st_o, first=(t == 0))
+        fq.fq_osci_track(tw, to_dev(q), st_g, first=(t == 0))
+        torch.cuda.synchronize()
+        for k in ("w_prev", "dist_m", "dist_q"):
+            assert np.array_equal(to_np(st_g[k]).view(np.uint32), st_o[k].view(np.uint32)), (t, k)
+        assert np.array_equal(to_bits(st_g["q_prev"]), st_o["q_prev"]), t
+    w_new, osc = oracle.osci_reset(w, q, st_o, 4.0)
+    assert osc.any() and not osc.all()
+    fq.fq_osci_reset(tw, to_dev(q), st_g, 4.0)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_np(tw).view(np.uint32), w_new.view(np.uint32))
+    for k in ("w_prev", "dist_m", "dist_q"):
+        assert np.array_equal(to_np(st_g[k]).view(np.uint32), st_o[k].view(np.uint32)), k
+
+
+@pytest.mark.parametrize("shape", [(1000, 4104), (64, 64)])
+def test_channel_selection_matches_oracle(shape):
+    R, C = shape
+    x, cols = wl.activation_and_outlier_channels(shape, 1.0, 8, 100.0, seed=R)
+    half = R // 2
+    am_o = oracle.channel_absmax(x[half:], oracle.channel_absmax(x[:half]))
+    tx = to_dev(x)
+    am_g = fq.fq_channel_absmax(tx[:half].contiguous())
+    fq.fq_channel_absmax(tx[half:].contiguous(), am_g)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_np(am_g).view(np.uint32), am_o)
+    for k in (0, 8, C // 10, C):
+        ret_o, sc_o = oracle.select_channels(am_o, k)
+        ret_g, sc_g = fq.fq_select_channels(am_g, k)
+        torch.cuda.synchronize()
+        assert np.array_equal(to_np(ret_g), np.packbits(ret_o, bitorder="little")), k
+        assert np.array_equal(to_np(sc_g).view(np.uint32), sc_o.view(np.uint32)), k
+        if k == 8:
+            assert np.flatnonzero(ret_o).tolist() == cols.tolist()
+
+
+def _retain_case(x, fmt, rnd, k, seed=31):
+    ret_o, sc_o = oracle.select_channels(oracle.channel_absmax(x), k)
+    ref = oracle.fake_quant_retain(x, fmt, ret_o, sc_o, rnd, seed)
+    d = make_desc(fmt, rnd, "row", seed)
+    tx = to_dev(x)
+    R, C = x.shape
+    out = fq.alloc_outputs(d, R, C, tx.device)
+    retain = torch.from_numpy(np.packbits(ret_o, bitorder="little")).to(DEV)
+    y = fq.fq_fake_quant_retain(d, tx, retain, torch.from_numpy(sc_o).to(DEV), out=out)
+    torch.cuda.synchronize()
+    got = {"y": to_bits(y), "codes": to_np(out.codes), "scales": to_np(out.scales),
+           "outer": None if out.outer is None else to_np(out.outer)}
+    assert_same(got, ref, tag=f"retain {fmt}/{rnd}/{x.shape}/k={k}")
+
+
+@pytest.mark.parametrize("shape", [(256, 384), (130, 1024)])
+@pytest.mark.parametrize("rnd", ["rne", "sr"])
+@pytest.mark.parametrize("fmt", ["mx", "nv_128"])
+def test_fake_quant_retain_matches_oracle(fmt, rnd, shape):
+    x = wl.activation_with_outlier_channels(shape, 1.0, 6, 100.0, seed=shape[0])
+    for k in (0, 6, shape[1] // 10):
+        _retain_case(x, fmt, rnd, k)
+
+
+def test_fake_quant_retain_full_size():
+    x = wl.nv_activation(16384, 4096, seed=3)
+    _retain_case(x, "nv_128", "sr", 410, seed=1234)
