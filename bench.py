@@ -382,6 +382,54 @@ def main():
                     "GBps": round(sb / (sms * 1e-3) / 1e9, 1),
                     "frac_hbm": round(sb / (sms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
 
+    # ---------------- TetraJet-v2 controls: retained channels, OsciReset ----------------
+    outc = None
+    if not args.only:
+        log("bench: retained channels and oscillation tracker")
+        kret = COLS // 10
+        amax = fq.fq_channel_absmax(xs[0])
+        retain, cscale = fq.fq_select_channels(amax, kret)
+        ret_outs = [fq.alloc_outputs(d_nv128, ROWS, COLS, dev) for _ in range(NBUF)]
+        for i in range(NBUF):
+            fq.fq_fake_quant_retain(d_nv128, xs[i], retain, cscale, y=ys[i], out=ret_outs[i])
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for s in range(K):
+            fq.fq_fake_quant_retain(d_nv128, xs[s % NBUF], retain, cscale, y=ys[s % NBUF],
+                                    out=ret_outs[s % NBUF])
+        e1.record()
+        torch.cuda.synchronize()
+        tms = e0.elapsed_time(e1) / K
+        tb = op_bytes("nv128_rne_row", n)
+        outc = {"retain_nv128_rne_row": {
+                    "op": f"NVFP4 double-block RNE fake quant of 16384x4096 with {kret} of "
+                          f"{COLS} channels kept in FP8 E4M3", "ms": round(tms, 5), "bytes": tb,
+                    "GBps": round(tb / (tms * 1e-3) / 1e9, 1),
+                    "frac_hbm": round(tb / (tms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}}
+        # the tracker and the check over the 2880x5760 weight (16.6 M weights)
+        nw = 2880 * 5760
+        wts = [torch.randn(nw, device=dev, dtype=torch.float32) * 0.02 for _ in range(NBUF)]
+        qts = [w.to(torch.bfloat16) for w in wts]
+        sts = [fq.osci_state(nw, dev) for _ in range(NBUF)]
+        for i in range(NBUF):
+            fq.fq_osci_track(wts[i], qts[i], sts[i], first=True)
+        torch.cuda.synchronize()
+        for name, fn, by in (("osci_track", lambda i: fq.fq_osci_track(wts[i], qts[i], sts[i]),
+                              34 * nw),
+                             ("osci_reset", lambda i: fq.fq_osci_reset(wts[i], qts[i], sts[i], 4.0),
+                              32 * nw)):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for s in range(K):
+                fn(s % NBUF)
+            e1.record()
+            torch.cuda.synchronize()
+            oms = e0.elapsed_time(e1) / K
+            outc[name] = {"op": f"{name} over 2880x5760 FP32 master weights", "ms": round(oms, 5),
+                          "bytes": by, "GBps": round(by / (oms * 1e-3) / 1e9, 1),
+                          "frac_hbm": round(by / (oms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+
     # ---------------- random Hadamard transform ----------------
     rht = None
     if not args.only:
@@ -463,6 +511,7 @@ def main():
         "qlinear_bwd": qbwd,
         "qlinear_bwd_mxfp4": qbwd_mx,
         "ste_mask": ste_mask,
+        "outcontrol": outc,
         "hadamard": rht,
     }
     print(json.dumps(out), flush=True)

@@ -749,7 +749,7 @@ fq_status fq_fake_quant_retain(const fq_desc *desc, const void *x_bf16, int64_t 
     FQ_TRY(check_ptr(scales, "scales", false));
     FQ_TRY(check_ptr(outer, "outer", false, 4));
     FQ_TRY(check_ptr(retain, "retain", true, 1));
-    FQ_TRY(check_ptr(chan_scale, "chan_scale", true, 4));
+    FQ_TRY(check_ptr(chan_scale, "chan_scale", true));
     fqimpl::RetainArgs a;
     a.fmt = f.fmt;
     a.sr = desc->rounding == FQ_ROUND_SR;

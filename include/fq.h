@@ -310,7 +310,8 @@ fq_status fq_select_channels(const uint32_t *amax, int64_t cols, int64_t k, void
  * carry FP4 code 0; every FP4 block and 128-element outer maximum is taken
  * over the other elements only.  desc: MXFP4 or NVFP4 double block
  * (FQ_OUTER_BLOCK128), axis FQ_AXIS_ROW, RNE or SR; y required, codes,
- * scales, outer optional (as fq_fake_quant). */
+ * scales, outer optional (as fq_fake_quant); retain and chan_scale as written
+ * by fq_select_channels, chan_scale 16-byte aligned. */
 fq_status fq_fake_quant_retain(const fq_desc *desc, const void *x_bf16, int64_t rows,
                                int64_t cols, void *y_bf16, void *codes, void *scales,
                                float *outer, const void *retain, const float *chan_scale,
