@@ -29,7 +29,7 @@ EXPORTED = (
     "fq_desc_mxfp4", "fq_desc_nvfp4", "fq_workspace_size", "fq_quantize",
     "fq_dequantize", "fq_fake_quant", "fq_fake_quant_mask", "fq_ste_backward",
     "fq_ste_backward_mask", "fq_osci_track", "fq_osci_reset", "fq_channel_absmax",
-    "fq_select_channels", "fq_fake_quant_retain",
+    "fq_select_channels", "fq_fake_quant_retain", "fq_fake_quant_rht",
     "fq_qlinear_workspace_size", "fq_qlinear_fwd", "fq_hadamard",
     "fq_qlinear_bwd_workspace_size", "fq_qlinear_bwd", "fq_status_string",
     "fq_last_error", "fq_version",
@@ -100,6 +100,9 @@ def lib() -> ctypes.CDLL:
         L.fq_select_channels.restype = ctypes.c_int
         L.fq_fake_quant_retain.argtypes = [dp, vp, i64, i64, vp, vp, vp, vp, vp, vp, vp]
         L.fq_fake_quant_retain.restype = ctypes.c_int
+        L.fq_fake_quant_rht.argtypes = [dp, vp, i64, i64, ctypes.c_int32, ctypes.c_uint64, vp, vp,
+                                        vp, vp, vp]
+        L.fq_fake_quant_rht.restype = ctypes.c_int
         L.fq_ste_backward_mask.argtypes = [vp, vp, i64, i64, vp, vp]
         L.fq_ste_backward.restype = ctypes.c_int
         L.fq_qlinear_workspace_size.argtypes = [dp, dp, i64, i64, i64]
@@ -349,6 +352,23 @@ def fq_fake_quant_retain(desc: FqDesc, x, retain, chan_scale, y=None,
     _check(lib().fq_fake_quant_retain(ctypes.byref(desc), _ptr(x), rows, cols, _ptr(y),
                                       _ptr(codes), _ptr(scales), _ptr(outer), _ptr(retain),
                                       _ptr(chan_scale), _stream(stream)))
+    return y
+
+
+def fq_fake_quant_rht(desc: FqDesc, x, rht_block: int, rht_seed: int, y=None,
+                      out: Quantized | None = None, stream=None):
+    """Fake quantization of the random Hadamard rotation of x along the
+    quantization axis, in one pass.  Returns y."""
+    torch = _torch()
+    rows, cols = x.shape
+    if y is None:
+        y = torch.empty_like(x)
+    codes = scales = outer = None
+    if out is not None:
+        codes, scales, outer = out.codes, out.scales, out.outer
+    _check(lib().fq_fake_quant_rht(ctypes.byref(desc), _ptr(x), rows, cols, rht_block, rht_seed,
+                                   _ptr(y), _ptr(codes), _ptr(scales), _ptr(outer),
+                                   _stream(stream)))
     return y
 
 

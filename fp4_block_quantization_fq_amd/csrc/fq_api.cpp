@@ -123,7 +123,8 @@ fq_status device_status(hipError_t e, const char *what)
 // Shared body of fq_quantize / fq_fake_quant once arguments are checked.
 fq_status run_quant(const Fmt &f, const fq_desc *d, const void *x, int64_t R, int64_t C,
                     void *y, void *codes, void *scales, float *outer, void *ws,
-                    hipStream_t st, bool cached = false, void *keep = nullptr)
+                    hipStream_t st, bool cached = false, void *keep = nullptr, int rht_n = 0,
+                    uint64_t rht_seed = 0)
 {
     fqimpl::QuantArgs a;
     a.fmt = f.fmt;
@@ -140,6 +141,8 @@ fq_status run_quant(const Fmt &f, const fq_desc *d, const void *x, int64_t R, in
     a.yt = nullptr;
     a.partials = (uint32_t *)ws;
     a.keep = keep;
+    a.rht_n = rht_n;
+    a.rht_seed = rht_seed;
     a.cached_outputs = cached;
     uint32_t npart = 0;
     if (f.fmt == fqimpl::FMT_NVT) {
@@ -271,6 +274,30 @@ fq_status fq_fake_quant_mask(const fq_desc *desc, const void *x_bf16, int64_t ro
     }
     return run_quant(f, desc, x_bf16, rows, cols, y_bf16, codes, scales, outer, ws,
                      (hipStream_t)stream, false, keep);
+}
+
+fq_status fq_fake_quant_rht(const fq_desc *desc, const void *x_bf16, int64_t rows, int64_t cols,
+                            int32_t rht_block, uint64_t rht_seed, void *y_bf16, void *codes,
+                            void *scales, float *outer, void *stream)
+{
+    Fmt f;
+    FQ_TRY(check_desc(desc, &f, "desc"));
+    if (f.fmt == fqimpl::FMT_NVT)
+        return fail(FQ_ERR_DESC, "the rotated quantizer takes MXFP4 or NVFP4 FQ_OUTER_BLOCK128");
+    if (rht_block != 16 && rht_block != 128)
+        return fail(FQ_ERR_DESC, "rht_block=%d is not 16 or 128", rht_block);
+    FQ_TRY(check_shape(f, desc->axis, rows, cols));
+    const int64_t q = desc->axis == FQ_AXIS_ROW ? cols : rows;
+    if (q % rht_block != 0)
+        return fail(FQ_ERR_SHAPE, "%s=%lld must be a multiple of rht_block=%d",
+                    desc->axis == FQ_AXIS_ROW ? "cols" : "rows", (long long)q, rht_block);
+    FQ_TRY(check_ptr(x_bf16, "x", true));
+    FQ_TRY(check_ptr(y_bf16, "y", true));
+    FQ_TRY(check_ptr(codes, "codes", false));
+    FQ_TRY(check_ptr(scales, "scales", false));
+    FQ_TRY(check_ptr(outer, "outer", false, 4));
+    return run_quant(f, desc, x_bf16, rows, cols, y_bf16, codes, scales, outer, nullptr,
+                     (hipStream_t)stream, false, nullptr, rht_block, rht_seed);
 }
 
 fq_status fq_ste_backward_mask(const void *keep, const void *dy_bf16, int64_t rows,
@@ -490,7 +517,9 @@ size_t fq_qlinear_bwd_workspace_size(const fq_desc *desc_x, const fq_desc *desc_
         return 0;
     if (rht_block != 0 && rht_block != 16 && rht_block != 128) return 0;
     if (M < 1 || K < 1 || N < 1 || M > kMaxElems || K > kMaxElems || N > kMaxElems) return 0;
-    return bwd_layout(rht_block != 0, M, K, N).total;
+    // rotated operand buffers only where the rotation cannot be fused into
+    // the quantizer (per-tensor gradient format: its maximum needs a pass)
+    return bwd_layout(rht_block != 0 && fg.fmt == fqimpl::FMT_NVT, M, K, N).total;
 }
 
 fq_status fq_hadamard(const void *x_bf16, int64_t rows, int64_t cols, int32_t axis,
@@ -527,7 +556,7 @@ fq_status fq_hadamard(const void *x_bf16, int64_t rows, int64_t cols, int32_t ax
 static fq_status bwd_quant(const Fmt &f, const fq_desc *d, uint64_t seed, bool col,
                            const void *src, int64_t R, int64_t C, void *y, void *yt,
                            void *codes, void *scales, void *keep, uint32_t *parts,
-                           hipStream_t st)
+                           hipStream_t st, int rht_n = 0, uint64_t rht_seed = 0)
 {
     fqimpl::QuantArgs a;
     a.fmt = f.fmt;
@@ -543,6 +572,8 @@ static fq_status bwd_quant(const Fmt &f, const fq_desc *d, uint64_t seed, bool c
     a.scales = scales;
     a.outer = nullptr;
     a.keep = keep;
+    a.rht_n = rht_n;
+    a.rht_seed = rht_seed;
     a.partials = parts;
     a.cached_outputs = true;
     uint32_t npart = 0;
@@ -593,7 +624,10 @@ fq_status fq_qlinear_bwd(const fq_desc *desc_x, const fq_desc *desc_w, const fq_
     FQ_TRY(check_ptr(dw_bf16, "dw", true));
     FQ_TRY(check_ptr(ws, "ws", true));
     const bool rht = rht_block != 0;
-    const BwdLayout L = bwd_layout(rht, M, K, N);
+    // MXFP4 and double-block gradient quantizers rotate their segments in
+    // registers; the per-tensor format rotates in separate passes first
+    const bool rht_fused = rht && fg.fmt != fqimpl::FMT_NVT;
+    const BwdLayout L = bwd_layout(rht && !rht_fused, M, K, N);
     if (ws_bytes < L.total)
         return fail(FQ_ERR_WORKSPACE, "workspace %zu bytes < %zu required", ws_bytes, L.total);
 
@@ -609,7 +643,7 @@ fq_status fq_qlinear_bwd(const fq_desc *desc_x, const fq_desc *desc_w, const fq_
                      nullptr, nullptr, b + L.wkeep, parts, st));
     // the operands before quantization, rotated along each contraction axis
     const void *op_dy_n = dy_bf16, *op_w_n = b + L.what, *op_x_m = b + L.xhat, *op_dy_m = dy_bf16;
-    if (rht) {
+    if (rht && !rht_fused) {
         struct { const void *src; int64_t R, C; int col; size_t dst; } rot[4] = {
             {dy_bf16, M, N, 0, L.rdy_n}, {b + L.what, K, N, 0, L.rw_n},
             {b + L.xhat, M, K, 1, L.rx_m}, {dy_bf16, M, N, 1, L.rdy_m}};
@@ -642,7 +676,7 @@ fq_status fq_qlinear_bwd(const fq_desc *desc_x, const fq_desc *desc_w, const fq_
             const size_t elems = (size_t)p.R * p.C;
             void *codes = b + p.at, *scales = b + p.at + round256(elems / 2);
             FQ_TRY(bwd_quant(fg, desc_g, sg + i, p.col, p.src, p.R, p.C, nullptr, nullptr, codes,
-                             scales, nullptr, parts, st));
+                             scales, nullptr, parts, st, rht_fused ? rht_block : 0, rht_seed));
             cd[i] = codes;
             sc[i] = scales;
         }
@@ -654,7 +688,8 @@ fq_status fq_qlinear_bwd(const fq_desc *desc_x, const fq_desc *desc_w, const fq_
         for (int i = 0; i < 4; ++i) {
             const Op &p = ops[i];
             FQ_TRY(bwd_quant(fg, desc_g, sg + i, p.col, p.src, p.R, p.C, p.col ? nullptr : b + p.at,
-                             p.col ? b + p.at : nullptr, nullptr, nullptr, nullptr, parts, st));
+                             p.col ? b + p.at : nullptr, nullptr, nullptr, nullptr, parts, st,
+                             rht_fused ? rht_block : 0, rht_seed));
         }
         e = fqimpl::launch_gemm_bf16_nt_pair(b + L.dyq_n, b + L.wq_n, dx_bf16, M, K, N,
                                              b + L.xq_mt, b + L.dyq_mt, dw_bf16, K, N, M, st,

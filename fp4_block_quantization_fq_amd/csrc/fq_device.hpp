@@ -294,6 +294,80 @@ __device__ __forceinline__ uint32_t bf16_pair_rne(float lo, float hi)
 __device__ __forceinline__ uint32_t lo_bits(uint32_t pair) { return pair << 16; }
 __device__ __forceinline__ uint32_t hi_bits(uint32_t pair) { return pair & 0xFFFF0000u; }
 
+// ---- random Hadamard transform of one 16-element segment ---------------------
+// "Resumo Tecnico: TetraJet-v2", sec. 2.C (OutControl): blockwise H_n (n = 16
+// or 128) with a Philox-seeded random sign vector, in Sylvester order by
+// radix-2 FP32 butterflies, times the FP32 value nearest to 1/sqrt(n), rounded
+// to BF16.  Sign bit of position j: bit (j mod 128) of Philox4x32-10(key =
+// seed, counter = (j / 128, 0, 0, 0)), bit t of word w being bit 32w + t.
+// The 16 sign bits of positions j0 .. j0 + 15 (j0 a multiple of 16).
+__device__ __forceinline__ uint32_t sign_bits16(uint64_t j0, uint32_t seed_lo, uint32_t seed_hi)
+{
+    const u32x4 o = philox4x32_10((uint32_t)(j0 >> 7), (uint32_t)(j0 >> 39), 0u, 0u, seed_lo,
+                                  seed_hi);
+    const uint32_t b = (uint32_t)(j0 & 127);
+    const uint32_t w = o.v[b >> 5];
+    return (w >> (b & 31)) & 0xFFFFu;
+}
+
+// In-lane stages h = 1, 2, 4, 8 over 16 values.
+__device__ __forceinline__ void fwht16(float (&v)[16])
+{
+#pragma unroll
+    for (int h = 1; h < 16; h *= 2)
+#pragma unroll
+        for (int g = 0; g < 16; g += 2 * h)
+#pragma unroll
+            for (int t = g; t < g + h; ++t) {
+                const float a = v[t], b = v[t + h];
+                v[t] = a + b;
+                v[t + h] = a - b;
+            }
+}
+
+// Cross-lane stages for n = 128: lane offsets 1, 2, 4 (element half-widths
+// 16, 32, 64).  The lower lane of a pair keeps a + b, the upper a - b, with a
+// the lower lane's value.
+__device__ __forceinline__ void fwht_lanes(float (&v)[16], uint32_t lane_in_block)
+{
+#pragma unroll
+    for (int d = 1; d < 8; d *= 2) {
+        const bool upper = (lane_in_block & d) != 0;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const float p = __shfl_xor(v[i], d);
+            v[i] = upper ? (p - v[i]) : (v[i] + p);
+        }
+    }
+}
+
+__device__ __forceinline__ float flip(float e, uint32_t bits, int i)
+{
+    return as_f(as_u(e) ^ (((bits >> i) & 1u) << 31));
+}
+
+// Rotate the lane's segment in place: xp holds 16 consecutive positions
+// j0 .. j0 + 15 along the transformed axis as BF16 pairs (position 2i in the
+// low half of xp[i]); for n = 128 the 8 lanes of a 128-block are lanes
+// 8k .. 8k + 7, lane_in_block = (j0 / 16) mod 8.
+template <int N>
+__device__ __forceinline__ void rht_segment(uint32_t (&xp)[8], uint64_t j0, uint32_t seed_lo,
+                                            uint32_t seed_hi)
+{
+    const uint32_t bits = sign_bits16(j0, seed_lo, seed_hi);
+    float v[16];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        v[2 * i] = flip(as_f(lo_bits(xp[i])), bits, 2 * i);
+        v[2 * i + 1] = flip(as_f(hi_bits(xp[i])), bits, 2 * i + 1);
+    }
+    fwht16(v);
+    if (N == 128) fwht_lanes(v, (uint32_t)(j0 >> 4) & 7);
+    const float c_n = N == 16 ? 0.25f : __builtin_bit_cast(float, 0x3DB504F3u);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) xp[i] = bf16_pair_rne(c_n * v[2 * i], c_n * v[2 * i + 1]);
+}
+
 // hardware converters with a compile-time byte selector
 template <int SEL>
 __device__ __forceinline__ uint32_t hw_enc_bf16(uint32_t old, uint32_t pair, float scale)

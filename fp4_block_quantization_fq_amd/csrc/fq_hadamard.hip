@@ -42,52 +42,6 @@ __device__ __forceinline__ void st_out(uint4 *p, const uint4 &v, bool nt)
     else *p = v;
 }
 
-// The 16 sign bits of positions j0 .. j0 + 15 (j0 a multiple of 16).
-__device__ __forceinline__ uint32_t sign_bits16(uint64_t j0, uint32_t seed_lo, uint32_t seed_hi)
-{
-    const u32x4 o = philox4x32_10((uint32_t)(j0 >> 7), (uint32_t)(j0 >> 39), 0u, 0u, seed_lo,
-                                  seed_hi);
-    const uint32_t b = (uint32_t)(j0 & 127);
-    const uint32_t w = o.v[b >> 5];
-    return (w >> (b & 31)) & 0xFFFFu;
-}
-
-// In-lane stages h = 1, 2, 4, 8 over 16 values.
-__device__ __forceinline__ void fwht16(float (&v)[16])
-{
-#pragma unroll
-    for (int h = 1; h < 16; h *= 2)
-#pragma unroll
-        for (int g = 0; g < 16; g += 2 * h)
-#pragma unroll
-            for (int t = g; t < g + h; ++t) {
-                const float a = v[t], b = v[t + h];
-                v[t] = a + b;
-                v[t + h] = a - b;
-            }
-}
-
-// Cross-lane stages for n = 128: lane offsets 1, 2, 4 (element half-widths
-// 16, 32, 64).  The lower lane of a pair keeps a + b, the upper a - b, with a
-// the lower lane's value.
-__device__ __forceinline__ void fwht_lanes(float (&v)[16], uint32_t lane_in_block)
-{
-#pragma unroll
-    for (int d = 1; d < 8; d *= 2) {
-        const bool upper = (lane_in_block & d) != 0;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const float p = __shfl_xor(v[i], d);
-            v[i] = upper ? (p - v[i]) : (v[i] + p);
-        }
-    }
-}
-
-__device__ __forceinline__ float flip(float e, uint32_t bits, int i)
-{
-    return as_f(as_u(e) ^ (((bits >> i) & 1u) << 31));
-}
-
 template <int N>
 __global__ __launch_bounds__(kThreads) void k_hadamard_row(const uint4 *__restrict__ x,
                                                            uint32_t nseg, uint32_t C,

@@ -27,6 +27,8 @@ struct QuantArgs {
     void *scales;         // or null
     float *outer;         // or null
     void *keep = nullptr; // uint8 [R, C/8] STE keep mask in the layout of x, or null
+    int rht_n = 0;        // 16 / 128: quantize the random Hadamard rotation of x along
+    uint64_t rht_seed = 0; //  the quantization axis (not with the per-tensor format)
     uint32_t *partials;   // kAbsmaxPartials words (NV per-tensor only)
     bool cached_outputs;  // ordinary stores (outputs re-read right away) instead of streaming
 };

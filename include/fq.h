@@ -178,6 +178,21 @@ fq_status fq_fake_quant_mask(const fq_desc *desc, const void *x_bf16, int64_t ro
                              float *outer, void *keep, void *ws, size_t ws_bytes,
                              void *stream);
 
+/* Fake quantization of the random Hadamard rotation of x along the
+ * quantization axis, in one pass: y = dequantize(quantize(H x)), codes and
+ * scales of H x.  H is blockwise H_n (n = rht_block, 16 or 128) with the
+ * Philox sign vector of rht_seed, exactly as fq_hadamard computes it
+ * (including the BF16 rounding of the rotated values), so the result equals
+ * fq_fake_quant applied to fq_hadamard's output.  desc: MXFP4 or NVFP4
+ * FQ_OUTER_BLOCK128 (the per-tensor scale would need the rotated tensor's
+ * maximum first), either axis, RNE or SR; the quantized axis a multiple of
+ * rht_block.  y required; codes, scales, outer optional.  Source: "Resumo
+ * Tecnico: TetraJet-v2", sec. 2.C (the rotation ahead of the backward's FP4
+ * quantization). */
+fq_status fq_fake_quant_rht(const fq_desc *desc, const void *x_bf16, int64_t rows, int64_t cols,
+                            int32_t rht_block, uint64_t rht_seed, void *y_bf16, void *codes,
+                            void *scales, float *outer, void *stream);
+
 /* Clipped straight-through estimator from a keep mask written by
  * fq_fake_quant_mask: dx = dy where the element's keep bit is set, else +0.
  * keep [rows, cols / 8] (layout above), dy and dx [rows, cols] BF16, all

@@ -218,10 +218,17 @@ def test_qlinear_bwd_validates(L):
                                            0, 128, 128, 128)
     assert need > 6 * 128 * 128 * 2
     assert call(nv, col, g, ws_bytes=need - 1) == fq.FQ_ERR_WORKSPACE
+    # the double-block gradient quantizer rotates in registers: no extra space
     need_r = L.fq_qlinear_bwd_workspace_size(ctypes.byref(nv), ctypes.byref(col), ctypes.byref(g),
                                              128, 128, 128, 128)
-    assert need_r >= need + 4 * 128 * 128 * 2
-    assert call(nv, col, g, ws_bytes=need_r - 1, rht=128) == fq.FQ_ERR_WORKSPACE
+    assert need_r == need
+    # a per-tensor gradient quantizer needs the rotated operands materialized
+    need_t = L.fq_qlinear_bwd_workspace_size(ctypes.byref(nv), ctypes.byref(col), ctypes.byref(nv),
+                                             0, 128, 128, 128)
+    need_tr = L.fq_qlinear_bwd_workspace_size(ctypes.byref(nv), ctypes.byref(col), ctypes.byref(nv),
+                                              128, 128, 128, 128)
+    assert need_tr >= need_t + 4 * 128 * 128 * 2
+    assert call(nv, col, nv, ws_bytes=need_tr - 1, rht=128) == fq.FQ_ERR_WORKSPACE
     bad = fq.fq_desc_mxfp4()
     bad.reserved = 1
     assert L.fq_qlinear_bwd_workspace_size(ctypes.byref(nv), ctypes.byref(col), ctypes.byref(bad),
@@ -238,6 +245,21 @@ def test_hadamard_validates(L):
     assert L.fq_hadamard(None, 64, 128, fq.FQ_AXIS_ROW, 16, 1, y, None) == fq.FQ_ERR_NULL
     assert L.fq_hadamard(fake(0x10008), 64, 128, fq.FQ_AXIS_ROW, 16, 1, y, None) == fq.FQ_ERR_ALIGN
     assert L.fq_hadamard(x, 64, 128, fq.FQ_AXIS_ROW, 16, 1, fake(0x10100), None) == fq.FQ_ERR_SHAPE
+
+
+def test_rotated_fake_quant_validates(L):
+    mx = fq.fq_desc_mxfp4()
+    nvt = fq.fq_desc_nvfp4()
+
+    def call(d, rows=128, cols=128, blk=16, y=fake()):
+        return L.fq_fake_quant_rht(ctypes.byref(d), fake(), rows, cols, blk, 3, y, None, None,
+                                   None, None)
+    assert call(nvt) == fq.FQ_ERR_DESC                  # per-tensor scale: not fused
+    assert call(mx, blk=32) == fq.FQ_ERR_DESC
+    assert call(mx, cols=96, blk=128) == fq.FQ_ERR_SHAPE
+    assert call(mx, y=None) == fq.FQ_ERR_NULL
+    col = fq.fq_desc_mxfp4(axis=fq.FQ_AXIS_COL)
+    assert call(col, rows=96, blk=128) == fq.FQ_ERR_SHAPE
 
 
 def test_status_strings(L):
