@@ -205,13 +205,12 @@ __device__ __forceinline__ void quant_row_chunk(uint32_t c, const uint4 &v, cons
 
 // MAP = 1: one 8-element chunk per lane (units = chunks); MAP = 0: one
 // 16-element segment per lane (units = segments).
-template <int FMT, int RND, int MAP, bool NT>
+template <int FMT, int RND, int MAP, bool NT, int RHT = 0>
 __global__ __launch_bounds__(kThreads) void k_quant_row(
     const uint4 *__restrict__ x, uint32_t nunits, uint4 *__restrict__ y,
     void *__restrict__ codes, uint8_t *__restrict__ scales, float *__restrict__ outer,
     void *__restrict__ keep, const uint32_t *__restrict__ partials, uint32_t npart,
-    uint32_t seed_lo, uint32_t seed_hi, uint32_t rht_n, uint32_t C, uint32_t rs_lo,
-    uint32_t rs_hi)
+    uint32_t seed_lo, uint32_t seed_hi, uint32_t C, uint32_t rs_lo, uint32_t rs_hi)
 {
     OuterScale ot = {0.0f, 0.0f};
     if (FMT == FMT_NVT) {
@@ -226,12 +225,11 @@ __global__ __launch_bounds__(kThreads) void k_quant_row(
                                           (uint8_t *)keep, seed_lo, seed_hi);
         } else {
             uint4 v0 = x[2 * u], v1 = x[2 * u + 1];
-            if (rht_n) {
+            if (RHT) {
                 // the rotated segment (position along the row: (16 u) mod C)
                 uint32_t xp[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
                 const uint64_t j0 = ((uint64_t)u * 16) % C;
-                if (rht_n == 16) rht_segment<16>(xp, j0, rs_lo, rs_hi);
-                else rht_segment<128>(xp, j0, rs_lo, rs_hi);
+                rht_segment<RHT>(xp, j0, rs_lo, rs_hi);
                 v0 = make_uint4(xp[0], xp[1], xp[2], xp[3]);
                 v1 = make_uint4(xp[4], xp[5], xp[6], xp[7]);
             }
@@ -313,13 +311,13 @@ __device__ __forceinline__ uint32_t qc_offset(uint32_t row, uint32_t chunk)
     return b * kQcBlockBytes + (row & 7) * (kQcCols * 2) + ((chunk ^ (b >> 1)) & 7) * 16;
 }
 
-template <int FMT, int RND, bool NT>
+template <int FMT, int RND, bool NT, int RHT = 0>
 __global__ __launch_bounds__(kThreads) void k_quant_col(
     const uint4 *__restrict__ x, uint32_t R, uint32_t C, uint4 *__restrict__ y,
     uint4 *__restrict__ yt, uint8_t *__restrict__ codes, uint8_t *__restrict__ scales,
     float *__restrict__ outer, uint8_t *__restrict__ keep,
     const uint32_t *__restrict__ partials, uint32_t npart, uint32_t seed_lo, uint32_t seed_hi,
-    uint32_t rht_n, uint32_t rs_lo, uint32_t rs_hi)
+    uint32_t rs_lo, uint32_t rs_hi)
 {
     constexpr uint32_t B = (FMT == FMT_MX) ? 32 : 16;
     __shared__ __attribute__((aligned(1024))) uint8_t s_tile[kQcRows / 8 * kQcBlockBytes];
@@ -376,8 +374,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_col(
             xp[i] = lo | (hi << 16);
         }
         // the rotation along the column (a 128-block is the lane's 8-lane group)
-        if (rht_n == 16) rht_segment<16>(xp, row0, rs_lo, rs_hi);
-        else if (rht_n == 128) rht_segment<128>(xp, row0, rs_lo, rs_hi);
+        if (RHT) rht_segment<RHT>(xp, row0, rs_lo, rs_hi);
         float so = 0.0f;
         const BlockScale b = lane_block_scale<FMT>(absmax_bits_pairs8(xp), ot, so);
         if (FMT == FMT_NV128 && outer && rb == 0)
@@ -625,26 +622,33 @@ hipError_t quant_dispatch_nt(const fqimpl::QuantArgs &a, uint32_t npart, hipStre
     if (!a.col) {
         // one 16-element segment per lane for SR and for rotated inputs (a
         // Hadamard block is one lane or an 8-lane group), else one chunk of 8
-        if (RND == RND_SR || a.rht_n) {
-            const uint64_t nunits = (uint64_t)a.R * a.C / 16;
-            hipLaunchKernelGGL((k_quant_row<FMT, RND, 0, NT>), dim3(row_grid(nunits, kThreads)),
-                               dim3(kThreads), 0, st, (const uint4 *)a.x, (uint32_t)nunits,
-                               (uint4 *)a.y, a.codes, (uint8_t *)a.scales, a.outer, a.keep,
-                               parts, npart, slo, shi, (uint32_t)a.rht_n, (uint32_t)a.C, rlo,
-                               rhi);
-        } else {
-            const uint64_t nunits = (uint64_t)a.R * a.C / 8;
-            hipLaunchKernelGGL((k_quant_row<FMT, RND, 1, NT>), dim3(row_grid(nunits, kThreads)),
-                               dim3(kThreads), 0, st, (const uint4 *)a.x, (uint32_t)nunits,
-                               (uint4 *)a.y, a.codes, (uint8_t *)a.scales, a.outer, a.keep,
-                               parts, npart, slo, shi, 0u, (uint32_t)a.C, 0u, 0u);
-        }
+        const uint64_t nseg = (uint64_t)a.R * a.C / 16, nchunk = (uint64_t)a.R * a.C / 8;
+        const dim3 gs(row_grid(nseg, kThreads)), gc(row_grid(nchunk, kThreads)), b(kThreads);
+#define FQ_ROW_ARGS(n)                                                                      \
+    (const uint4 *)a.x, (uint32_t)(n), (uint4 *)a.y, a.codes, (uint8_t *)a.scales, a.outer, \
+        a.keep, parts, npart, slo, shi, (uint32_t)a.C, rlo, rhi
+        if (a.rht_n == 16)
+            hipLaunchKernelGGL((k_quant_row<FMT, RND, 0, NT, 16>), gs, b, 0, st, FQ_ROW_ARGS(nseg));
+        else if (a.rht_n == 128)
+            hipLaunchKernelGGL((k_quant_row<FMT, RND, 0, NT, 128>), gs, b, 0, st, FQ_ROW_ARGS(nseg));
+        else if (RND == RND_SR)
+            hipLaunchKernelGGL((k_quant_row<FMT, RND, 0, NT>), gs, b, 0, st, FQ_ROW_ARGS(nseg));
+        else
+            hipLaunchKernelGGL((k_quant_row<FMT, RND, 1, NT>), gc, b, 0, st, FQ_ROW_ARGS(nchunk));
+#undef FQ_ROW_ARGS
     } else {
-        hipLaunchKernelGGL((k_quant_col<FMT, RND, NT>), quant_col_grid(a.R, a.C), dim3(kThreads), 0,
-                           st, (const uint4 *)a.x, (uint32_t)a.R, (uint32_t)a.C, (uint4 *)a.y,
-                           (uint4 *)a.yt, (uint8_t *)a.codes, (uint8_t *)a.scales, a.outer,
-                           (uint8_t *)a.keep, parts, npart, slo, shi, (uint32_t)a.rht_n, rlo,
-                           rhi);
+#define FQ_COL_ARGS                                                                          \
+    (const uint4 *)a.x, (uint32_t)a.R, (uint32_t)a.C, (uint4 *)a.y, (uint4 *)a.yt,          \
+        (uint8_t *)a.codes, (uint8_t *)a.scales, a.outer, (uint8_t *)a.keep, parts, npart, slo, \
+        shi, rlo, rhi
+        const dim3 g = quant_col_grid(a.R, a.C), b(kThreads);
+        if (a.rht_n == 16)
+            hipLaunchKernelGGL((k_quant_col<FMT, RND, NT, 16>), g, b, 0, st, FQ_COL_ARGS);
+        else if (a.rht_n == 128)
+            hipLaunchKernelGGL((k_quant_col<FMT, RND, NT, 128>), g, b, 0, st, FQ_COL_ARGS);
+        else
+            hipLaunchKernelGGL((k_quant_col<FMT, RND, NT>), g, b, 0, st, FQ_COL_ARGS);
+#undef FQ_COL_ARGS
     }
     return hipGetLastError();
 }
