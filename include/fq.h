@@ -263,8 +263,12 @@ size_t fq_qlinear_bwd_workspace_size(const fq_desc *desc_x, const fq_desc *desc_
  * along M), + 3 (dY along M); desc_g->axis is ignored.  rht_block = 16 or
  * 128 first rotates both operands of each product along its contraction axis
  * by the random Hadamard transform of fq_hadamard with seed rht_seed (which
- * cancels in the exact product); 0 leaves them as they are.  Products accumulate
- * in FP32 on the matrix cores and are rounded to BF16 before the STE.
+ * cancels in the exact product); 0 leaves them as they are (with an MXFP4 or
+ * double-block desc_g the rotation runs inside the quantizers, as in
+ * fq_fake_quant_rht).  Products accumulate in FP32 on the matrix cores and are
+ * rounded to BF16 before the STE, which is applied as the product is stored.
+ * With an MXFP4 desc_g both products run on the scaled FP4 matrix cores from
+ * the gradient operands' codes and E8M0 scales.
  * Shapes: K a multiple of 8 and of desc_x's and desc_w's block sizes (128
  * for FQ_OUTER_BLOCK128); M and N multiples of 64 and of desc_g's block size
  * (128 for FQ_OUTER_BLOCK128) and of rht_block; desc_x->axis FQ_AXIS_ROW,

@@ -93,3 +93,26 @@ def test_fake_quant_retain_matches_oracle(fmt, rnd, shape):
 def test_fake_quant_retain_full_size():
     x = wl.nv_activation(16384, 4096, seed=3)
     _retain_case(x, "nv_128", "sr", 410, seed=1234)
+
+
+@pytest.mark.parametrize("n", [4, 132, 4096 * 33 + 4])
+def test_osci_sizes(n):
+    # the smallest size, a size that leaves a partial wave, and one that
+    # leaves a partial workgroup: every element tracked and checked
+    rng = np.random.default_rng(n)
+    w0 = rng.standard_normal(n).astype(np.float32)
+    w1 = (w0 + rng.standard_normal(n).astype(np.float32) * np.float32(1e-3)).astype(np.float32)
+    q0 = wl.f32_to_bf16_bits(w0)
+    q1 = wl.f32_to_bf16_bits(np.where(rng.random(n) < 0.5, w1, w0 + np.float32(0.25)))
+    st_o, st_g = oracle.osci_state(n), fq.osci_state(n, DEV)
+    tw = torch.from_numpy(w0.copy()).to(DEV)
+    oracle.osci_track(w0, q0, st_o, first=True)
+    fq.fq_osci_track(tw, to_dev(q0), st_g, first=True)
+    tw.copy_(torch.from_numpy(w1))
+    oracle.osci_track(w1, q1, st_o, first=False)
+    fq.fq_osci_track(tw, to_dev(q1), st_g)
+    w_new, osc = oracle.osci_reset(w1, q1, st_o, 8.0)
+    fq.fq_osci_reset(tw, to_dev(q1), st_g, 8.0)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_np(tw).view(np.uint32), w_new.view(np.uint32))
+    assert np.array_equal(to_bits(st_g["q_prev"]), st_o["q_prev"])
