@@ -54,10 +54,12 @@ __global__ __launch_bounds__(kThreads) void k_osci_track(const float4 *__restric
                                                          float4 *__restrict__ w_prev,
                                                          uint2 *__restrict__ q_prev,
                                                          float4 *__restrict__ dm,
-                                                         float4 *__restrict__ dq, uint32_t n4,
+                                                         float4 *__restrict__ dq, uint64_t n4,
                                                          int first)
 {
-    for (uint32_t i = blockIdx.x * kThreads + threadIdx.x; i < n4; i += gridDim.x * kThreads) {
+    // 64-bit index: n4 reaches 2^32 at the largest accepted size
+    for (uint64_t i = (uint64_t)blockIdx.x * kThreads + threadIdx.x; i < n4;
+         i += (uint64_t)gridDim.x * kThreads) {
         const float4 wv = w[i];
         const uint2 qv = q[i];
         if (first) {
@@ -96,10 +98,12 @@ __global__ __launch_bounds__(kThreads) void k_osci_reset(float4 *__restrict__ w,
                                                          float4 *__restrict__ w_prev,
                                                          uint2 *__restrict__ q_prev,
                                                          float4 *__restrict__ dm,
-                                                         float4 *__restrict__ dq, uint32_t n4,
+                                                         float4 *__restrict__ dq, uint64_t n4,
                                                          float tau)
 {
-    for (uint32_t i = blockIdx.x * kThreads + threadIdx.x; i < n4; i += gridDim.x * kThreads) {
+    // 64-bit index: n4 reaches 2^32 at the largest accepted size
+    for (uint64_t i = (uint64_t)blockIdx.x * kThreads + threadIdx.x; i < n4;
+         i += (uint64_t)gridDim.x * kThreads) {
         float4 wv = w[i];
         const uint2 qv = q[i];
         const float4 m = dm[i], d = dq[i];
@@ -293,7 +297,7 @@ hipError_t launch_osci_track(const float *w, const void *q, float *w_prev, void 
     const uint64_t n4 = (uint64_t)n / 4;
     hipLaunchKernelGGL(k_osci_track, dim3(grid_for(n4)), dim3(kThreads), 0, st,
                        (const float4 *)w, (const uint2 *)q, (float4 *)w_prev, (uint2 *)q_prev,
-                       (float4 *)dist_m, (float4 *)dist_q, (uint32_t)n4, first);
+                       (float4 *)dist_m, (float4 *)dist_q, n4, first);
     return hipGetLastError();
 }
 
@@ -303,7 +307,7 @@ hipError_t launch_osci_reset(float *w, const void *q, float *w_prev, void *q_pre
     const uint64_t n4 = (uint64_t)n / 4;
     hipLaunchKernelGGL(k_osci_reset, dim3(grid_for(n4)), dim3(kThreads), 0, st, (float4 *)w,
                        (const uint2 *)q, (float4 *)w_prev, (uint2 *)q_prev, (float4 *)dist_m,
-                       (float4 *)dist_q, (uint32_t)n4, tau);
+                       (float4 *)dist_q, n4, tau);
     return hipGetLastError();
 }
 
