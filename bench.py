@@ -28,7 +28,9 @@ roofline figures.
 The QAT linear forward (X 8192x2880 @ W 2880x5760, both NVFP4 RNE) and its
 backward (dY 8192x5760, gradient operands NVFP4 double block with stochastic
 rounding; two products) are timed after the step and reported in TFLOP/s under
-"qlinear" and "qlinear_bwd".  The CPU oracle is
+"qlinear" and "qlinear_bwd", each after 0.3 s of back-to-back calls so that the
+figures are taken at the clock that sustained matrix-core work settles at (from
+idle the first calls run up to 20 % slower).  The CPU oracle is
 timed on a bounded sample (the first rows of the same tensors) for
 "cpu_baseline".
 """
@@ -49,6 +51,7 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense BF16 MFMA, TFLOP/s
 METRIC = "FP4 fake-quant GB/s and % of HBM peak (MXFP4/NVFP4, 16384x4096 bf16)"
 ROWS, COLS = 16384, 4096
 NBUF = 3
+WARM_SECONDS = 0.3                # sustained warm-up before each matrix-core timing
 
 
 def log(msg):
@@ -98,11 +101,27 @@ def load_traffic(op: str):
     return None if ent is None else ent.get("hbm_bytes_per_launch")
 
 
+def warm(fn, torch, seconds=WARM_SECONDS):
+    """Run fn until the GPU has been busy with it for `seconds` of wall time.
+    The matrix-core kernels run at a clock that settles only after some
+    tenths of a second of sustained load (a few calls from idle run up to
+    20 % slower); their figures are taken at that settled clock, as a training
+    loop that calls them back to back sees it."""
+    for _ in range(3):
+        fn()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(10):
+            fn()
+        torch.cuda.synchronize()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=16384,
                     help="rows of the workload the CPU oracle is timed on")
@@ -269,9 +288,7 @@ def main():
         dwd = fq.fq_desc_nvfp4(axis=fq.FQ_AXIS_COL)
         qws = fq.qlinear_workspace(dxd, dwd, M, Kd, N, dev)
         yq = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-        for _ in range(3):
-            fq.fq_qlinear_fwd(dxd, dwd, xq, wq, y=yq, ws=qws)
-        torch.cuda.synchronize()
+        warm(lambda: fq.fq_qlinear_fwd(dxd, dwd, xq, wq, y=yq, ws=qws), torch)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(args.qlinear_iters):
@@ -292,9 +309,7 @@ def main():
         log("bench: qlinear mxfp4")
         dxm = fq.fq_desc_mxfp4()
         dwm = fq.fq_desc_mxfp4(axis=fq.FQ_AXIS_COL)
-        for _ in range(3):
-            fq.fq_qlinear_fwd(dxm, dwm, xq, wq, y=yq, ws=qws)
-        torch.cuda.synchronize()
+        warm(lambda: fq.fq_qlinear_fwd(dxm, dwm, xq, wq, y=yq, ws=qws), torch)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(args.qlinear_iters):
@@ -319,9 +334,7 @@ def main():
         bws = fq.qlinear_bwd_workspace(dxd, dwd, dgd, M, Kd, N, dev)
         gx = torch.empty((M, Kd), dtype=torch.bfloat16, device=dev)
         gw = torch.empty((Kd, N), dtype=torch.bfloat16, device=dev)
-        for _ in range(3):
-            fq.fq_qlinear_bwd(dxd, dwd, dgd, xq, wq, dyq, dx=gx, dw=gw, ws=bws)
-        torch.cuda.synchronize()
+        warm(lambda: fq.fq_qlinear_bwd(dxd, dwd, dgd, xq, wq, dyq, dx=gx, dw=gw, ws=bws), torch)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(args.qlinear_iters):
@@ -344,9 +357,8 @@ def main():
         mxd_x, mxd_w = fq.fq_desc_mxfp4(), fq.fq_desc_mxfp4(axis=fq.FQ_AXIS_COL)
         mxd_g = fq.fq_desc_mxfp4(rounding=fq.FQ_ROUND_SR, seed=1234)
         bws_mx = fq.qlinear_bwd_workspace(mxd_x, mxd_w, mxd_g, M, Kd, N, dev)
-        for _ in range(3):
-            fq.fq_qlinear_bwd(mxd_x, mxd_w, mxd_g, xq, wq, dyq, dx=gx, dw=gw, ws=bws_mx)
-        torch.cuda.synchronize()
+        warm(lambda: fq.fq_qlinear_bwd(mxd_x, mxd_w, mxd_g, xq, wq, dyq, dx=gx, dw=gw,
+                                       ws=bws_mx), torch)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(args.qlinear_iters):
@@ -451,10 +463,8 @@ def main():
                          "frac_hbm": round(4 * n / (hms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
         # the backward again with both products' operands rotated (128-blocks)
         bws_r = fq.qlinear_bwd_workspace(dxd, dwd, dgd, M, Kd, N, dev, rht_block=128)
-        for _ in range(2):
-            fq.fq_qlinear_bwd(dxd, dwd, dgd, xq, wq, dyq, dx=gx, dw=gw, ws=bws_r,
-                              rht_block=128, rht_seed=55)
-        torch.cuda.synchronize()
+        warm(lambda: fq.fq_qlinear_bwd(dxd, dwd, dgd, xq, wq, dyq, dx=gx, dw=gw, ws=bws_r,
+                                       rht_block=128, rht_seed=55), torch)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(args.qlinear_iters):

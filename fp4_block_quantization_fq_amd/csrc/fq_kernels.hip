@@ -285,25 +285,31 @@ __device__ __forceinline__ void scatter_pairs(uint4 (&v)[16], int k, const uint3
 // Column quantizer: the tile goes through LDS, so that every lane works on
 // one 16-row segment of one column at a time, exactly like a row-axis lane on
 // its 16-element segment (same block scale, draws and encoder), with a small
-// register footprint and many waves per CU.
+// register footprint.
 //
-//  * A workgroup owns a kQcCols x kQcRows tile (64 columns x 128 rows).  Its
-//    waves copy it into LDS with direct loads (global_load_lds_dwordx4: no
-//    registers, 1 KB of 8 full 128-byte row pieces per instruction).  LDS
-//    block b holds tile rows 8b .. 8b+7, 128 bytes each; the 16-byte chunk of
-//    columns 8g .. 8g+7 of a row in block b sits in slot g ^ (b >> 1), so the
-//    eight segments a wave reads at once (8 row blocks of one chunk) hit
-//    eight different slots, i.e. all banks.
-//  * Lane l of wave w takes row block rb = l & 7 (rows 16 rb .. 16 rb + 15)
-//    of tile columns (l >> 3) + 8 w + 32 u, u = 0, 1.  The eight lanes of a
-//    column are consecutive, so an MXFP4 block is a lane pair and the
-//    double block's 128-row outer block is the 8 lanes, as on the row axis.
-//  * Codes (8 bytes), the scale byte and the outer scale of a segment go
-//    straight to their transposed rows ([C, R/2], [C, R/B], [C, R/128]): the
-//    eight lanes of a column write one contiguous run.  The fake-quantized
-//    BF16 values replace the inputs in LDS and leave as full rows at the end.
-constexpr uint32_t kQcCols = 64, kQcRows = 128;
+//  * A workgroup of 8 waves owns a kQcCols x kQcRows tile (64 columns x 256
+//    rows).  Its waves copy it into LDS with direct loads
+//    (global_load_lds_dwordx4: no registers, 1 KB of 8 full 128-byte row
+//    pieces per instruction).  LDS block b holds tile rows 8b .. 8b+7, 128
+//    bytes each; the 16-byte chunk of columns 8g .. 8g+7 of a row in block b
+//    sits in slot g ^ ((b >> 1) & 7), so the eight segments a wave reads at
+//    once (8 row blocks of one chunk) hit eight different slots, i.e. all
+//    banks.
+//  * Waves 0-3 take tile rows 0-127, waves 4-7 rows 128-255.  Lane l of wave
+//    w takes row block rb = l & 7 (16 rows) of its half, in tile columns
+//    (l >> 3) + 8 (w & 3) + 32 u, u = 0, 1.  The eight lanes of a column are
+//    consecutive, so an MXFP4 block is a lane pair and the double block's
+//    128-row outer block is the 8 lanes, as on the row axis.
+//  * Codes, scales and outer scales are transposed outputs ([C, R/2],
+//    [C, R/B], [C, R/128]): 256 rows of one column are one 128-byte line of
+//    codes.  They are collected in LDS and leave after the tile is done as
+//    whole lines (16 lanes of 8 bytes per column), 4-byte scale words and
+//    8-byte outer pairs, instead of the 64-byte half lines one 128-row half
+//    would give.  The fake-quantized BF16 values replace the inputs in LDS
+//    and leave as full row pieces.
+constexpr uint32_t kQcCols = 64, kQcRows = 256, kQcThreads = 512;
 constexpr uint32_t kQcBlockBytes = 8 * kQcCols * 2;      // 8 rows of 128 bytes
+constexpr uint32_t kQcSegs = kQcRows / 16;               // 16-row segments per column
 
 __device__ __forceinline__ uint32_t qc_offset(uint32_t row, uint32_t chunk)
 {
@@ -312,7 +318,7 @@ __device__ __forceinline__ uint32_t qc_offset(uint32_t row, uint32_t chunk)
 }
 
 template <int FMT, int RND, bool NT, int RHT = 0>
-__global__ __launch_bounds__(kThreads) void k_quant_col(
+__global__ __launch_bounds__(kQcThreads) void k_quant_col(
     const uint4 *__restrict__ x, uint32_t R, uint32_t C, uint4 *__restrict__ y,
     uint4 *__restrict__ yt, uint8_t *__restrict__ codes, uint8_t *__restrict__ scales,
     float *__restrict__ outer, uint8_t *__restrict__ keep,
@@ -320,11 +326,17 @@ __global__ __launch_bounds__(kThreads) void k_quant_col(
     uint32_t rs_lo, uint32_t rs_hi)
 {
     constexpr uint32_t B = (FMT == FMT_MX) ? 32 : 16;
+    constexpr uint32_t NS = kQcRows / B;                  // scales per column of the tile
     __shared__ __attribute__((aligned(1024))) uint8_t s_tile[kQcRows / 8 * kQcBlockBytes];
+    // the tile's codes (segment g of column c at 128 c + 8 g), scales (column
+    // c, block k at NS c + k) and outer scales (column c, half h at 2 c + h)
+    __shared__ __attribute__((aligned(16))) uint8_t s_codes[kQcCols * kQcSegs * 8];
+    __shared__ __attribute__((aligned(16))) uint8_t s_scales[kQcCols * NS];
+    __shared__ float s_outer[kQcCols * 2];
     // clip bits of the tile for the keep mask: row r, columns 32h .. 32h + 31
     // in word 2r + h (clipped elements are rare, so they are the ones set)
     __shared__ uint32_t s_clip[kQcRows * (kQcCols / 32)];
-    static_assert(kQcRows * (kQcCols / 32) == kThreads, "one clip word per thread");
+    static_assert(kQcRows * (kQcCols / 32) == kQcThreads, "one clip word per thread");
 
     OuterScale ot = {0.0f, 0.0f};
     if (FMT == FMT_NVT) {
@@ -353,11 +365,13 @@ __global__ __launch_bounds__(kThreads) void k_quant_col(
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
-    const uint32_t rb = lane & 7;
-    const uint32_t row0 = tr0 + rb * 16;             // first row of this lane's segments
+    const uint32_t rb = lane & 7, half = wave >> 2;
+    const uint32_t seg = half * 8 + rb;              // this lane's segment of each column
+    const uint32_t rl0 = seg * 16;                   // its first tile row
+    const uint32_t row0 = tr0 + rl0;
 #pragma unroll 1
     for (uint32_t u = 0; u < 2; ++u) {
-        const uint32_t lc = (lane >> 3) + 8 * wave + 32 * u;
+        const uint32_t lc = (lane >> 3) + 8 * (wave & 3) + 32 * u;
         const uint32_t col = tc0 + lc;
         // MXFP4 pairs and double-block groups share their column and are
         // valid together (R is a multiple of B, and of 128 for the double block)
@@ -366,7 +380,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_col(
         uint32_t xp[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const uint32_t r = rb * 16 + 2 * i;
+            const uint32_t r = rl0 + 2 * i;
             const uint32_t lo = *reinterpret_cast<const uint16_t *>(
                 s_tile + qc_offset(r, lc >> 3) + byte_in_chunk);
             const uint32_t hi = *reinterpret_cast<const uint16_t *>(
@@ -377,10 +391,9 @@ __global__ __launch_bounds__(kThreads) void k_quant_col(
         if (RHT) rht_segment<RHT>(xp, row0, rs_lo, rs_hi);
         float so = 0.0f;
         const BlockScale b = lane_block_scale<FMT>(absmax_bits_pairs8(xp), ot, so);
-        if (FMT == FMT_NV128 && outer && rb == 0)
-            outer[(size_t)col * (R >> 7) + (row0 >> 7)] = so;
-        if (scales && (FMT != FMT_MX || (rb & 1) == 0))
-            scales[(size_t)col * (R / B) + row0 / B] = (uint8_t)b.code;
+        if (FMT == FMT_NV128 && rb == 0) s_outer[lc * 2 + half] = so;
+        if (FMT != FMT_MX) s_scales[lc * NS + seg] = (uint8_t)b.code;
+        else if ((rb & 1) == 0) s_scales[lc * NS + seg / 2] = (uint8_t)b.code;
         u32x4 rnd[2];
         if (RND == RND_SR) {
             const uint64_t call0 = ((uint64_t)col * R + row0) >> 3;
@@ -392,15 +405,13 @@ __global__ __launch_bounds__(kThreads) void k_quant_col(
         uint32_t cw[2], yq[8];
         encode_pairs<FMT, RND, 8>(xp, b, rnd, cw, yq);
         if (keep) {
-            // element i of the segment is row 16 rb + i of the tile
+            // element i of the segment is row rl0 + i of the tile
             for (uint32_t clip = ~keep_mask<FMT, 8>(xp, b) & 0xFFFFu; clip; clip &= clip - 1) {
                 const uint32_t i = __builtin_ctz(clip);
-                atomicOr(&s_clip[(rb * 16 + i) * (kQcCols / 32) + (lc >> 5)], 1u << (lc & 31));
+                atomicOr(&s_clip[(rl0 + i) * (kQcCols / 32) + (lc >> 5)], 1u << (lc & 31));
             }
         }
-        if (codes)
-            st_stream<NT>(reinterpret_cast<uint2 *>(codes + (size_t)col * (R >> 1) + (row0 >> 1)),
-                          make_uint2(cw[0], cw[1]));
+        *reinterpret_cast<uint2 *>(s_codes + lc * (kQcSegs * 8) + seg * 8) = make_uint2(cw[0], cw[1]);
         if (yt) {
             uint4 *dst = yt + (((size_t)col * R + row0) >> 3);
             st_stream<NT>(&dst[0], make_uint4(yq[0], yq[1], yq[2], yq[3]));
@@ -409,7 +420,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_col(
         if (y) {
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                const uint32_t r = rb * 16 + 2 * i;
+                const uint32_t r = rl0 + 2 * i;
                 *reinterpret_cast<uint16_t *>(s_tile + qc_offset(r, lc >> 3) + byte_in_chunk) =
                     (uint16_t)yq[i];
                 *reinterpret_cast<uint16_t *>(s_tile + qc_offset(r + 1, lc >> 3) + byte_in_chunk) =
@@ -417,14 +428,54 @@ __global__ __launch_bounds__(kThreads) void k_quant_col(
             }
         }
     }
-    if (!y && !keep) return;
     __syncthreads();
+    const uint32_t t = threadIdx.x;
+    if (codes) {
+        // 16 threads per column, 8 bytes (one segment) each: a wave stores four
+        // whole 128-byte lines
+#pragma unroll
+        for (uint32_t p = 0; p < 2; ++p) {
+            const uint32_t q = p * kQcThreads + t;
+            const uint32_t c = q / kQcSegs, g = q % kQcSegs;
+            if (tc0 + c < C && tr0 + g * 16 < R)
+                st_stream<NT>(reinterpret_cast<uint2 *>(codes + (size_t)(tc0 + c) * (R >> 1) +
+                                                        ((tr0 + g * 16) >> 1)),
+                              *reinterpret_cast<const uint2 *>(s_codes + q * 8));
+        }
+    }
+    if (scales && t < kQcCols * NS / 4) {
+        // four consecutive scale bytes of one column per thread
+        const uint32_t c = t / (NS / 4), k0 = (t % (NS / 4)) * 4;
+        const uint32_t first_row = tr0 + k0 * B;
+        if (tc0 + c < C && first_row < R) {
+            const uint32_t w = *reinterpret_cast<const uint32_t *>(s_scales + t * 4);
+            uint8_t *dst = scales + (size_t)(tc0 + c) * (R / B) + first_row / B;
+            if (R % (4 * B) == 0) {
+                *reinterpret_cast<uint32_t *>(dst) = w;
+            } else {
+                for (uint32_t k = 0; k < 4 && first_row + k * B < R; ++k)
+                    dst[k] = (uint8_t)(w >> (8 * k));
+            }
+        }
+    }
+    if (FMT == FMT_NV128 && outer && t < kQcCols) {
+        const uint32_t c = t;
+        if (tc0 + c < C && tr0 < R) {
+            float *dst = outer + (size_t)(tc0 + c) * (R >> 7) + (tr0 >> 7);
+            if (R % 256 == 0) {
+                *reinterpret_cast<float2 *>(dst) = make_float2(s_outer[2 * c], s_outer[2 * c + 1]);
+            } else {
+                dst[0] = s_outer[2 * c];
+                if (tr0 + 128 < R) dst[1] = s_outer[2 * c + 1];
+            }
+        }
+    }
     if (keep) {
         // thread t: tile row t / 2, columns 32 (t % 2) .. + 31 of the keep mask
-        const uint32_t r = threadIdx.x / (kQcCols / 32), h = threadIdx.x % (kQcCols / 32);
+        const uint32_t r = t / (kQcCols / 32), h = t % (kQcCols / 32);
         const uint32_t c0 = tc0 + 32 * h;
         if (tr0 + r < R && c0 < C) {
-            const uint32_t kw = ~s_clip[threadIdx.x];
+            const uint32_t kw = ~s_clip[t];
             uint8_t *dst = keep + ((size_t)(tr0 + r) * C + c0) / 8;
             if (c0 + 32 <= C && (((uintptr_t)dst) & 3) == 0) {
                 *reinterpret_cast<uint32_t *>(dst) = kw;
@@ -437,8 +488,8 @@ __global__ __launch_bounds__(kThreads) void k_quant_col(
     if (!y) return;
     // the fake-quantized tile back to [R, C] as full 128-byte row pieces
 #pragma unroll
-    for (uint32_t i = 0; i < 4; ++i) {
-        const uint32_t q = i * kThreads + threadIdx.x;
+    for (uint32_t i = 0; i < kQcRows * 8 / kQcThreads; ++i) {
+        const uint32_t q = i * kQcThreads + t;
         const uint32_t r = q >> 3, chunk = q & 7;
         if (tr0 + r < R && tc0 + chunk * 8 < C)
             st_stream<NT>(&y[(size_t)(tr0 + r) * ldx + (tc0 >> 3) + chunk],
@@ -641,7 +692,7 @@ hipError_t quant_dispatch_nt(const fqimpl::QuantArgs &a, uint32_t npart, hipStre
     (const uint4 *)a.x, (uint32_t)a.R, (uint32_t)a.C, (uint4 *)a.y, (uint4 *)a.yt,          \
         (uint8_t *)a.codes, (uint8_t *)a.scales, a.outer, (uint8_t *)a.keep, parts, npart, slo, \
         shi, rlo, rhi
-        const dim3 g = quant_col_grid(a.R, a.C), b(kThreads);
+        const dim3 g = quant_col_grid(a.R, a.C), b(kQcThreads);
         if (a.rht_n == 16)
             hipLaunchKernelGGL((k_quant_col<FMT, RND, NT, 16>), g, b, 0, st, FQ_COL_ARGS);
         else if (a.rht_n == 128)
