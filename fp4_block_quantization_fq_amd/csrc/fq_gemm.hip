@@ -22,6 +22,10 @@
 // measured).  The direct loads write 1 KB per wave instruction in lane
 // order; each lane fetches the global chunk that belongs in its LDS slot.
 //
+// Epilogue: each wave writes its 128 x 64 BF16 tile into its own 16 KB of the
+// idle stage buffers and stores it back as whole 128-byte row pieces (the
+// accumulator layout alone gives 64-byte runs of 2-byte stores).
+//
 // Workgroups are renumbered so that each XCD (the hardware deals workgroups
 // round-robin over 8 XCDs, each with its own L2) works on a contiguous run of
 // tiles, grouped 8 tile-rows at a time so that B strips are reused in L2.
@@ -65,21 +69,68 @@ struct Problem {
     int tiles;     // workgroups of this problem in the grid
 };
 
-// Output element (row, col) of C [M, N], zeroed where the keep mask clears it
-// (the straight-through gradient of a clipped element is +0).
-__device__ __forceinline__ void store_out(uint16_t *__restrict__ C,
-                                          const uint8_t *__restrict__ keep, int row, int col,
-                                          int N, float v)
-{
-    const size_t n = (size_t)row * N + col;
-    uint16_t bits = __builtin_bit_cast(uint16_t, (__bf16)v);
-    if (keep && !((keep[n >> 3] >> (n & 7)) & 1u)) bits = 0;
-    C[n] = bits;
-}
-
 __device__ __forceinline__ int swz(int row, int chunk)
 {
     return chunk ^ (row & 7) ^ ((row >> 3) & 1);
+}
+
+// Epilogue of one wave's WTM x 64 output tile.  The accumulators go to the
+// wave's own 16 KB of the (now idle) stage buffers as BF16 rows of 128 bytes
+// (16-byte chunk g of row r in slot g ^ (r & 7), so the two row groups of a
+// store instruction hit different banks), then leave as whole 128-byte row
+// pieces: lane l stores chunk l & 7 of row 8k + (l >> 3).  A 16-byte chunk
+// is 8 columns starting at a multiple of 8 and N is a multiple of 8, so it is
+// valid or invalid as a whole and its keep bits are one byte.  Accumulator
+// element v of lane l sits at row (v/4)*8 + (l/32)*4 + v%4, column l%32 of
+// its 32 x 32 tile.
+template <int TM, int TN>
+__device__ __forceinline__ void store_wave_tile(const floatx16 (&acc)[TM][TN], uint8_t *ep,
+                                                uint16_t *__restrict__ C,
+                                                const uint8_t *__restrict__ keep, int row0,
+                                                int col0, int M, int N, int lane)
+{
+    static_assert(TN * 32 * 2 == 128, "one 128-byte LDS row per tile row");
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int r = i * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
+                const int c = j * 32 + (lane & 31);
+                *reinterpret_cast<uint16_t *>(ep + r * 128 + (((c >> 3) ^ (r & 7)) << 4) +
+                                              (c & 7) * 2) =
+                    __builtin_bit_cast(uint16_t, (__bf16)acc[i][j][v]);
+            }
+    // the keep bytes of all chunks first, so that their loads overlap
+    constexpr int NCH = TM * 32 / 8;
+    uint32_t kb[NCH];
+#pragma unroll
+    for (int k = 0; k < NCH; ++k) {
+        const int row = row0 + k * 8 + (lane >> 3), col = col0 + (lane & 7) * 8;
+        kb[k] = (keep && row < M && col < N) ? keep[((size_t)row * N + col) >> 3] : 0xFFu;
+    }
+    // the wave reads back only what it wrote itself: LDS executes one wave's
+    // instructions in order, so no barrier is needed
+#pragma unroll
+    for (int k = 0; k < NCH; ++k) {
+        const int r = k * 8 + (lane >> 3), g = lane & 7;
+        const int row = row0 + r, col = col0 + g * 8;
+        uint4 w = *reinterpret_cast<const uint4 *>(ep + r * 128 + ((g ^ (r & 7)) << 4));
+        if (row < M && col < N) {
+            const size_t n = (size_t)row * N + col;
+            if (keep) {
+                // zero the elements whose keep bit is clear
+                const uint32_t b = kb[k];
+                const uint32_t m0 = ((b & 1u) ? 0xFFFFu : 0u) | ((b & 2u) ? 0xFFFF0000u : 0u);
+                const uint32_t m1 = ((b & 4u) ? 0xFFFFu : 0u) | ((b & 8u) ? 0xFFFF0000u : 0u);
+                const uint32_t m2 = ((b & 16u) ? 0xFFFFu : 0u) | ((b & 32u) ? 0xFFFF0000u : 0u);
+                const uint32_t m3 = ((b & 64u) ? 0xFFFFu : 0u) | ((b & 128u) ? 0xFFFF0000u : 0u);
+                w = make_uint4(w.x & m0, w.y & m1, w.z & m2, w.w & m3);
+            }
+            *reinterpret_cast<uint4 *>(C + n) = w;
+        }
+    }
 }
 
 // Issue the direct loads of one ROWS-row operand tile at k0 into LDS.  Wave
@@ -190,21 +241,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_nt(Problem p0, Problem p1)
         __syncthreads();                    // all loads landed, all reads of `cur` done
     }
 
-    // epilogue: accumulator element v of lane l sits at row (v/4)*8 + (l/32)*4 + v%4,
-    // column l%32 of its 32 x 32 tile
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            const int col = tn * BN + wn * WTN + j * 32 + (lane & 31);
-            if (col >= N) continue;
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int row = tm * BM + wm * WTM + i * 32 + (v >> 2) * 8 +
-                                (lane >> 5) * 4 + (v & 3);
-                if (row < M) store_out(C, keep, row, col, N, acc[i][j][v]);
-            }
-        }
+    // epilogue through this wave's 16 KB of the stage buffers (all reads of
+    // them ended at the last barrier)
+    store_wave_tile<TM, TN>(acc, lds + wave * (WTM * WTN * 2), C, keep, tm * BM + wm * WTM,
+                            tn * BN + wn * WTN, M, N, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -389,19 +429,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mxfp4_nt(Fp4Problem p0, Fp
         if (kt + 1 < nk) stage(kt + 1, lds1, lds0, sc1, sc0);
     }
 
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            const int col = tn * BN + wn * WTN + j * 32 + (lane & 31);
-            if (col >= N) continue;
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int row = tm * BM + wm * WTM + i * 32 + (v >> 2) * 8 +
-                                (lane >> 5) * 4 + (v & 3);
-                if (row < M) store_out(C, keep, row, col, N, acc[i][j][v]);
-            }
-        }
+    // epilogue through this wave's 16 KB of the stage buffers (all reads of
+    // them ended at the last barrier)
+    uint8_t *ep = (wave < 4 ? lds0 : lds1) + (wave & 3) * (WTM * WTN * 2);
+    store_wave_tile<TM, TN>(acc, ep, C, keep, tm * BM + wm * WTM, tn * BN + wn * WTN, M, N,
+                            lane);
 }
 
 int tile_count(int64_t M, int64_t N) { return (int)(((M + BM - 1) / BM) * ((N + BN - 1) / BN)); }
@@ -420,6 +452,12 @@ Problem make_problem(const void *a, const void *bt, void *c, int64_t M, int64_t 
     return p;
 }
 
+// The epilogue stores 16-byte chunks of 8 columns: C rows must be whole chunks.
+bool epilogue_ok(const void *c, int64_t N)
+{
+    return N % 8 == 0 && ((uintptr_t)c & 15) == 0;
+}
+
 }  // namespace
 
 namespace fqimpl {
@@ -427,6 +465,7 @@ namespace fqimpl {
 hipError_t launch_gemm_bf16_nt(const void *a, const void *bt, void *c, int64_t M, int64_t N,
                                int64_t K, hipStream_t stream)
 {
+    if (!epilogue_ok(c, N)) return hipErrorInvalidValue;
     Problem p0 = make_problem(a, bt, c, M, N, K), p1 = p0;
     p1.tiles = 0;
     hipLaunchKernelGGL(k_gemm_nt, dim3((uint32_t)p0.tiles), dim3(kThreads), 0, stream, p0, p1);
@@ -438,6 +477,7 @@ hipError_t launch_gemm_bf16_nt_pair(const void *a0, const void *bt0, void *c0, i
                                     void *c1, int64_t M1, int64_t N1, int64_t K1,
                                     hipStream_t stream, const void *keep0, const void *keep1)
 {
+    if (!epilogue_ok(c0, N0) || !epilogue_ok(c1, N1)) return hipErrorInvalidValue;
     Problem p0 = make_problem(a0, bt0, c0, M0, N0, K0);
     Problem p1 = make_problem(a1, bt1, c1, M1, N1, K1);
     p0.keep = (const uint8_t *)keep0;
@@ -473,6 +513,8 @@ hipError_t launch_gemm_mxfp4_nt_pair(const Fp4Operands &o0, const Fp4Operands &o
         p.tiles = tile_count(o.M, o.N);
         return p;
     };
+    if (!epilogue_ok(o0.c, o0.N) || (count > 1 && !epilogue_ok(o1.c, o1.N)))
+        return hipErrorInvalidValue;
     Fp4Problem p0 = mk(o0), p1 = mk(count > 1 ? o1 : o0);
     if (count < 2) {
         p1.tiles = 0;
