@@ -14,7 +14,7 @@
 // global memory into LDS with gfx950's global_load_lds_dwordx4 (no staging
 // registers), double-buffered, so the loads of step k+1 overlap the MFMAs of
 // step k.  Each wave issues v_mfma_f32_32x32x16_bf16 on 4 x 2 accumulator
-// tiles, one fragment read interleaved between MFMA pairs.
+// tiles, its fragment reads interleaved with the MFMAs.
 //
 // LDS layout: one 128-byte row per tile row (64 BF16 of K).  Its eight
 // 16-byte chunks are XOR-swizzled by (row & 7) ^ ((row >> 3) & 1), so the
@@ -231,11 +231,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_nt(Problem p0, Problem p1)
                 for (int j = 0; j < TN; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j],
                                                                         0, 0, 0);
-            // interleave: one fragment read between MFMA pairs
-            for (int q = 0; q < TM + TN; ++q) {
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
-                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // MFMA
-            }
+            // the compiler's single-wave MFMA interleaving strategy: spreads the
+            // fragment reads among the MFMAs (measured 2 % faster than one read
+            // between MFMA pairs placed by hand)
+            __builtin_amdgcn_iglp_opt(1);
         }
         __builtin_amdgcn_s_waitcnt(0);      // this wave's loads of step kt+1 have landed
         __syncthreads();                    // all loads landed, all reads of `cur` done
