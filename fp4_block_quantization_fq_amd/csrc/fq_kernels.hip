@@ -506,21 +506,40 @@ __device__ __forceinline__ float stored_s_eff(uint32_t code, float s)
     return (FMT == FMT_MX) ? e8m0_value(code) : e4m3_value(code) * s;
 }
 
+constexpr uint32_t kDequantChunks = 2;
+
 template <int FMT>
 __global__ __launch_bounds__(kThreads) void k_dequant_row(
     const uint32_t *__restrict__ codes, const uint8_t *__restrict__ scales,
     const float *__restrict__ outer, uint32_t nchunks, uint4 *__restrict__ y)
 {
+    // two chunks per lane, 64 apart, with all loads issued before any decode:
+    // twice the bytes in flight per wave for the small code and scale reads
+    constexpr uint32_t U = kDequantChunks;
     const float s_t = (FMT == FMT_NVT) ? outer[0] : 0.0f;
-    for (uint32_t c = blockIdx.x * kThreads + threadIdx.x; c < nchunks;
-         c += gridDim.x * kThreads) {
-        const uint32_t cw = codes[c];
-        float s = s_t;
-        if (FMT == FMT_NV128) s = outer[c >> 4];
-        const float se = stored_s_eff<FMT>(scales[FMT == FMT_MX ? (c >> 2) : (c >> 1)], s);
-        uint32_t yp[4];
-        decode8<FMT>(cw, se, yp);
-        st_stream<true>(&y[c], make_uint4(yp[0], yp[1], yp[2], yp[3]));
+    const uint32_t lane = threadIdx.x & 63;
+    const uint32_t stride = gridDim.x * kThreads * U;
+    for (uint32_t base = (blockIdx.x * kThreads + (threadIdx.x & ~63u)) * U; base < nchunks;
+         base += stride) {
+        uint32_t cw[U], sc[U];
+        float s[U];
+#pragma unroll
+        for (uint32_t k = 0; k < U; ++k) {
+            const uint32_t c = base + k * 64 + lane;
+            const bool ok = c < nchunks;
+            cw[k] = ok ? codes[c] : 0u;
+            s[k] = s_t;
+            if (FMT == FMT_NV128) s[k] = ok ? outer[c >> 4] : 0.0f;
+            sc[k] = ok ? scales[FMT == FMT_MX ? (c >> 2) : (c >> 1)] : 0u;
+        }
+#pragma unroll
+        for (uint32_t k = 0; k < U; ++k) {
+            const uint32_t c = base + k * 64 + lane;
+            if (c >= nchunks) continue;
+            uint32_t yp[4];
+            decode8<FMT>(cw[k], stored_s_eff<FMT>(sc[k], s[k]), yp);
+            st_stream<true>(&y[c], make_uint4(yp[0], yp[1], yp[2], yp[3]));
+        }
     }
 }
 
@@ -748,7 +767,9 @@ static hipError_t dequant_dispatch(int col, const void *codes, const void *scale
 {
     if (!col) {
         const uint64_t nchunks = (uint64_t)R * C / 8;
-        hipLaunchKernelGGL(k_dequant_row<FMT>, dim3(row_grid(nchunks, kThreads)), dim3(kThreads),
+        hipLaunchKernelGGL(k_dequant_row<FMT>,
+                           dim3(row_grid((nchunks + kDequantChunks - 1) / kDequantChunks, kThreads)),
+                           dim3(kThreads),
                            0, st, (const uint32_t *)codes, (const uint8_t *)scales, outer,
                            (uint32_t)nchunks, (uint4 *)y);
     } else {
