@@ -132,8 +132,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print("bench.py: this build measures one GPU only (--gpus 1); the multi-GPU "
-              "sharding of this path is a design note, not a benchmark.", file=sys.stderr)
+        print("bench.py: measures one GPU only (--gpus 1); how the path shards across GPUs "
+              "is a design note, not a benchmark.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
