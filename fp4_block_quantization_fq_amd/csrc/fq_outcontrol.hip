@@ -192,83 +192,110 @@ __global__ __launch_bounds__(kThreads) void k_select_channels(const uint32_t *__
 // FP8 E4M3 fake quantization under the channel scale s: a = |x| / s (IEEE
 // division), E4M3 nearest-even saturating at 448, value * s, sign kept; a
 // zero scale gives +-0.
-__device__ __forceinline__ float fp8_fake(float x, float s)
+__device__ __forceinline__ float fp8_fake(float x, const BlockScale &s)
 {
-    float mag = 0.0f;
-    if (s != 0.0f) mag = e4m3_value(e4m3_encode_sat(__builtin_fabsf(x) / s)) * s;
+    // RN(|x| / s) by the corrected reciprocal, as for the FP4 block quotient
+    const float a = div_corrected(__builtin_fabsf(x) * s.xs, s.sq, s.rcp);
+    const float mag = e4m3_value(e4m3_encode_sat(a)) * s.s_eff;
     return as_f(as_u(mag) | (as_u(x) & 0x80000000u));
 }
 
 // One 8-element chunk per lane, as the row quantizer's chunk mapping; a
-// workgroup covers 256 consecutive chunks of one row (row and part from the
-// workgroup index, so no per-lane division), which also gives every lane its
-// channels directly: chunk j of a row holds columns 8j .. 8j + 7, retain byte
-// j, channel scales 8j .. 8j + 7 (two 16-byte loads).
+// workgroup covers 256 consecutive chunks of kRetainRows consecutive rows
+// (row group and part from the workgroup index, so no per-lane division),
+// which also gives every lane its channels directly: chunk j of a row holds
+// columns 8j .. 8j + 7, retain byte j, channel scales 8j .. 8j + 7 (two
+// 16-byte loads).  The lane sets up the correctly rounded quotient by each of
+// its eight channel scales once (reciprocal, and the 2^64 pre-scaling of
+// tiny scales, exactly as for an NVFP4 block scale) and reuses it for all
+// rows of its group.
+constexpr uint32_t kRetainRows = 8;
+
 template <int FMT, int RND, bool NT>
 __global__ __launch_bounds__(kThreads) void k_quant_row_retain(
-    const uint4 *__restrict__ x, uint32_t cpr, uint32_t wpr, const uint8_t *__restrict__ retain,
-    const float4 *__restrict__ chan_scale, uint4 *__restrict__ y, uint32_t *__restrict__ codes,
-    uint8_t *__restrict__ scales, float *__restrict__ outer, uint32_t seed_lo, uint32_t seed_hi)
+    const uint4 *__restrict__ x, uint32_t R, uint32_t cpr, uint32_t wpr,
+    const uint8_t *__restrict__ retain, const float4 *__restrict__ chan_scale,
+    uint4 *__restrict__ y, uint32_t *__restrict__ codes, uint8_t *__restrict__ scales,
+    float *__restrict__ outer, uint32_t seed_lo, uint32_t seed_hi)
 {
     const uint32_t lane = threadIdx.x & 63;
-    const uint32_t row = blockIdx.x / wpr, part = blockIdx.x % wpr;
+    const uint32_t group = blockIdx.x / wpr, part = blockIdx.x % wpr;
     const uint32_t j = part * kThreads + threadIdx.x;       // chunk within the row
     if (j >= cpr) return;      // block groups never straddle this edge (C % B == 0)
-    const size_t c = (size_t)row * cpr + j;
-    const uint4 v = x[c];
     const uint32_t rbits = retain[j];                       // bit e: element e is an FP8 channel
-    const float4 cs0 = chan_scale[2 * j], cs1 = chan_scale[2 * j + 1];
-    const uint32_t xp[4] = {v.x, v.y, v.z, v.w};
-    // FP4 maxima over the other elements only
-    uint32_t mp[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const uint32_t keep_lo = ((rbits >> (2 * i)) & 1u) ? 0u : 0x7FFFu;
-        const uint32_t keep_hi = ((rbits >> (2 * i + 1)) & 1u) ? 0u : 0x7FFF0000u;
-        mp[i] = xp[i] & (keep_lo | keep_hi);
-    }
-    const uint32_t m = pkmax_u16(pkmax_u16(mp[0], mp[1]), pkmax_u16(mp[2], mp[3]));
-    const OuterScale ot = {0.0f, 0.0f};
-    float so = 0.0f;
-    const BlockScale b = chunk_block_scale<FMT>(max(m & 0xFFFFu, m >> 16), ot, so);
-    if (FMT == FMT_NV128 && outer && (lane & 15) == 0) outer[c >> 4] = so;
-    if (scales) {
-        if (FMT == FMT_MX) {
-            if ((lane & 3) == 0) scales[c >> 2] = (uint8_t)b.code;
-        } else {
-            if ((lane & 1) == 0) scales[c >> 1] = (uint8_t)b.code;
-        }
-    }
-    u32x4 rnd[1];
-    if (RND == RND_SR) rnd[0] = philox4x32_10((uint32_t)c, (uint32_t)(c >> 32), 0u, 0u, seed_lo,
-                                              seed_hi);
-    uint32_t cw[1], yp[4];
-    encode_pairs<FMT, RND, 4>(xp, b, rnd, cw, yp);
+    BlockScale ch[8];
     if (rbits) {
-        // every element's FP8 value, then a select per element
+        const float4 cs0 = chan_scale[2 * j], cs1 = chan_scale[2 * j + 1];
         const float sc[8] = {cs0.x, cs0.y, cs0.z, cs0.w, cs1.x, cs1.y, cs1.z, cs1.w};
-        uint32_t nib = 0;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) nib |= ((rbits >> e) & 1u) * (0xFu << (4 * e));
-        cw[0] &= ~nib;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint32_t f = bf16_pair_rne(fp8_fake(bf16_lo(xp[i]), sc[2 * i]),
-                                             fp8_fake(bf16_hi(xp[i]), sc[2 * i + 1]));
-            const uint32_t sel = (((rbits >> (2 * i)) & 1u) ? 0xFFFFu : 0u) |
-                                 (((rbits >> (2 * i + 1)) & 1u) ? 0xFFFF0000u : 0u);
-            yp[i] = (f & sel) | (yp[i] & ~sel);
+        for (int e = 0; e < 8; ++e) {
+            ch[e].s_eff = sc[e];
+            ch[e].code = 0;
+            finish_nv_scale(ch[e]);
         }
     }
-    if (codes) {
-        if (NT) __builtin_nontemporal_store(cw[0], &codes[c]);
-        else codes[c] = cw[0];
-    }
-    if (y) {
-        typedef uint32_t u32v4 __attribute__((ext_vector_type(4)));
-        const u32v4 o = {yp[0], yp[1], yp[2], yp[3]};
-        if (NT) __builtin_nontemporal_store(o, reinterpret_cast<u32v4 *>(&y[c]));
-        else *reinterpret_cast<u32v4 *>(&y[c]) = o;
+    // the FP4 maxima skip the retained elements
+    uint32_t keep[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        keep[i] = (((rbits >> (2 * i)) & 1u) ? 0u : 0x7FFFu) |
+                  (((rbits >> (2 * i + 1)) & 1u) ? 0u : 0x7FFF0000u);
+    // the retained elements' code nibbles and BF16 halves
+    uint32_t nib = 0, sel[4];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) nib |= ((rbits >> e) & 1u) * (0xFu << (4 * e));
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        sel[i] = (((rbits >> (2 * i)) & 1u) ? 0xFFFFu : 0u) |
+                 (((rbits >> (2 * i + 1)) & 1u) ? 0xFFFF0000u : 0u);
+
+    // every lane of a workgroup has the same row group: the exit is uniform
+    for (uint32_t r = 0; r < kRetainRows; ++r) {
+        const uint32_t row = group * kRetainRows + r;
+        if (row >= R) break;
+        const size_t c = (size_t)row * cpr + j;
+        const uint4 v = x[c];
+        const uint32_t xp[4] = {v.x, v.y, v.z, v.w};
+        uint32_t mp[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mp[i] = xp[i] & keep[i];
+        const uint32_t m = pkmax_u16(pkmax_u16(mp[0], mp[1]), pkmax_u16(mp[2], mp[3]));
+        const OuterScale ot = {0.0f, 0.0f};
+        float so = 0.0f;
+        const BlockScale b = chunk_block_scale<FMT>(max(m & 0xFFFFu, m >> 16), ot, so);
+        if (FMT == FMT_NV128 && outer && (lane & 15) == 0) outer[c >> 4] = so;
+        if (scales) {
+            if (FMT == FMT_MX) {
+                if ((lane & 3) == 0) scales[c >> 2] = (uint8_t)b.code;
+            } else {
+                if ((lane & 1) == 0) scales[c >> 1] = (uint8_t)b.code;
+            }
+        }
+        u32x4 rnd[1];
+        if (RND == RND_SR)
+            rnd[0] = philox4x32_10((uint32_t)c, (uint32_t)(c >> 32), 0u, 0u, seed_lo, seed_hi);
+        uint32_t cw[1], yp[4];
+        encode_pairs<FMT, RND, 4>(xp, b, rnd, cw, yp);
+        if (rbits) {
+            // every element's FP8 value, then a select per element
+            cw[0] &= ~nib;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t f = bf16_pair_rne(fp8_fake(bf16_lo(xp[i]), ch[2 * i]),
+                                                 fp8_fake(bf16_hi(xp[i]), ch[2 * i + 1]));
+                yp[i] = (f & sel[i]) | (yp[i] & ~sel[i]);
+            }
+        }
+        if (codes) {
+            if (NT) __builtin_nontemporal_store(cw[0], &codes[c]);
+            else codes[c] = cw[0];
+        }
+        if (y) {
+            typedef uint32_t u32v4 __attribute__((ext_vector_type(4)));
+            const u32v4 o = {yp[0], yp[1], yp[2], yp[3]};
+            if (NT) __builtin_nontemporal_store(o, reinterpret_cast<u32v4 *>(&y[c]));
+            else *reinterpret_cast<u32v4 *>(&y[c]) = o;
+        }
     }
 }
 
@@ -277,12 +304,13 @@ hipError_t retain_dispatch(const fqimpl::RetainArgs &a, hipStream_t st)
 {
     const uint32_t cpr = (uint32_t)(a.C / 8);
     const uint32_t wpr = (cpr + kThreads - 1) / kThreads;
-    const uint64_t grid = (uint64_t)a.R * wpr;
+    const uint64_t groups = ((uint64_t)a.R + kRetainRows - 1) / kRetainRows;
+    const uint64_t grid = groups * wpr;
     const uint32_t slo = (uint32_t)a.seed, shi = (uint32_t)(a.seed >> 32);
     hipLaunchKernelGGL((k_quant_row_retain<FMT, RND, true>), dim3((uint32_t)grid), dim3(kThreads),
-                       0, st, (const uint4 *)a.x, cpr, wpr, (const uint8_t *)a.retain,
-                       (const float4 *)a.chan_scale, (uint4 *)a.y, (uint32_t *)a.codes,
-                       (uint8_t *)a.scales, a.outer, slo, shi);
+                       0, st, (const uint4 *)a.x, (uint32_t)a.R, cpr, wpr,
+                       (const uint8_t *)a.retain, (const float4 *)a.chan_scale, (uint4 *)a.y,
+                       (uint32_t *)a.codes, (uint8_t *)a.scales, a.outer, slo, shi);
     return hipGetLastError();
 }
 
