@@ -368,6 +368,22 @@ __device__ __forceinline__ void rht_segment(uint32_t (&xp)[8], uint64_t j0, uint
     for (int i = 0; i < 8; ++i) xp[i] = bf16_pair_rne(c_n * v[2 * i], c_n * v[2 * i + 1]);
 }
 
+// ---- column tile in LDS (column quantizer, column Hadamard transform) ------
+// A 64-column x 256-row BF16 tile: LDS block b holds tile rows 8b .. 8b+7,
+// 128 bytes each, and the 16-byte chunk of columns 8g .. 8g+7 of a row in
+// block b sits in slot g ^ ((b >> 1) & 7), so that eight lanes reading one
+// chunk of eight row blocks hit eight different slots.
+typedef __attribute__((address_space(3))) void lds_void;   // direct-load LDS target
+constexpr uint32_t kQcCols = 64, kQcRows = 256, kQcThreads = 512;
+constexpr uint32_t kQcBlockBytes = 8 * kQcCols * 2;      // 8 rows of 128 bytes
+constexpr uint32_t kQcSegs = kQcRows / 16;               // 16-row segments per column
+
+__device__ __forceinline__ uint32_t qc_offset(uint32_t row, uint32_t chunk)
+{
+    const uint32_t b = row >> 3;
+    return b * kQcBlockBytes + (row & 7) * (kQcCols * 2) + ((chunk ^ (b >> 1)) & 7) * 16;
+}
+
 // hardware converters with a compile-time byte selector
 template <int SEL>
 __device__ __forceinline__ uint32_t hw_enc_bf16(uint32_t old, uint32_t pair, float scale)

@@ -70,52 +70,75 @@ __global__ __launch_bounds__(kThreads) void k_hadamard_row(const uint4 *__restri
     }
 }
 
-// Column tile as the column quantizer's: 8 columns x 16 rows per lane, 8
-// lanes stacking 128 rows, a workgroup 64 columns x 512 rows.
+// Column transform through LDS, with the column quantizer's tile and lane
+// mapping: a workgroup of 8 waves copies a 64-column x 256-row tile into LDS
+// with direct loads, every lane rotates one 16-row segment of one column
+// (the 8 lanes of a column's 128-row block are consecutive, so the
+// cross-lane butterflies of a 128-block stay inside an 8-lane group), writes
+// it back, and the tile leaves as full 128-byte row pieces.
 template <int N>
-__global__ __launch_bounds__(kThreads) void k_hadamard_col(const uint4 *__restrict__ x,
-                                                           uint32_t R, uint32_t C,
-                                                           uint4 *__restrict__ y, float c_n,
-                                                           uint32_t seed_lo, uint32_t seed_hi,
-                                                           int nt)
+__global__ __launch_bounds__(kQcThreads) void k_hadamard_col(const uint4 *__restrict__ x,
+                                                             uint32_t R, uint32_t C,
+                                                             uint4 *__restrict__ y,
+                                                             uint32_t seed_lo, uint32_t seed_hi,
+                                                             int nt)
 {
+    __shared__ __attribute__((aligned(1024))) uint8_t s_tile[kQcRows / 8 * kQcBlockBytes];
     const uint32_t lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const uint32_t tiles_c = (C + 63) >> 6;
-    const uint32_t rb = lane & 7;
-    const uint32_t col0 = (blockIdx.x % tiles_c) * 64 + (lane >> 3) * 8;
-    const uint32_t row0 = (((blockIdx.x / tiles_c) * 4 + wave) * 8 + rb) * 16;
-    if (col0 >= C || row0 >= R) return;     // 128-row groups are valid together (R % N == 0)
+    const uint32_t tiles_c = (C + kQcCols - 1) / kQcCols;
+    const uint32_t tc0 = (blockIdx.x % tiles_c) * kQcCols;
+    const uint32_t tr0 = (blockIdx.x / tiles_c) * kQcRows;
     const uint32_t ldx = C >> 3;
-    uint4 v[16];
+    // wave w fills blocks 4w .. 4w+3; rows and chunks outside the tensor
+    // re-read its last row / chunk (the segments they would feed are unused)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) v[r] = x[(size_t)(row0 + r) * ldx + (col0 >> 3)];
-    const uint32_t bits = sign_bits16(row0, seed_lo, seed_hi);
+    for (uint32_t i = 0; i < 4; ++i) {
+        const uint32_t blk = wave * 4 + i;
+        const uint32_t row = min(tr0 + blk * 8 + (lane >> 3), R - 1);
+        const uint32_t chunk = min((tc0 >> 3) + (((lane & 7) ^ (blk >> 1)) & 7), ldx - 1);
+        __builtin_amdgcn_global_load_lds((const void *)(x + (size_t)row * ldx + chunk),
+                                         (lds_void *)(s_tile + blk * kQcBlockBytes), 16, 0, 0);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+
+    const uint32_t rl0 = ((wave >> 2) * 8 + (lane & 7)) * 16;   // the lane's first tile row
+    const uint32_t row0 = tr0 + rl0;
+#pragma unroll 1
+    for (uint32_t u = 0; u < 2; ++u) {
+        const uint32_t lc = (lane >> 3) + 8 * (wave & 3) + 32 * u;
+        // a 128-row block's 8 lanes are valid together (R % N == 0)
+        if (tc0 + lc >= C || row0 >= R) continue;
+        const uint32_t byte_in_chunk = (lc & 7) * 2;
+        uint32_t xp[8];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        float lo[16], hi[16];      // columns 2k and 2k+1 down the 16 rows
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const uint32_t wd = k == 0 ? v[r].x : k == 1 ? v[r].y : k == 2 ? v[r].z : v[r].w;
-            lo[r] = flip(as_f(lo_bits(wd)), bits, r);
-            hi[r] = flip(as_f(hi_bits(wd)), bits, r);
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t r = rl0 + 2 * i;
+            const uint32_t lo = *reinterpret_cast<const uint16_t *>(
+                s_tile + qc_offset(r, lc >> 3) + byte_in_chunk);
+            const uint32_t hi = *reinterpret_cast<const uint16_t *>(
+                s_tile + qc_offset(r + 1, lc >> 3) + byte_in_chunk);
+            xp[i] = lo | (hi << 16);
         }
-        fwht16(lo);
-        fwht16(hi);
-        if (N == 128) {
-            fwht_lanes(lo, rb);
-            fwht_lanes(hi, rb);
-        }
+        rht_segment<N>(xp, row0, seed_lo, seed_hi);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const uint32_t wd = bf16_pair_rne(c_n * lo[r], c_n * hi[r]);
-            if (k == 0) v[r].x = wd;
-            else if (k == 1) v[r].y = wd;
-            else if (k == 2) v[r].z = wd;
-            else v[r].w = wd;
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t r = rl0 + 2 * i;
+            *reinterpret_cast<uint16_t *>(s_tile + qc_offset(r, lc >> 3) + byte_in_chunk) =
+                (uint16_t)xp[i];
+            *reinterpret_cast<uint16_t *>(s_tile + qc_offset(r + 1, lc >> 3) + byte_in_chunk) =
+                (uint16_t)(xp[i] >> 16);
         }
     }
+    __syncthreads();
 #pragma unroll
-    for (int r = 0; r < 16; ++r) st_out(&y[(size_t)(row0 + r) * ldx + (col0 >> 3)], v[r], nt != 0);
+    for (uint32_t i = 0; i < kQcRows * 8 / kQcThreads; ++i) {
+        const uint32_t q = i * kQcThreads + threadIdx.x;
+        const uint32_t r = q >> 3, chunk = q & 7;
+        if (tr0 + r < R && tc0 + chunk * 8 < C)
+            st_out(&y[(size_t)(tr0 + r) * ldx + (tc0 >> 3) + chunk],
+                   *reinterpret_cast<const uint4 *>(s_tile + qc_offset(r, chunk)), nt != 0);
+    }
 }
 
 }  // namespace
@@ -141,13 +164,13 @@ hipError_t launch_hadamard(const void *x, int64_t R, int64_t C, int col, int n, 
                                (const uint4 *)x, (uint32_t)nseg, (uint32_t)C, (uint4 *)y, c_n, slo,
                                shi, nt);
     } else {
-        const dim3 grid((uint32_t)(((C + 63) / 64) * ((R + 511) / 512)));
+        const dim3 grid((uint32_t)(((C + kQcCols - 1) / kQcCols) * ((R + kQcRows - 1) / kQcRows)));
         if (n == 16)
-            hipLaunchKernelGGL(k_hadamard_col<16>, grid, dim3(kThreads), 0, st, (const uint4 *)x,
-                               (uint32_t)R, (uint32_t)C, (uint4 *)y, c_n, slo, shi, nt);
+            hipLaunchKernelGGL(k_hadamard_col<16>, grid, dim3(kQcThreads), 0, st,
+                               (const uint4 *)x, (uint32_t)R, (uint32_t)C, (uint4 *)y, slo, shi, nt);
         else
-            hipLaunchKernelGGL(k_hadamard_col<128>, grid, dim3(kThreads), 0, st, (const uint4 *)x,
-                               (uint32_t)R, (uint32_t)C, (uint4 *)y, c_n, slo, shi, nt);
+            hipLaunchKernelGGL(k_hadamard_col<128>, grid, dim3(kQcThreads), 0, st,
+                               (const uint4 *)x, (uint32_t)R, (uint32_t)C, (uint4 *)y, slo, shi, nt);
     }
     return hipGetLastError();
 }

@@ -42,7 +42,6 @@ constexpr uint32_t kRowGridCap = 1u << 20;
 
 typedef uint32_t u32v4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32v2 __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(3))) void lds_void;
 
 template <bool NT>
 __device__ __forceinline__ void st_stream(uint4 *p, const uint4 &v)
@@ -320,15 +319,7 @@ __device__ __forceinline__ void scatter_pairs(uint4 (&v)[16], int k, const uint3
 //    8-byte outer pairs, instead of the 64-byte half lines one 128-row half
 //    would give.  The fake-quantized BF16 values replace the inputs in LDS
 //    and leave as full row pieces.
-constexpr uint32_t kQcCols = 64, kQcRows = 256, kQcThreads = 512;
-constexpr uint32_t kQcBlockBytes = 8 * kQcCols * 2;      // 8 rows of 128 bytes
-constexpr uint32_t kQcSegs = kQcRows / 16;               // 16-row segments per column
-
-__device__ __forceinline__ uint32_t qc_offset(uint32_t row, uint32_t chunk)
-{
-    const uint32_t b = row >> 3;
-    return b * kQcBlockBytes + (row & 7) * (kQcCols * 2) + ((chunk ^ (b >> 1)) & 7) * 16;
-}
+// (tile constants and qc_offset: fq_device.hpp)
 
 template <int FMT, int RND, bool NT, int RHT = 0>
 __global__ __launch_bounds__(kQcThreads) void k_quant_col(
