@@ -653,7 +653,7 @@ __global__ __launch_bounds__(kThreads) void k_ste_mask(const uint8_t *__restrict
 {
     for (uint32_t c = blockIdx.x * kThreads + threadIdx.x; c < nchunks;
          c += gridDim.x * kThreads) {
-        const uint4 d = dy[c];
+        const uint4 d = ld_stream<true>(&dy[c]);
         const uint32_t k = keep[c];
         st_stream<true>(&dx[c], make_uint4(ste_word(d.x, k, 0), ste_word(d.y, k, 2),
                                            ste_word(d.z, k, 4), ste_word(d.w, k, 6)));
