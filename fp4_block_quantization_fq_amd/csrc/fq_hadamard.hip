@@ -19,9 +19,9 @@
 // Row axis: a lane owns 16 consecutive elements of a row (two 16-byte loads);
 // the first four butterfly stages stay in the lane, and for n = 128 the last
 // three pair lanes 1, 2 and 4 apart (a 128-element block is 8 consecutive
-// lanes).  Column axis: a lane owns 8 columns of 16 consecutive rows (sixteen
-// 16-byte row loads, the quantizer's column tile); the stages run down each
-// column, crossing lanes 1, 2 and 4 apart for n = 128.
+// lanes).  Column axis: the column quantizer's 64-column x 256-row LDS tile;
+// a lane rotates one 16-row segment of one column (the fused quantizers'
+// rht_segment), crossing lanes 1, 2 and 4 apart for n = 128.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 

@@ -10,7 +10,7 @@
 //    segment base+i, so an MXFP4 block is a lane pair and a 128-element outer
 //    block is 8 lanes; block maxima are combined with DPP, without LDS.
 //  * Column axis (groups of consecutive rows of one column, i.e. the rows of
-//    x^T).  The quantizer stages a 64-column x 128-row tile in LDS and then
+//    x^T).  The quantizer stages a 64-column x 256-row tile in LDS and then
 //    gives each lane one 16-row segment of one column, the row-axis work
 //    unit; see k_quant_col.  The dequantizer and the STE, which need no
 //    cross-lane work, let a lane own an 8-column x 16-row tile loaded as 16
@@ -26,11 +26,13 @@ using namespace fqdev;
 namespace {
 
 // Row-axis streams, chosen by measurement on MI355X (16384 x 4096 BF16):
-//  - round-to-nearest kernels, the STE and dequantize map one 8-element chunk
-//    to a lane (every load and store instruction is one contiguous 1 KB run);
-//  - stochastic-rounding kernels, which are bound by Philox and encoder ALU
-//    work, map a 16-element segment to a lane, halving the per-lane block
-//    scale work;
+//  - round-to-nearest kernels and the STE map one 8-element chunk to a lane
+//    (every load and store instruction is one contiguous 1 KB run), the
+//    dequantizer two chunks 64 apart (more bytes in flight for its small
+//    code and scale reads);
+//  - stochastic-rounding kernels, which carry more ALU work per element
+//    (Philox and the SR encoder), map a 16-element segment to a lane,
+//    halving the per-lane block scale work;
 //  - one unit per thread and a grid as large as the tensor (capped), so that
 //    every CU has many waves in flight;
 //  - streamed outputs use non-temporal stores (they are not re-read by the
