@@ -40,6 +40,29 @@ uint32_t grid_for(uint64_t units)
     return (uint32_t)(g ? g : 1);
 }
 
+// Streaming accesses: every array of the tracker is read once and written
+// once per call and not touched again until the next training step.
+typedef float f32v4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32v2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float4 ld_nt(const float4 *p)
+{
+    const f32v4 v = __builtin_nontemporal_load(reinterpret_cast<const f32v4 *>(p));
+    return make_float4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint2 ld_nt(const uint2 *p)
+{
+    const u32v2 v = __builtin_nontemporal_load(reinterpret_cast<const u32v2 *>(p));
+    return make_uint2(v.x, v.y);
+}
+__device__ __forceinline__ void st_nt(float4 *p, const float4 &v)
+{
+    __builtin_nontemporal_store((f32v4){v.x, v.y, v.z, v.w}, reinterpret_cast<f32v4 *>(p));
+}
+__device__ __forceinline__ void st_nt(uint2 *p, const uint2 &v)
+{
+    __builtin_nontemporal_store((u32v2){v.x, v.y}, reinterpret_cast<u32v2 *>(p));
+}
+
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return as_f(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return as_f(w & 0xFFFF0000u); }
 
@@ -60,15 +83,15 @@ __global__ __launch_bounds__(kThreads) void k_osci_track(const float4 *__restric
     // 64-bit index: n4 reaches 2^32 at the largest accepted size
     for (uint64_t i = (uint64_t)blockIdx.x * kThreads + threadIdx.x; i < n4;
          i += (uint64_t)gridDim.x * kThreads) {
-        const float4 wv = w[i];
-        const uint2 qv = q[i];
+        const float4 wv = ld_nt(&w[i]);
+        const uint2 qv = ld_nt(&q[i]);
         if (first) {
-            dm[i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-            dq[i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            st_nt(&dm[i], make_float4(0.0f, 0.0f, 0.0f, 0.0f));
+            st_nt(&dq[i], make_float4(0.0f, 0.0f, 0.0f, 0.0f));
         } else {
-            const float4 wp = w_prev[i];
-            const uint2 qp = q_prev[i];
-            float4 m = dm[i], d = dq[i];
+            const float4 wp = ld_nt(&w_prev[i]);
+            const uint2 qp = ld_nt(&q_prev[i]);
+            float4 m = ld_nt(&dm[i]), d = ld_nt(&dq[i]);
             m.x = m.x + __builtin_fabsf(wv.x - wp.x);
             m.y = m.y + __builtin_fabsf(wv.y - wp.y);
             m.z = m.z + __builtin_fabsf(wv.z - wp.z);
@@ -77,11 +100,11 @@ __global__ __launch_bounds__(kThreads) void k_osci_track(const float4 *__restric
             d.y = d.y + __builtin_fabsf(bf16_hi(qv.x) - bf16_hi(qp.x));
             d.z = d.z + __builtin_fabsf(bf16_lo(qv.y) - bf16_lo(qp.y));
             d.w = d.w + __builtin_fabsf(bf16_hi(qv.y) - bf16_hi(qp.y));
-            dm[i] = m;
-            dq[i] = d;
+            st_nt(&dm[i], m);
+            st_nt(&dq[i], d);
         }
-        w_prev[i] = wv;
-        q_prev[i] = qv;
+        st_nt(&w_prev[i], wv);
+        st_nt(&q_prev[i], qv);
     }
 }
 
@@ -104,18 +127,18 @@ __global__ __launch_bounds__(kThreads) void k_osci_reset(float4 *__restrict__ w,
     // 64-bit index: n4 reaches 2^32 at the largest accepted size
     for (uint64_t i = (uint64_t)blockIdx.x * kThreads + threadIdx.x; i < n4;
          i += (uint64_t)gridDim.x * kThreads) {
-        float4 wv = w[i];
-        const uint2 qv = q[i];
-        const float4 m = dm[i], d = dq[i];
+        float4 wv = ld_nt(&w[i]);
+        const uint2 qv = ld_nt(&q[i]);
+        const float4 m = ld_nt(&dm[i]), d = ld_nt(&dq[i]);
         wv.x = osci_one(wv.x, bf16_lo(qv.x), m.x, d.x, tau);
         wv.y = osci_one(wv.y, bf16_hi(qv.x), m.y, d.y, tau);
         wv.z = osci_one(wv.z, bf16_lo(qv.y), m.z, d.z, tau);
         wv.w = osci_one(wv.w, bf16_hi(qv.y), m.w, d.w, tau);
-        w[i] = wv;
-        w_prev[i] = wv;
-        q_prev[i] = qv;
-        dm[i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-        dq[i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        st_nt(&w[i], wv);
+        st_nt(&w_prev[i], wv);
+        st_nt(&q_prev[i], qv);
+        st_nt(&dm[i], make_float4(0.0f, 0.0f, 0.0f, 0.0f));
+        st_nt(&dq[i], make_float4(0.0f, 0.0f, 0.0f, 0.0f));
     }
 }
 
