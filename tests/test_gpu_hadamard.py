@@ -16,7 +16,8 @@ pytestmark = pytest.mark.gpu
 
 @pytest.mark.parametrize("n", [16, 128])
 @pytest.mark.parametrize("axis", ["row", "col"])
-@pytest.mark.parametrize("shape", [(256, 256), (384, 1024), (640, 136)])
+@pytest.mark.parametrize("shape", [(256, 256), (384, 1024), (640, 136), (16, 8), (48, 72),
+                                   (128, 8), (272, 200)])
 def test_hadamard_bit_exact(n, axis, shape):
     R, C = shape
     q = C if axis == "row" else R
