@@ -12,6 +12,7 @@ torch.uint8; outer scales as torch.float32.  Layouts are those of fq.h.
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 from dataclasses import dataclass
 
@@ -163,8 +164,40 @@ def _torch():
     return torch
 
 
-def _ptr(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+def _ptr(t, nbytes: int | None = None, name: str = "buffer", elem: int | None = None):
+    """Device pointer of a tensor the library will read or write.  The C
+    library sees only pointers and sizes, so the binding checks here what it
+    cannot: the tensor is on the GPU, contiguous, of the expected element
+    size, and holds at least `nbytes` bytes (a smaller buffer would be written
+    past its end)."""
+    if t is None:
+        return None
+    if not getattr(t, "is_cuda", False):
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous (row-major)")
+    if elem is not None and t.element_size() != elem:
+        raise ValueError(f"{name} has {t.element_size()}-byte elements, expected {elem}")
+    if nbytes is not None and t.numel() * t.element_size() < nbytes:
+        raise ValueError(f"{name} holds {t.numel() * t.element_size()} bytes, "
+                         f"{nbytes} are needed")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _bf16(t, rows: int, cols: int, name: str):
+    """A BF16 [rows, cols] operand (2-byte elements)."""
+    return _ptr(t, rows * cols * 2, name, elem=2)
+
+
+def _qptrs(desc, out, rows: int, cols: int):
+    """Pointers of the codes, scales and outer outputs, checked against the
+    sizes the descriptor implies (each may be None)."""
+    if out is None:
+        return None, None, None
+    s = output_shapes(desc, rows, cols)
+    n = lambda shp: 0 if shp is None else math.prod(shp)
+    return (_ptr(out.codes, n(s["codes"]), "codes"), _ptr(out.scales, n(s["scales"]), "scales"),
+            _ptr(out.outer, 4 * n(s["outer"]), "outer"))
 
 
 def _stream(stream=None):
@@ -222,9 +255,9 @@ def fq_quantize(desc: FqDesc, x, out: Quantized | None = None, ws=None, stream=N
         ws, nbytes = workspace(desc, rows, cols, x.device)
     else:
         nbytes = ws.numel() * ws.element_size()
-    _check(lib().fq_quantize(ctypes.byref(desc), _ptr(x), rows, cols, _ptr(out.codes),
-                             _ptr(out.scales), _ptr(out.outer), _ptr(ws), nbytes,
-                             _stream(stream)))
+    codes, scales, outer = _qptrs(desc, out, rows, cols)
+    _check(lib().fq_quantize(ctypes.byref(desc), _bf16(x, rows, cols, "x"), rows, cols, codes,
+                             scales, outer, _ptr(ws, nbytes, "ws"), nbytes, _stream(stream)))
     return out
 
 
@@ -232,8 +265,9 @@ def fq_dequantize(desc: FqDesc, q: Quantized, rows: int, cols: int, y=None, stre
     torch = _torch()
     if y is None:
         y = torch.empty((rows, cols), dtype=torch.bfloat16, device=q.codes.device)
-    _check(lib().fq_dequantize(ctypes.byref(desc), _ptr(q.codes), _ptr(q.scales),
-                               _ptr(q.outer), rows, cols, _ptr(y), _stream(stream)))
+    codes, scales, outer = _qptrs(desc, q, rows, cols)
+    _check(lib().fq_dequantize(ctypes.byref(desc), codes, scales, outer, rows, cols,
+                               _bf16(y, rows, cols, "y"), _stream(stream)))
     return y
 
 
@@ -249,11 +283,10 @@ def fq_fake_quant(desc: FqDesc, x, y=None, out: Quantized | None = None, ws=None
         ws, nbytes = workspace(desc, rows, cols, x.device)
     else:
         nbytes = ws.numel() * ws.element_size()
-    codes = scales = outer = None
-    if out is not None:
-        codes, scales, outer = out.codes, out.scales, out.outer
-    _check(lib().fq_fake_quant(ctypes.byref(desc), _ptr(x), rows, cols, _ptr(y), _ptr(codes),
-                               _ptr(scales), _ptr(outer), _ptr(ws), nbytes, _stream(stream)))
+    codes, scales, outer = _qptrs(desc, out, rows, cols)
+    _check(lib().fq_fake_quant(ctypes.byref(desc), _bf16(x, rows, cols, "x"), rows, cols,
+                               _bf16(y, rows, cols, "y"), codes, scales, outer,
+                               _ptr(ws, nbytes, "ws"), nbytes, _stream(stream)))
     return y
 
 
@@ -272,12 +305,11 @@ def fq_fake_quant_mask(desc: FqDesc, x, y=None, out: Quantized | None = None, ke
         ws, nbytes = workspace(desc, rows, cols, x.device)
     else:
         nbytes = ws.numel() * ws.element_size()
-    codes = scales = outer = None
-    if out is not None:
-        codes, scales, outer = out.codes, out.scales, out.outer
-    _check(lib().fq_fake_quant_mask(ctypes.byref(desc), _ptr(x), rows, cols, _ptr(y),
-                                    _ptr(codes), _ptr(scales), _ptr(outer), _ptr(keep),
-                                    _ptr(ws), nbytes, _stream(stream)))
+    codes, scales, outer = _qptrs(desc, out, rows, cols)
+    _check(lib().fq_fake_quant_mask(ctypes.byref(desc), _bf16(x, rows, cols, "x"), rows, cols,
+                                    _bf16(y, rows, cols, "y"), codes, scales, outer,
+                                    _ptr(keep, rows * cols // 8, "keep"),
+                                    _ptr(ws, nbytes, "ws"), nbytes, _stream(stream)))
     return y, keep
 
 
@@ -287,8 +319,9 @@ def fq_ste_backward_mask(keep, dy, dx=None, stream=None):
     rows, cols = dy.shape
     if dx is None:
         dx = torch.empty_like(dy)
-    _check(lib().fq_ste_backward_mask(_ptr(keep), _ptr(dy), rows, cols, _ptr(dx),
-                                      _stream(stream)))
+    _check(lib().fq_ste_backward_mask(_ptr(keep, rows * cols // 8, "keep"),
+                                      _bf16(dy, rows, cols, "dy"), rows, cols,
+                                      _bf16(dx, rows, cols, "dx"), _stream(stream)))
     return dx
 
 
@@ -301,19 +334,24 @@ def osci_state(n: int, device):
             "dist_q": torch.zeros(n, dtype=torch.float32, device=device)}
 
 
+def _osci_ptrs(w, q, st: dict, n: int):
+    return (_ptr(w, 4 * n, "w", elem=4), _ptr(q, 2 * n, "q", elem=2),
+            _ptr(st["w_prev"], 4 * n, "w_prev", elem=4), _ptr(st["q_prev"], 2 * n, "q_prev", elem=2),
+            _ptr(st["dist_m"], 4 * n, "dist_m", elem=4), _ptr(st["dist_q"], 4 * n, "dist_q", elem=4))
+
+
 def fq_osci_track(w, q, st: dict, first: bool = False, stream=None):
     """One step of the oscillation tracker (w FP32 master, q BF16 quantized)."""
-    _check(lib().fq_osci_track(_ptr(w), _ptr(q), _ptr(st["w_prev"]), _ptr(st["q_prev"]),
-                               _ptr(st["dist_m"]), _ptr(st["dist_q"]), w.numel(),
-                               1 if first else 0, _stream(stream)))
+    n = w.numel()
+    _check(lib().fq_osci_track(*_osci_ptrs(w, q, st, n), n, 1 if first else 0, _stream(stream)))
 
 
 def fq_osci_reset(w, q, st: dict, tau: float, stream=None):
     """The OsciReset check: oscillating master weights (in place in w) take
     their quantized value; every element starts a new window."""
-    _check(lib().fq_osci_reset(_ptr(w), _ptr(q), _ptr(st["w_prev"]), _ptr(st["q_prev"]),
-                               _ptr(st["dist_m"]), _ptr(st["dist_q"]), w.numel(),
-                               ctypes.c_float(tau), _stream(stream)))
+    n = w.numel()
+    _check(lib().fq_osci_reset(*_osci_ptrs(w, q, st, n), n, ctypes.c_float(tau),
+                               _stream(stream)))
 
 
 def fq_channel_absmax(x, amax=None, stream=None):
@@ -323,7 +361,8 @@ def fq_channel_absmax(x, amax=None, stream=None):
     rows, cols = x.shape
     if amax is None:
         amax = torch.zeros(cols, dtype=torch.int32, device=x.device)
-    _check(lib().fq_channel_absmax(_ptr(x), rows, cols, _ptr(amax), _stream(stream)))
+    _check(lib().fq_channel_absmax(_bf16(x, rows, cols, "x"), rows, cols,
+                                   _ptr(amax, 4 * cols, "amax", elem=4), _stream(stream)))
     return amax
 
 
@@ -334,8 +373,8 @@ def fq_select_channels(amax, k: int, stream=None):
     cols = amax.numel()
     retain = torch.empty(cols // 8, dtype=torch.uint8, device=amax.device)
     scale = torch.empty(cols, dtype=torch.float32, device=amax.device)
-    _check(lib().fq_select_channels(_ptr(amax), cols, k, _ptr(retain), _ptr(scale),
-                                    _stream(stream)))
+    _check(lib().fq_select_channels(_ptr(amax, 4 * cols, "amax", elem=4), cols, k,
+                                    _ptr(retain), _ptr(scale), _stream(stream)))
     return retain, scale
 
 
@@ -346,12 +385,12 @@ def fq_fake_quant_retain(desc: FqDesc, x, retain, chan_scale, y=None,
     rows, cols = x.shape
     if y is None:
         y = torch.empty_like(x)
-    codes = scales = outer = None
-    if out is not None:
-        codes, scales, outer = out.codes, out.scales, out.outer
-    _check(lib().fq_fake_quant_retain(ctypes.byref(desc), _ptr(x), rows, cols, _ptr(y),
-                                      _ptr(codes), _ptr(scales), _ptr(outer), _ptr(retain),
-                                      _ptr(chan_scale), _stream(stream)))
+    codes, scales, outer = _qptrs(desc, out, rows, cols)
+    _check(lib().fq_fake_quant_retain(ctypes.byref(desc), _bf16(x, rows, cols, "x"), rows, cols,
+                                      _bf16(y, rows, cols, "y"), codes, scales, outer,
+                                      _ptr(retain, cols // 8, "retain"),
+                                      _ptr(chan_scale, 4 * cols, "chan_scale", elem=4),
+                                      _stream(stream)))
     return y
 
 
@@ -363,12 +402,10 @@ def fq_fake_quant_rht(desc: FqDesc, x, rht_block: int, rht_seed: int, y=None,
     rows, cols = x.shape
     if y is None:
         y = torch.empty_like(x)
-    codes = scales = outer = None
-    if out is not None:
-        codes, scales, outer = out.codes, out.scales, out.outer
-    _check(lib().fq_fake_quant_rht(ctypes.byref(desc), _ptr(x), rows, cols, rht_block, rht_seed,
-                                   _ptr(y), _ptr(codes), _ptr(scales), _ptr(outer),
-                                   _stream(stream)))
+    codes, scales, outer = _qptrs(desc, out, rows, cols)
+    _check(lib().fq_fake_quant_rht(ctypes.byref(desc), _bf16(x, rows, cols, "x"), rows, cols,
+                                   rht_block, rht_seed, _bf16(y, rows, cols, "y"), codes, scales,
+                                   outer, _stream(stream)))
     return y
 
 
@@ -377,8 +414,10 @@ def fq_ste_backward(desc: FqDesc, x, q: Quantized, dy, dx=None, stream=None):
     rows, cols = x.shape
     if dx is None:
         dx = torch.empty_like(dy)
-    _check(lib().fq_ste_backward(ctypes.byref(desc), _ptr(x), _ptr(q.scales), _ptr(q.outer),
-                                 _ptr(dy), rows, cols, _ptr(dx), _stream(stream)))
+    _, scales, outer = _qptrs(desc, Quantized(None, q.scales, q.outer), rows, cols)
+    _check(lib().fq_ste_backward(ctypes.byref(desc), _bf16(x, rows, cols, "x"), scales, outer,
+                                 _bf16(dy, rows, cols, "dy"), rows, cols,
+                                 _bf16(dx, rows, cols, "dx"), _stream(stream)))
     return dx
 
 
@@ -419,8 +458,9 @@ def fq_qlinear_fwd(desc_x: FqDesc, desc_w: FqDesc, x, w, y=None, ws=None, stream
         y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
     if ws is None:
         ws = qlinear_workspace(desc_x, desc_w, M, K, N, x.device)
-    _check(lib().fq_qlinear_fwd(ctypes.byref(desc_x), ctypes.byref(desc_w), _ptr(x), _ptr(w),
-                                M, K, N, _ptr(y), _ptr(ws), ws.numel(), _stream(stream)))
+    _check(lib().fq_qlinear_fwd(ctypes.byref(desc_x), ctypes.byref(desc_w), _bf16(x, M, K, "x"),
+                                _bf16(w, K, N, "w"), M, K, N, _bf16(y, M, N, "y"),
+                                _ptr(ws, None, "ws", elem=1), ws.numel(), _stream(stream)))
     return y
 
 
@@ -430,7 +470,8 @@ def fq_hadamard(x, block: int, axis: int = FQ_AXIS_ROW, seed: int = 0, y=None, s
     rows, cols = x.shape
     if y is None:
         y = torch.empty_like(x)
-    _check(lib().fq_hadamard(_ptr(x), rows, cols, axis, block, seed, _ptr(y), _stream(stream)))
+    _check(lib().fq_hadamard(_bf16(x, rows, cols, "x"), rows, cols, axis, block, seed,
+                             _bf16(y, rows, cols, "y"), _stream(stream)))
     return y
 
 
@@ -458,8 +499,10 @@ def fq_qlinear_bwd(desc_x: FqDesc, desc_w: FqDesc, desc_g: FqDesc, x, w, dy, dx=
     if ws is None:
         ws = qlinear_bwd_workspace(desc_x, desc_w, desc_g, M, K, N, x.device, rht_block)
     _check(lib().fq_qlinear_bwd(ctypes.byref(desc_x), ctypes.byref(desc_w), ctypes.byref(desc_g),
-                                rht_block, rht_seed, _ptr(x), _ptr(w), _ptr(dy), M, K, N,
-                                _ptr(dx), _ptr(dw), _ptr(ws), ws.numel(), _stream(stream)))
+                                rht_block, rht_seed, _bf16(x, M, K, "x"), _bf16(w, K, N, "w"),
+                                _bf16(dy, M, N, "dy"), M, K, N, _bf16(dx, M, K, "dx"),
+                                _bf16(dw, K, N, "dw"), _ptr(ws, None, "ws", elem=1), ws.numel(),
+                                _stream(stream)))
     return dx, dw
 
 

@@ -266,3 +266,12 @@ def test_status_strings(L):
     for s in range(7):
         assert L.fq_status_string(s).decode().startswith("FQ_")
     assert L.fq_version().decode().count(".") == 2
+
+
+def test_binding_rejects_host_tensors():
+    # the binding checks what the C library cannot see (device, layout, size)
+    # before anything reaches a kernel
+    import torch
+    x = torch.zeros((4, 32), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        fq.fq_hadamard(x, 16)

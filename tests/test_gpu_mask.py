@@ -88,3 +88,21 @@ def test_mask_ste_equals_recomputing_ste():
     b = fq.fq_ste_backward_mask(keep, tdy)
     torch.cuda.synchronize()
     assert np.array_equal(to_bits(a), to_bits(b))
+
+
+def test_binding_checks_buffers():
+    DEV = "cuda:0"
+    # a buffer too small, a non-contiguous operand or the wrong element size
+    # is refused before any launch
+    x = torch.zeros((64, 256), dtype=torch.bfloat16, device=DEV)
+    d = fq.fq_desc_nvfp4(outer=fq.FQ_OUTER_BLOCK128)
+    with pytest.raises(ValueError, match="bytes"):
+        fq.fq_fake_quant(d, x, y=torch.empty((32, 256), dtype=torch.bfloat16, device=DEV))
+    with pytest.raises(ValueError, match="contiguous"):
+        fq.fq_fake_quant(d, torch.zeros((256, 64), dtype=torch.bfloat16, device=DEV).t())
+    with pytest.raises(ValueError, match="element"):
+        fq.fq_fake_quant(d, x.float())
+    out = fq.alloc_outputs(d, 64, 256, DEV)
+    out.codes = out.codes[:32]
+    with pytest.raises(ValueError, match="codes"):
+        fq.fq_fake_quant(d, x, out=out)
