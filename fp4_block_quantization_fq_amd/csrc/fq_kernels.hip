@@ -354,6 +354,10 @@ __global__ __launch_bounds__(kQcThreads) void k_quant_col(
     const uint32_t tc0 = (blockIdx.x % tiles_c) * kQcCols;
     const uint32_t tr0 = (blockIdx.x / tiles_c) * kQcRows;
     const uint32_t ldx = C >> 3;                     // 16-byte chunks per row
+    // Waves issuing loads or stores run at a raised priority, so that on a CU
+    // shared by several tiles the memory phases go ahead of the arithmetic
+    // (about 1 us on 16384x4096)
+    __builtin_amdgcn_s_setprio(1);
 
     // Direct loads: wave w fills blocks 4w .. 4w+3; lane l brings row l >> 3
     // of the block into slot l & 7, i.e. global chunk (l & 7) ^ (b >> 1).
@@ -370,6 +374,7 @@ __global__ __launch_bounds__(kQcThreads) void k_quant_col(
     if (keep) s_clip[threadIdx.x] = 0u;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    __builtin_amdgcn_s_setprio(0);
 
     const uint32_t rb = lane & 7, half = wave >> 2;
     const uint32_t seg = half * 8 + rb;              // this lane's segment of each column
@@ -435,6 +440,7 @@ __global__ __launch_bounds__(kQcThreads) void k_quant_col(
         }
     }
     __syncthreads();
+    __builtin_amdgcn_s_setprio(1);
     const uint32_t t = threadIdx.x;
     if (codes) {
         // 16 threads per column, 8 bytes (one segment) each: a wave stores four
