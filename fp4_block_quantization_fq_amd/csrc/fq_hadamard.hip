@@ -89,6 +89,7 @@ __global__ __launch_bounds__(kQcThreads) void k_hadamard_col(const uint4 *__rest
     const uint32_t tc0 = (blockIdx.x % tiles_c) * kQcCols;
     const uint32_t tr0 = (blockIdx.x / tiles_c) * kQcRows;
     const uint32_t ldx = C >> 3;
+    __builtin_amdgcn_s_setprio(1);      // memory phases ahead of the arithmetic
     // wave w fills blocks 4w .. 4w+3; rows and chunks outside the tensor
     // re-read its last row / chunk (the segments they would feed are unused)
 #pragma unroll
@@ -101,6 +102,7 @@ __global__ __launch_bounds__(kQcThreads) void k_hadamard_col(const uint4 *__rest
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    __builtin_amdgcn_s_setprio(0);
 
     const uint32_t rl0 = ((wave >> 2) * 8 + (lane & 7)) * 16;   // the lane's first tile row
     const uint32_t row0 = tr0 + rl0;
@@ -131,6 +133,7 @@ __global__ __launch_bounds__(kQcThreads) void k_hadamard_col(const uint4 *__rest
         }
     }
     __syncthreads();
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (uint32_t i = 0; i < kQcRows * 8 / kQcThreads; ++i) {
         const uint32_t q = i * kQcThreads + threadIdx.x;
