@@ -616,39 +616,94 @@ __global__ __launch_bounds__(kThreads) void k_ste_row(
     }
 }
 
+// Column-axis STE on the column quantizer's tile and lane mapping: the x tile
+// (64 columns x 256 rows) arrives in LDS by direct loads while every thread
+// loads its four 16-byte row pieces of dy into registers; each lane then
+// recomputes the clip test of one 16-row segment of one column from x and
+// the stored block scale and marks the clipped elements (rare) in an LDS bit
+// mask, and every thread stores its dy pieces as dx with those elements +0.
 template <int FMT>
-__global__ __launch_bounds__(kThreads) void k_ste_col(
+__global__ __launch_bounds__(kQcThreads) void k_ste_col(
     const uint4 *__restrict__ x, const uint8_t *__restrict__ scales,
     const float *__restrict__ outer, const uint4 *__restrict__ dy, uint32_t R, uint32_t C,
     uint4 *__restrict__ dx)
 {
     constexpr uint32_t B = (FMT == FMT_MX) ? 32 : 16;
-    const ColTile t = col_tile(R, C);
-    if (!t.valid) return;
+    constexpr uint32_t PIECES = kQcRows * 8 / kQcThreads;   // row pieces per thread
+    __shared__ __attribute__((aligned(1024))) uint8_t s_x[kQcRows / 8 * kQcBlockBytes];
+    // clip bits: row r, columns 32h .. 32h + 31 in word 2r + h
+    __shared__ uint32_t s_clip[kQcRows * (kQcCols / 32)];
+    static_assert(kQcRows * (kQcCols / 32) == kQcThreads, "one clip word per thread");
+    const uint32_t lane = threadIdx.x & 63, wave = threadIdx.x >> 6, t = threadIdx.x;
+    const uint32_t tiles_c = (C + kQcCols - 1) / kQcCols;
+    const uint32_t tc0 = (blockIdx.x % tiles_c) * kQcCols;
+    const uint32_t tr0 = (blockIdx.x / tiles_c) * kQcRows;
     const uint32_t ldx = C >> 3;
-    BlockScale bs[8];
+    __builtin_amdgcn_s_setprio(1);      // memory phases ahead of the arithmetic
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-        const uint32_t col = t.col0 + c;
+    for (uint32_t i = 0; i < 4; ++i) {
+        const uint32_t blk = wave * 4 + i;
+        const uint32_t row = min(tr0 + blk * 8 + (lane >> 3), R - 1);
+        const uint32_t chunk = min((tc0 >> 3) + (((lane & 7) ^ (blk >> 1)) & 7), ldx - 1);
+        __builtin_amdgcn_global_load_lds((const void *)(x + (size_t)row * ldx + chunk),
+                                         (lds_void *)(s_x + blk * kQcBlockBytes), 16, 0, 0);
+    }
+    // this thread's dy pieces: tile row q >> 3, chunk q & 7 for q = i * 512 + t
+    uint4 d[PIECES];
+#pragma unroll
+    for (uint32_t i = 0; i < PIECES; ++i) {
+        const uint32_t q = i * kQcThreads + t;
+        const uint32_t r = min(tr0 + (q >> 3), R - 1);
+        const uint32_t chunk = min((tc0 >> 3) + (q & 7), ldx - 1);
+        d[i] = ld_stream<true>(&dy[(size_t)r * ldx + chunk]);
+    }
+    s_clip[t] = 0u;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    __builtin_amdgcn_s_setprio(0);
+
+    const uint32_t rl0 = ((wave >> 2) * 8 + (lane & 7)) * 16;   // the lane's first tile row
+    const uint32_t row0 = tr0 + rl0;
+#pragma unroll 1
+    for (uint32_t u = 0; u < 2; ++u) {
+        const uint32_t lc = (lane >> 3) + 8 * (wave & 3) + 32 * u;
+        const uint32_t col = tc0 + lc;
+        if (col >= C || row0 >= R) continue;
+        const uint32_t byte_in_chunk = (lc & 7) * 2;
+        uint32_t xp[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t r = rl0 + 2 * i;
+            const uint32_t lo = *reinterpret_cast<const uint16_t *>(
+                s_x + qc_offset(r, lc >> 3) + byte_in_chunk);
+            const uint32_t hi = *reinterpret_cast<const uint16_t *>(
+                s_x + qc_offset(r + 1, lc >> 3) + byte_in_chunk);
+            xp[i] = lo | (hi << 16);
+        }
         float s = 0.0f;
         if (FMT == FMT_NVT) s = outer[0];
-        if (FMT == FMT_NV128) s = outer[(size_t)col * (R >> 7) + (t.row0 >> 7)];
-        bs[c] = scale_from_code<FMT>(scales[(size_t)col * (R / B) + t.row0 / B], s);
-    }
-#pragma unroll 4
-    for (int r = 0; r < 16; ++r) {
-        const size_t idx = (size_t)(t.row0 + r) * ldx + (t.col0 >> 3);
-        const uint4 v = x[idx];
-        const uint4 d = dy[idx];
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-        uint32_t keep = 0;
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            const uint32_t xb = (c & 1) ? hi_bits(w[c >> 1]) : lo_bits(w[c >> 1]);
-            keep |= (scaled_mag<FMT>(xb, bs[c]) <= 6.0f ? 1u : 0u) << c;
+        if (FMT == FMT_NV128) s = outer[(size_t)col * (R >> 7) + (row0 >> 7)];
+        const BlockScale b = scale_from_code<FMT>(scales[(size_t)col * (R / B) + row0 / B], s);
+        // element i of the segment is row rl0 + i of the tile
+        for (uint32_t clip = ~keep_mask<FMT, 8>(xp, b) & 0xFFFFu; clip; clip &= clip - 1) {
+            const uint32_t i = __builtin_ctz(clip);
+            atomicOr(&s_clip[(rl0 + i) * (kQcCols / 32) + (lc >> 5)], 1u << (lc & 31));
         }
-        st_stream<true>(&dx[idx], make_uint4(ste_word(d.x, keep, 0), ste_word(d.y, keep, 2),
-                                             ste_word(d.z, keep, 4), ste_word(d.w, keep, 6)));
+    }
+    __syncthreads();
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (uint32_t i = 0; i < PIECES; ++i) {
+        const uint32_t q = i * kQcThreads + t;
+        const uint32_t r = q >> 3, chunk = q & 7;
+        if (tr0 + r < R && tc0 + chunk * 8 < C) {
+            // the chunk's 8 columns are bits 8 (chunk & 3) .. + 7 of word 2r + chunk / 4
+            const uint32_t keep =
+                ~(s_clip[r * (kQcCols / 32) + (chunk >> 2)] >> (8 * (chunk & 3))) & 0xFFu;
+            st_stream<true>(&dx[(size_t)(tr0 + r) * ldx + (tc0 >> 3) + chunk],
+                            make_uint4(ste_word(d[i].x, keep, 0), ste_word(d[i].y, keep, 2),
+                                       ste_word(d[i].z, keep, 4), ste_word(d[i].w, keep, 6)));
+        }
     }
 }
 
@@ -815,7 +870,7 @@ static hipError_t ste_dispatch(int col, const void *x, const void *scales, const
                            st, (const uint4 *)x, (const uint8_t *)scales, outer,
                            (const uint4 *)dy, (uint32_t)nchunks, (uint4 *)dx);
     } else {
-        hipLaunchKernelGGL(k_ste_col<FMT>, col_grid(R, C), dim3(kThreads), 0, st,
+        hipLaunchKernelGGL(k_ste_col<FMT>, quant_col_grid(R, C), dim3(kQcThreads), 0, st,
                            (const uint4 *)x, (const uint8_t *)scales, outer, (const uint4 *)dy,
                            (uint32_t)R, (uint32_t)C, (uint4 *)dx);
     }
