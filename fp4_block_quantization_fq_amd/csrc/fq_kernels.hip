@@ -10,12 +10,10 @@
 //    segment base+i, so an MXFP4 block is a lane pair and a 128-element outer
 //    block is 8 lanes; block maxima are combined with DPP, without LDS.
 //  * Column axis (groups of consecutive rows of one column, i.e. the rows of
-//    x^T).  The quantizer stages a 64-column x 256-row tile in LDS and then
-//    gives each lane one 16-row segment of one column, the row-axis work
-//    unit; see k_quant_col.  The dequantizer and the STE, which need no
-//    cross-lane work, let a lane own an 8-column x 16-row tile loaded as 16
-//    row segments of 16 bytes: the 8 lanes of one column group hold
-//    consecutive row blocks, so 64 lanes cover 64 columns x 128 rows.
+//    x^T).  The quantizer, the dequantizer and the STE stage a 64-column x
+//    256-row tile in LDS, so that the BF16 tensor moves as whole 128-byte row
+//    pieces, and give each lane one 16-row segment of a column, the row-axis
+//    work unit; see k_quant_col.
 //
 // Numerics follow fq_device.hpp; the op definitions are those of fq.h.
 #include "fq_device.hpp"
@@ -254,48 +252,8 @@ __global__ __launch_bounds__(kThreads) void k_quant_row(
 }
 
 // ---------------------------------------------------------------------------
-// Column-axis kernels: lane = 8 columns x 16 rows
+// Column-axis kernels on a kQcCols x kQcRows tile staged in LDS
 // ---------------------------------------------------------------------------
-struct ColTile {
-    uint32_t col0;   // first of the lane's 8 columns
-    uint32_t row0;   // first of the lane's 16 rows
-    uint32_t rb;     // lane's row block within its 8-lane group
-    bool valid;
-};
-
-// One workgroup covers 64 columns x 512 rows (4 waves of 128 rows); the 1-D
-// grid runs column tiles fastest.
-__device__ __forceinline__ ColTile col_tile(uint32_t R, uint32_t C)
-{
-    const uint32_t lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const uint32_t tiles_c = (C + 63) >> 6;
-    ColTile t;
-    t.rb = lane & 7;
-    t.col0 = (blockIdx.x % tiles_c) * 64 + (lane >> 3) * 8;
-    t.row0 = (((blockIdx.x / tiles_c) * 4 + wave) * 8 + t.rb) * 16;
-    t.valid = t.col0 < C && t.row0 < R;
-    return t;
-}
-
-__device__ __forceinline__ void seg_set_word(uint4 &v, int k, uint32_t w)
-{
-    if (k == 0) v.x = w;
-    else if (k == 1) v.y = w;
-    else if (k == 2) v.z = w;
-    else v.w = w;
-}
-// Put the column-pair results of columns 2k and 2k+1 (pairs along rows) back
-// into the row segments.
-__device__ __forceinline__ void scatter_pairs(uint4 (&v)[16], int k, const uint32_t (&ya)[8],
-                                              const uint32_t (&yb)[8])
-{
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        seg_set_word(v[2 * i], k, (ya[i] & 0xFFFFu) | (yb[i] << 16));
-        seg_set_word(v[2 * i + 1], k, (ya[i] >> 16) | (yb[i] & 0xFFFF0000u));
-    }
-}
-
 // Column quantizer: the tile goes through LDS, so that every lane works on
 // one 16-row segment of one column at a time, exactly like a row-axis lane on
 // its 16-element segment (same block scale, draws and encoder), with a small
@@ -555,35 +513,59 @@ __global__ __launch_bounds__(kThreads) void k_dequant_row(
     }
 }
 
+// Column-axis dequantizer on the column quantizer's 64-column x 256-row tile:
+// each lane decodes one 16-row segment of two adjacent columns (8 code bytes
+// each; the 16 lanes of a column read its 128-byte line of codes), writes the
+// BF16 pairs into the tile in LDS, and the tile leaves as full 128-byte row
+// pieces instead of the 16-byte column pieces a register transpose would give.
 template <int FMT>
-__global__ __launch_bounds__(kThreads) void k_dequant_col(
+__global__ __launch_bounds__(kQcThreads) void k_dequant_col(
     const uint8_t *__restrict__ codes, const uint8_t *__restrict__ scales,
     const float *__restrict__ outer, uint32_t R, uint32_t C, uint4 *__restrict__ y)
 {
     constexpr uint32_t B = (FMT == FMT_MX) ? 32 : 16;
-    const ColTile t = col_tile(R, C);
-    if (!t.valid) return;
+    __shared__ __attribute__((aligned(1024))) uint8_t s_tile[kQcRows / 8 * kQcBlockBytes];
+    const uint32_t lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const uint32_t tiles_c = (C + kQcCols - 1) / kQcCols;
+    const uint32_t tc0 = (blockIdx.x % tiles_c) * kQcCols;
+    const uint32_t tr0 = (blockIdx.x / tiles_c) * kQcRows;
     const uint32_t ldx = C >> 3;
-    uint4 v[16];
+    const float s_t = (FMT == FMT_NVT) ? outer[0] : 0.0f;
+    const uint32_t rl0 = ((wave >> 2) * 8 + (lane & 7)) * 16;   // the lane's first tile row
+    const uint32_t row0 = tr0 + rl0;
+    const uint32_t lc = 2 * ((lane >> 3) + 8 * (wave & 3));     // the lane's column pair
+    if (tc0 + lc < C && row0 < R) {
+        uint32_t yq[2][8];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        uint32_t yph[2][8];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const uint32_t col = t.col0 + 2 * k + h;
+        for (uint32_t h = 0; h < 2; ++h) {
+            const uint32_t col = tc0 + lc + h;
             const uint2 cw =
-                *reinterpret_cast<const uint2 *>(codes + (size_t)col * (R >> 1) + (t.row0 >> 1));
-            float s = 0.0f;
-            if (FMT == FMT_NVT) s = outer[0];
-            if (FMT == FMT_NV128) s = outer[(size_t)col * (R >> 7) + (t.row0 >> 7)];
-            const float se = stored_s_eff<FMT>(scales[(size_t)col * (R / B) + t.row0 / B], s);
-            decode8<FMT>(cw.x, se, &yph[h][0]);
-            decode8<FMT>(cw.y, se, &yph[h][4]);
+                *reinterpret_cast<const uint2 *>(codes + (size_t)col * (R >> 1) + (row0 >> 1));
+            float s = s_t;
+            if (FMT == FMT_NV128) s = outer[(size_t)col * (R >> 7) + (row0 >> 7)];
+            const float se = stored_s_eff<FMT>(scales[(size_t)col * (R / B) + row0 / B], s);
+            decode8<FMT>(cw.x, se, &yq[h][0]);
+            decode8<FMT>(cw.y, se, &yq[h][4]);
         }
-        scatter_pairs(v, k, yph[0], yph[1]);
-    }
+        const uint32_t byte_in_chunk = (lc & 7) * 2;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) st_stream<true>(&y[(size_t)(t.row0 + r) * ldx + (t.col0 >> 3)], v[r]);
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t r = rl0 + 2 * i;
+            *reinterpret_cast<uint32_t *>(s_tile + qc_offset(r, lc >> 3) + byte_in_chunk) =
+                (yq[0][i] & 0xFFFFu) | (yq[1][i] << 16);
+            *reinterpret_cast<uint32_t *>(s_tile + qc_offset(r + 1, lc >> 3) + byte_in_chunk) =
+                (yq[0][i] >> 16) | (yq[1][i] & 0xFFFF0000u);
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (uint32_t i = 0; i < kQcRows * 8 / kQcThreads; ++i) {
+        const uint32_t q = i * kQcThreads + threadIdx.x;
+        const uint32_t r = q >> 3, chunk = q & 7;
+        if (tr0 + r < R && tc0 + chunk * 8 < C)
+            st_stream<true>(&y[(size_t)(tr0 + r) * ldx + (tc0 >> 3) + chunk],
+                            *reinterpret_cast<const uint4 *>(s_tile + qc_offset(r, chunk)));
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -734,15 +716,8 @@ uint32_t row_grid(uint64_t nseg, uint32_t per_block)
     return (uint32_t)g;
 }
 
-// Column-axis grid: one workgroup per 64-column x 512-row tile.
-dim3 col_grid(int64_t R, int64_t C)
-{
-    uint64_t gx = (uint64_t)((C + 63) / 64);
-    uint64_t gy = (uint64_t)((R + 511) / 512);
-    return dim3((uint32_t)(gx * gy), 1, 1);
-}
-
-// Column-axis quantizer grid: one workgroup per kQcCols x kQcRows tile.
+// Column-axis grid (quantizer, dequantizer, STE): one workgroup per
+// kQcCols x kQcRows tile.
 dim3 quant_col_grid(int64_t R, int64_t C)
 {
     uint64_t gx = (uint64_t)((C + kQcCols - 1) / kQcCols);
@@ -840,7 +815,7 @@ static hipError_t dequant_dispatch(int col, const void *codes, const void *scale
                            0, st, (const uint32_t *)codes, (const uint8_t *)scales, outer,
                            (uint32_t)nchunks, (uint4 *)y);
     } else {
-        hipLaunchKernelGGL(k_dequant_col<FMT>, col_grid(R, C), dim3(kThreads), 0, st,
+        hipLaunchKernelGGL(k_dequant_col<FMT>, quant_col_grid(R, C), dim3(kQcThreads), 0, st,
                            (const uint8_t *)codes, (const uint8_t *)scales, outer, (uint32_t)R,
                            (uint32_t)C, (uint4 *)y);
     }
