@@ -407,6 +407,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mxfp4_nt(Fp4Problem p0, Fp
                 for (int j = 0; j < TN; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
                         af[i], bfr[j], acc[i][j], 4, 4, 0, sca[i], 0, scb[j]);
+            // the single-wave MFMA interleaving strategy, as in k_gemm_nt
+            // (about 2 us off the 8192x2880x5760 product)
+            __builtin_amdgcn_iglp_opt(1);
         }
         // the other scale buffer was last read in the previous stage, before
         // its closing barrier; past the last stage the values go unused
