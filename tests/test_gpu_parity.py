@@ -247,3 +247,27 @@ def test_workload_qlinear_mxfp4():
     # the same shape with both operands MXFP4: codes and scales on the FP4 matrix cores
     err = _qlinear_check(8192, 2880, 5760, "mx", "mx")
     assert err < 4e-3
+
+
+def test_workload_column_ops_at_bench_size():
+    """The transposed-axis ops exactly as the benchmark step runs them: SR fake
+    quant of the 16384x4096 activation along columns (double block, seed 1234;
+    MXFP4, seed 1235), then the column dequantizer and the column STE on the
+    double-block result, every output element against the oracle."""
+    x = wl.nv_activation(16384, 4096, seed=3)
+    dy = wl.grad_output(16384, 4096, seed=4)
+    xd, dyd = to_dev(x), to_dev(dy)
+    for fmt, seed in (("nv_128", 1234), ("mx", 1235)):
+        ref = oracle.fake_quant(x, fmt, "sr", "col", seed)
+        assert_same(gpu_fake_quant(x, fmt, "sr", "col", seed), ref,
+                    tag=f"{fmt} sr col 16384x4096")
+        if fmt != "nv_128":
+            continue
+        d = make_desc(fmt, "sr", "col", seed)
+        q = fq.fq_quantize(d, xd)
+        yq = fq.fq_dequantize(d, q, 16384, 4096)
+        dx = fq.fq_ste_backward(d, xd, q, dyd)
+        torch.cuda.synchronize()
+        assert np.array_equal(to_bits(yq), ref["y"]), "column dequantize"
+        ref_dx = oracle.ste_backward(x, ref["scales"], ref["outer"], dy, fmt, axis="col")
+        assert np.array_equal(to_bits(dx), ref_dx), "column STE"
