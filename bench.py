@@ -419,17 +419,23 @@ def main():
                           f"{COLS} channels kept in FP8 E4M3", "ms": round(tms, 5), "bytes": tb,
                     "GBps": round(tb / (tms * 1e-3) / 1e9, 1),
                     "frac_hbm": round(tb / (tms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}}
-        # the tracker and the check over the 2880x5760 weight (16.6 M weights)
-        nw = 2880 * 5760
-        wts = [torch.randn(nw, device=dev, dtype=torch.float32) * 0.02 for _ in range(NBUF)]
-        qts = [w.to(torch.bfloat16) for w in wts]
+        # the tracker and the check over the 2880x5760 weight (16.6 M weights),
+        # q and its codes from the NVFP4 per-tensor quantizer along K (the
+        # linear's weight); the check resets to the bin centre
+        wr, wc = 2880, 5760
+        nw = wr * wc
+        d_wq = fq.fq_desc_nvfp4(axis=fq.FQ_AXIS_COL)
+        wts = [torch.randn(wr, wc, device=dev, dtype=torch.float32) * 0.02 for _ in range(NBUF)]
+        wq_outs = [fq.alloc_outputs(d_wq, wr, wc, dev) for _ in range(NBUF)]
+        qts = [fq.fq_fake_quant(d_wq, w.to(torch.bfloat16), out=o) for w, o in zip(wts, wq_outs)]
         sts = [fq.osci_state(nw, dev) for _ in range(NBUF)]
         for i in range(NBUF):
             fq.fq_osci_track(wts[i], qts[i], sts[i], first=True)
         torch.cuda.synchronize()
         for name, fn, by in (("osci_track", lambda i: fq.fq_osci_track(wts[i], qts[i], sts[i]),
                               34 * nw),
-                             ("osci_reset", lambda i: fq.fq_osci_reset(wts[i], qts[i], sts[i], 4.0),
+                             ("osci_reset", lambda i: fq.fq_osci_reset(wts[i], qts[i], sts[i], 4.0,
+                                                                       d_wq, wq_outs[i]),
                               32 * nw)):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()

@@ -24,6 +24,7 @@ FQ_SCALE_E8M0, FQ_SCALE_E4M3 = 0, 1
 FQ_OUTER_NONE, FQ_OUTER_TENSOR, FQ_OUTER_BLOCK128 = 0, 1, 2
 FQ_ROUND_RNE, FQ_ROUND_SR = 0, 1
 FQ_AXIS_ROW, FQ_AXIS_COL = 0, 1
+FQ_OSCI_BIN_CENTRE, FQ_OSCI_GRID_VALUE = 0, 1
 
 # every symbol include/fq.h declares
 EXPORTED = (
@@ -93,7 +94,8 @@ def lib() -> ctypes.CDLL:
         f32 = ctypes.c_float
         L.fq_osci_track.argtypes = [vp, vp, vp, vp, vp, vp, i64, ctypes.c_int32, vp]
         L.fq_osci_track.restype = ctypes.c_int
-        L.fq_osci_reset.argtypes = [vp, vp, vp, vp, vp, vp, i64, f32, vp]
+        L.fq_osci_reset.argtypes = [ctypes.POINTER(FqDesc), vp, vp, vp, vp, vp, i64, i64, vp, vp,
+                                    vp, vp, f32, ctypes.c_int32, vp]
         L.fq_osci_reset.restype = ctypes.c_int
         L.fq_channel_absmax.argtypes = [vp, i64, i64, vp, vp]
         L.fq_channel_absmax.restype = ctypes.c_int
@@ -346,12 +348,24 @@ def fq_osci_track(w, q, st: dict, first: bool = False, stream=None):
     _check(lib().fq_osci_track(*_osci_ptrs(w, q, st, n), n, 1 if first else 0, _stream(stream)))
 
 
-def fq_osci_reset(w, q, st: dict, tau: float, stream=None):
-    """The OsciReset check: oscillating master weights (in place in w) take
-    their quantized value; every element starts a new window."""
-    n = w.numel()
-    _check(lib().fq_osci_reset(*_osci_ptrs(w, q, st, n), n, ctypes.c_float(tau),
-                               _stream(stream)))
+def fq_osci_reset(w, q, st: dict, tau: float, desc=None, quant=None,
+                  target: int = FQ_OSCI_BIN_CENTRE, stream=None):
+    """The OsciReset check: oscillating master weights (in place in w, an FP32
+    [rows, cols] tensor) go to the centre of their current quantization bin,
+    read from `quant` (the Quantized outputs of the quantization with `desc`
+    that gave q), or with target=FQ_OSCI_GRID_VALUE to q itself; every
+    element starts a new window."""
+    assert w.dim() == 2, "w must be [rows, cols]"
+    rows, cols = w.shape
+    n = rows * cols
+    ptrs = _osci_ptrs(w, q, st, n)
+    if target == FQ_OSCI_GRID_VALUE:
+        d, codes, scales, outer = None, None, None, None
+    else:
+        d = ctypes.byref(desc)
+        codes, scales, outer = _qptrs(desc, quant, rows, cols)
+    _check(lib().fq_osci_reset(d, ptrs[0], ptrs[1], codes, scales, outer, rows, cols, *ptrs[2:],
+                               ctypes.c_float(tau), target, _stream(stream)))
 
 
 def fq_channel_absmax(x, amax=None, stream=None):

@@ -723,15 +723,53 @@ fq_status fq_osci_track(const float *w, const void *q_bf16, float *w_prev, void 
                          "osci track launch");
 }
 
-fq_status fq_osci_reset(float *w, const void *q_bf16, float *w_prev, void *q_prev_bf16,
-                        float *dist_m, float *dist_q, int64_t n, float tau, void *stream)
+fq_status fq_osci_reset(const fq_desc *desc, float *w, const void *q_bf16, const void *codes,
+                        const void *scales, const float *outer, int64_t rows, int64_t cols,
+                        float *w_prev, void *q_prev_bf16, float *dist_m, float *dist_q,
+                        float tau, int32_t target, void *stream)
 {
+    if (target != FQ_OSCI_BIN_CENTRE && target != FQ_OSCI_GRID_VALUE)
+        return fail(FQ_ERR_DESC, "target=%d is not FQ_OSCI_BIN_CENTRE/GRID_VALUE", target);
+    if (rows < 1 || cols < 1 || rows > kMaxElems || cols > kMaxElems ||
+        rows * cols > kMaxElems)
+        return fail(FQ_ERR_SHAPE, "rows=%lld cols=%lld out of range", (long long)rows,
+                    (long long)cols);
+    if (cols % 4 != 0)
+        return fail(FQ_ERR_SHAPE, "cols=%lld must be a multiple of 4", (long long)cols);
+    const int64_t n = rows * cols;
     FQ_TRY(check_osci(w, q_bf16, w_prev, q_prev_bf16, dist_m, dist_q, n));
     if (!(tau >= 0.0f) || tau > 3.4e38f)
         return fail(FQ_ERR_DESC, "tau=%g must be finite and >= 0", (double)tau);
-    return device_status(fqimpl::launch_osci_reset(w, q_bf16, w_prev, q_prev_bf16, dist_m,
-                                                   dist_q, n, tau, (hipStream_t)stream),
-                         "osci reset launch");
+    fqimpl::OsciResetArgs a;
+    a.w = w;
+    a.q = q_bf16;
+    a.w_prev = w_prev;
+    a.q_prev = q_prev_bf16;
+    a.dist_m = dist_m;
+    a.dist_q = dist_q;
+    a.n = n;
+    a.R = rows;
+    a.C = cols;
+    a.tau = tau;
+    a.grid_target = target == FQ_OSCI_GRID_VALUE;
+    a.fmt = fqimpl::FMT_MX;
+    a.col = false;
+    a.codes = a.scales = nullptr;
+    a.outer = nullptr;
+    if (!a.grid_target) {
+        Fmt f;
+        FQ_TRY(check_desc(desc, &f, "desc"));
+        FQ_TRY(check_shape(f, desc->axis, rows, cols));
+        FQ_TRY(check_ptr(codes, "codes", true));
+        FQ_TRY(check_ptr(scales, "scales", true));
+        FQ_TRY(check_ptr(outer, "outer", f.fmt != fqimpl::FMT_MX, 4));
+        a.fmt = f.fmt;
+        a.col = desc->axis == FQ_AXIS_COL;
+        a.codes = codes;
+        a.scales = scales;
+        a.outer = f.fmt == fqimpl::FMT_MX ? nullptr : outer;
+    }
+    return device_status(fqimpl::launch_osci_reset(a, (hipStream_t)stream), "osci reset launch");
 }
 
 fq_status fq_channel_absmax(const void *x_bf16, int64_t rows, int64_t cols, uint32_t *amax,

@@ -76,9 +76,21 @@ hipError_t launch_gemm_bf16_nt_pair(const void *a0, const void *bt0, void *c0, i
 hipError_t launch_osci_track(const float *w, const void *q, float *w_prev, void *q_prev,
                              float *dist_m, float *dist_q, int64_t n, int first,
                              hipStream_t stream);
-hipError_t launch_osci_reset(float *w, const void *q, float *w_prev, void *q_prev,
-                             float *dist_m, float *dist_q, int64_t n, float tau,
-                             hipStream_t stream);
+struct OsciResetArgs {
+    float *w;                // FP32 [R, C] master weight (n = R * C elements)
+    const void *q;           // BF16 [R, C] quantized weight
+    float *w_prev;
+    void *q_prev;
+    float *dist_m, *dist_q;
+    int64_t n, R, C;
+    float tau;
+    bool grid_target;        // reset to q instead of the bin centre
+    int fmt;                 // FMT_* of the quantization that gave q (bin-centre target)
+    bool col;                // its axis
+    const void *codes, *scales;
+    const float *outer;
+};
+hipError_t launch_osci_reset(const OsciResetArgs &a, hipStream_t stream);
 hipError_t launch_channel_absmax(const void *x, int64_t R, int64_t C, uint32_t *amax,
                                  hipStream_t stream);
 hipError_t launch_select_channels(const uint32_t *amax, int64_t C, int64_t k, void *retain,

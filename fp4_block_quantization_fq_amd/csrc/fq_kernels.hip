@@ -121,14 +121,18 @@ __global__ __launch_bounds__(kAbsmaxThreads) void k_absmax(const uint4 *__restri
     if (threadIdx.x == 0) partials[blockIdx.x] = m;
 }
 
-// NVFP4 per-tensor outer scale from the partial maxima (every thread).
+// NVFP4 per-tensor outer scale from the partial maxima (every thread of a
+// workgroup of NT threads; NT must be the launching workgroup's size, which
+// sizes the per-wave slots of the reduction).
+template <int NT>
 __device__ __forceinline__ OuterScale tensor_scale(const uint32_t *__restrict__ partials,
                                                    uint32_t npart)
 {
-    __shared__ uint32_t red[kThreads / 64];
+    static_assert(NT % 64 == 0 && NT <= 1024, "whole waves, at most 16");
+    __shared__ uint32_t red[NT / 64];
     uint32_t m = 0;
-    for (uint32_t i = threadIdx.x; i < npart; i += kThreads) m = max(m, partials[i]);
-    m = block_reduce_max<kThreads>(m, red);
+    for (uint32_t i = threadIdx.x; i < npart; i += NT) m = max(m, partials[i]);
+    m = block_reduce_max<NT>(m, red);
     return make_outer(as_f(m << 16));
 }
 
@@ -226,7 +230,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_row(
 {
     OuterScale ot = {0.0f, 0.0f};
     if (FMT == FMT_NVT) {
-        ot = tensor_scale(partials, npart);
+        ot = tensor_scale<kThreads>(partials, npart);
         if (outer && blockIdx.x == 0 && threadIdx.x == 0) outer[0] = ot.s;
     }
     for (uint32_t u = blockIdx.x * kThreads + threadIdx.x; u < nunits;
@@ -304,7 +308,7 @@ __global__ __launch_bounds__(kQcThreads) void k_quant_col(
 
     OuterScale ot = {0.0f, 0.0f};
     if (FMT == FMT_NVT) {
-        ot = tensor_scale(partials, npart);
+        ot = tensor_scale<kQcThreads>(partials, npart);
         if (outer && blockIdx.x == 0 && threadIdx.x == 0) outer[0] = ot.s;
     }
     const uint32_t lane = threadIdx.x & 63, wave = threadIdx.x >> 6;

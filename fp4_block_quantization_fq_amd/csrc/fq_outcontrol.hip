@@ -3,10 +3,11 @@
 // "Resumo Tecnico: TetraJet-v2", sec. 2.B (OsciReset): a weight oscillates
 // when its quantized value keeps travelling between bins while the master
 // weight barely moves; the risk is the ratio of the two distances travelled,
-// and at a low learning rate an oscillating master weight is reset to its
-// quantization bin.  Sec. 2.C (OutControl, static outlier retention): the few
-// channels with large norms, found once during a calibration window, stay in
-// FP8 in the forward and backward passes while the rest is FP4.
+// and at a low learning rate an oscillating master weight is reset to the
+// centre of its current quantization bin.  Sec. 2.C (OutControl, static
+// outlier retention): the few channels with large norms, found once during a
+// calibration window, stay in FP8 in the forward and backward passes while
+// the rest is FP4.
 //
 // All of it is elementwise or per-channel streaming work:
 //  * k_osci_track / k_osci_reset: four weights per lane (16-byte FP32 and
@@ -108,21 +109,66 @@ __global__ __launch_bounds__(kThreads) void k_osci_track(const float4 *__restric
     }
 }
 
-// The check: an element whose dist_q exceeds RN(tau * dist_m) takes its
-// quantized value as its master weight; then every element starts a new
-// window (distances 0, trajectory continuing from the possibly reset w).
-__device__ __forceinline__ float osci_one(float w, float q, float m, float d, float tau)
+// The check: an element whose dist_q exceeds RN(tau * dist_m) is reset;
+// then every element starts a new window (distances 0, trajectory continuing
+// from the possibly reset w).
+//
+// Reset targets:
+//  * kTargetCentre (the page's mechanism): the centre of the element's current
+//    quantization bin, sign(code) * RN(c_m * s_eff), where c_m is the centre of
+//    the interval of scaled magnitudes that round to E2M1 magnitude m:
+//    0, 0.5, 1, 1.5, 2.125, 3, 4.25 and 6 (the bins of 2 and 4 are lopsided on
+//    the E2M1 grid, [1.75, 2.5] and [3.5, 5]; the top bin is closed at 7, the
+//    midpoint with 8, which the format's exponent progression would put next).
+//    Code and block scale come from the quantizer outputs that produced q.
+//  * kTargetGrid: the quantized value q itself.
+enum { kTargetCentre = 0, kTargetGrid = 1 };
+
+// 8 * c_m for m = 0..7 as bytes: {0, 4, 8, 12} and {17, 24, 34, 48}
+constexpr uint32_t kCentreLo = 0x0C080400u, kCentreHi = 0x30221811u;
+
+__device__ __forceinline__ float bin_centre(uint32_t code, float s_eff)
 {
-    return d > tau * m ? q : w;
+    const uint32_t m = code & 7u;
+    const uint32_t e8 = ((m < 4 ? kCentreLo : kCentreHi) >> (8 * (m & 3))) & 0xFFu;
+    const float mag = ((float)e8 * 0.125f) * s_eff;          // c_m exact; one rounding
+    return as_f(as_u(mag) | ((code & 8u) << 28));
 }
 
+struct OsciQuant {
+    const uint8_t *codes;    // E2M1 codes in the quantizer's layout
+    const uint8_t *scales;   // block scales in the quantizer's layout
+    const float *outer;      // NVFP4 outer scale(s), or null
+    uint32_t C;              // columns of w (row-major [R, C])
+    uint64_t R;
+};
+
+// Code and effective scale of element (r, c) of w from the quantizer outputs:
+// row axis codes [R, C/2], scales [R, C/B], outer [R, C/128]; column axis the
+// transposed layouts [C, R/2], [C, R/B], [C, R/128].
+template <int FMT, bool COL>
+__device__ __forceinline__ float centre_of(const OsciQuant &oq, uint64_t r, uint64_t c)
+{
+    constexpr uint32_t B = FMT == FMT_MX ? 32 : 16;
+    const uint64_t qr = COL ? c : r, qc = COL ? r : c;      // quantized orientation
+    const uint64_t L = COL ? oq.R : oq.C;                   // its row length
+    const uint64_t n = qr * L + qc;
+    const uint32_t code = (oq.codes[n >> 1] >> (4 * (uint32_t)(n & 1))) & 0xFu;
+    const uint32_t sc = oq.scales[n / B];
+    float s_eff;
+    if (FMT == FMT_MX) s_eff = e8m0_value(sc);
+    else s_eff = e4m3_value(sc) * (FMT == FMT_NVT ? oq.outer[0] : oq.outer[n >> 7]);
+    return bin_centre(code, s_eff);
+}
+
+template <int TARGET, int FMT, bool COL>
 __global__ __launch_bounds__(kThreads) void k_osci_reset(float4 *__restrict__ w,
                                                          const uint2 *__restrict__ q,
                                                          float4 *__restrict__ w_prev,
                                                          uint2 *__restrict__ q_prev,
                                                          float4 *__restrict__ dm,
                                                          float4 *__restrict__ dq, uint64_t n4,
-                                                         float tau)
+                                                         float tau, OsciQuant oq)
 {
     // 64-bit index: n4 reaches 2^32 at the largest accepted size
     for (uint64_t i = (uint64_t)blockIdx.x * kThreads + threadIdx.x; i < n4;
@@ -130,10 +176,22 @@ __global__ __launch_bounds__(kThreads) void k_osci_reset(float4 *__restrict__ w,
         float4 wv = ld_nt(&w[i]);
         const uint2 qv = ld_nt(&q[i]);
         const float4 m = ld_nt(&dm[i]), d = ld_nt(&dq[i]);
-        wv.x = osci_one(wv.x, bf16_lo(qv.x), m.x, d.x, tau);
-        wv.y = osci_one(wv.y, bf16_hi(qv.x), m.y, d.y, tau);
-        wv.z = osci_one(wv.z, bf16_lo(qv.y), m.z, d.z, tau);
-        wv.w = osci_one(wv.w, bf16_hi(qv.y), m.w, d.w, tau);
+        const bool o0 = d.x > tau * m.x, o1 = d.y > tau * m.y;
+        const bool o2 = d.z > tau * m.z, o3 = d.w > tau * m.w;
+        if (TARGET == kTargetGrid) {
+            wv.x = o0 ? bf16_lo(qv.x) : wv.x;
+            wv.y = o1 ? bf16_hi(qv.x) : wv.y;
+            wv.z = o2 ? bf16_lo(qv.y) : wv.z;
+            wv.w = o3 ? bf16_hi(qv.y) : wv.w;
+        } else if (o0 | o1 | o2 | o3) {
+            // the four elements 4i .. 4i + 3 share one row (C % 4 == 0); the
+            // quantizer outputs are read only for lanes that reset something
+            const uint64_t e = 4 * i, r = e / oq.C, c = e % oq.C;
+            if (o0) wv.x = centre_of<FMT, COL>(oq, r, c);
+            if (o1) wv.y = centre_of<FMT, COL>(oq, r, c + 1);
+            if (o2) wv.z = centre_of<FMT, COL>(oq, r, c + 2);
+            if (o3) wv.w = centre_of<FMT, COL>(oq, r, c + 3);
+        }
         st_nt(&w[i], wv);
         st_nt(&w_prev[i], wv);
         st_nt(&q_prev[i], qv);
@@ -352,13 +410,29 @@ hipError_t launch_osci_track(const float *w, const void *q, float *w_prev, void 
     return hipGetLastError();
 }
 
-hipError_t launch_osci_reset(float *w, const void *q, float *w_prev, void *q_prev,
-                             float *dist_m, float *dist_q, int64_t n, float tau, hipStream_t st)
+hipError_t launch_osci_reset(const OsciResetArgs &a, hipStream_t st)
 {
-    const uint64_t n4 = (uint64_t)n / 4;
-    hipLaunchKernelGGL(k_osci_reset, dim3(grid_for(n4)), dim3(kThreads), 0, st, (float4 *)w,
-                       (const uint2 *)q, (float4 *)w_prev, (uint2 *)q_prev, (float4 *)dist_m,
-                       (float4 *)dist_q, n4, tau);
+    const uint64_t n4 = (uint64_t)a.n / 4;
+    const OsciQuant oq = {(const uint8_t *)a.codes, (const uint8_t *)a.scales, a.outer,
+                          (uint32_t)a.C, (uint64_t)a.R};
+#define FQ_OSCI_ARGS                                                                        \
+    dim3(grid_for(n4)), dim3(kThreads), 0, st, (float4 *)a.w, (const uint2 *)a.q,          \
+        (float4 *)a.w_prev, (uint2 *)a.q_prev, (float4 *)a.dist_m, (float4 *)a.dist_q, n4, \
+        a.tau, oq
+    if (a.grid_target) {
+        hipLaunchKernelGGL((k_osci_reset<kTargetGrid, FMT_MX, false>), FQ_OSCI_ARGS);
+        return hipGetLastError();
+    }
+    switch (a.fmt * 2 + (a.col ? 1 : 0)) {
+    case FMT_MX * 2 + 0: hipLaunchKernelGGL((k_osci_reset<kTargetCentre, FMT_MX, false>), FQ_OSCI_ARGS); break;
+    case FMT_MX * 2 + 1: hipLaunchKernelGGL((k_osci_reset<kTargetCentre, FMT_MX, true>), FQ_OSCI_ARGS); break;
+    case FMT_NVT * 2 + 0: hipLaunchKernelGGL((k_osci_reset<kTargetCentre, FMT_NVT, false>), FQ_OSCI_ARGS); break;
+    case FMT_NVT * 2 + 1: hipLaunchKernelGGL((k_osci_reset<kTargetCentre, FMT_NVT, true>), FQ_OSCI_ARGS); break;
+    case FMT_NV128 * 2 + 0: hipLaunchKernelGGL((k_osci_reset<kTargetCentre, FMT_NV128, false>), FQ_OSCI_ARGS); break;
+    case FMT_NV128 * 2 + 1: hipLaunchKernelGGL((k_osci_reset<kTargetCentre, FMT_NV128, true>), FQ_OSCI_ARGS); break;
+    default: return hipErrorInvalidValue;
+    }
+#undef FQ_OSCI_ARGS
     return hipGetLastError();
 }
 

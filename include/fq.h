@@ -138,7 +138,15 @@ fq_status fq_quantize(const fq_desc *desc, const void *x_bf16, int64_t rows,
 
 /* Dequantize: codes, scales, outer -> y [rows, cols] BF16, where rows x cols
  * is the shape of the original x and desc->axis says which layout codes and
- * scales are in.  Rounding and seed are ignored. */
+ * scales are in: y = BF16_RNE(RN(+-g * s_eff)) per element, the value the
+ * quantized element stands for.  Rounding and seed are ignored.  codes and
+ * scales are required, outer for NVFP4; shape rules as fq_quantize.  Source:
+ * the dequantize half of fake quantization, which brings the quantized
+ * values back into the wider type the forward pass computes in ("Como o
+ * Treinamento ...", "Detalhes tecnicos ou Implementacao"); for the formats,
+ * OCP MX v1.0 (an element's value is its E2M1 value times the block scale)
+ * and, for NVFP4, the E4M3 block scale times the FP32 outer scale
+ * ("Resumo Tecnico: TetraJet-v2", sec. 2.A). */
 fq_status fq_dequantize(const fq_desc *desc, const void *codes, const void *scales,
                         const float *outer, int64_t rows, int64_t cols,
                         void *y_bf16, void *stream);
@@ -204,8 +212,7 @@ fq_status fq_ste_backward_mask(const void *keep, const void *dy_bf16, int64_t ro
 /* Workspace for fq_qlinear_fwd: the dequantized X_hat [M, K] BF16 at offset
  * 0, the dequantized and transposed W_hat^T [N, K] BF16 at offset
  * round_up(M * K * 2, 256), then 8192 bytes of reduction scratch.  When both
- * descriptors are MXFP4 and K is a multiple of 64, the operands stay encoded
- * instead: X's codes [M, K/2] at 0, X's E8M0 scales [M, K/32] at
+ * descriptors are MXFP4, the operands stay encoded instead: X's codes [M, K/2] at 0, X's E8M0 scales [M, K/32] at
  * c1 = round_up(M * K / 2, 256), W's codes in the transposed layout [N, K/2]
  * at c2 = c1 + round_up(M * K / 32, 256), W's scales [N, K/32] at
  * c2 + round_up(N * K / 2, 256) (same total size). */
@@ -216,12 +223,15 @@ size_t fq_qlinear_workspace_size(const fq_desc *desc_x, const fq_desc *desc_w,
  * accumulation on the matrix cores.  X is quantized in groups along K (its
  * rows: desc_x->axis must be FQ_AXIS_ROW), W in groups along K (its
  * columns: desc_w->axis must be FQ_AXIS_COL), so both operands are blocked
- * along the contraction.  K must be divisible by both block sizes (and by
- * 128 for FQ_OUTER_BLOCK128); M, N >= 1; M * K and K * N <= 2^34.
+ * along the contraction.  Shapes: M, N >= 1; K a multiple of 64 (the
+ * matrix-core kernels step through K 64 elements at a time and have no
+ * partial step; this also covers both block sizes), and of 128 for
+ * FQ_OUTER_BLOCK128; N a multiple of 8 (W is quantized along its columns,
+ * whose kernels move 8 columns at a time); M * K, K * N and M * N <= 2^34.
+ * Otherwise FQ_ERR_SHAPE.
  * Source: gpt-oss QAT tutorial, "NVFP4: The Next Generation"
  * (weight-activation quantization of the MLP); TetraJet-v2 sec. 2 (NVFP4
- * activations and weights in every linear layer).  MXFP4 x MXFP4 (K % 64 ==
- * 0) multiplies the E2M1 codes with their E8M0 block scales on the scaled FP4
+ * activations and weights in every linear layer).  MXFP4 x MXFP4 multiplies the E2M1 codes with their E8M0 block scales on the scaled FP4
  * matrix cores (OCP Microscaling v1.0 block scaling), which is the same
  * product of the same dequantized values. */
 fq_status fq_qlinear_fwd(const fq_desc *desc_x, const fq_desc *desc_w,
@@ -302,11 +312,30 @@ fq_status fq_osci_track(const float *w, const void *q_bf16, float *w_prev, void 
 
 /* fq_osci_reset: the check, called when the learning rate is low.  The
  * oscillation risk is dist_q / dist_m; an element with dist_q > RN(tau *
- * dist_m) gets w = q (its quantized value), all others keep w.  Then every
- * element starts a new window: w_prev = w, q_prev = q, distances 0.  tau is
- * the risk threshold (finite, >= 0). */
-fq_status fq_osci_reset(float *w, const void *q_bf16, float *w_prev, void *q_prev_bf16,
-                        float *dist_m, float *dist_q, int64_t n, float tau, void *stream);
+ * dist_m) is reset, all others keep w.  Then every element starts a new
+ * window: w_prev = w, q_prev = q, distances 0.  tau is the risk threshold
+ * (finite, >= 0).  w, q and the state are [rows, cols] row-major (n =
+ * rows * cols), cols a multiple of 4.
+ * target FQ_OSCI_BIN_CENTRE (sec. 2.B, "Mecanismo": the master weight goes
+ * to the centre of its current quantization bin): w = sign * RN(c_m * s_eff)
+ * for the element's current E2M1 code (sign, magnitude m) and effective
+ * block scale s_eff, read from codes / scales / outer, the fq_quantize or
+ * fq_fake_quant outputs of the quantization that gave q, in desc's format
+ * and axis layout (rows x cols is the shape of that quantization's input).
+ * c_m is the centre of the interval of scaled magnitudes that round to grid
+ * value g_m: 0, 0.5, 1, 1.5, 2.125, 3, 4.25, 6 for g = 0, 0.5, 1, 1.5, 2, 3,
+ * 4, 6 (the bins of 2 and 4, [1.75, 2.5] and [3.5, 5], are lopsided; the top
+ * bin, from 5, is read as closing at 7, midway to 8, the next value of the
+ * E2M1 exponent progression, so its centre is 6).  desc, codes, scales
+ * (16-byte aligned) are required, outer (4-byte aligned) for NVFP4; desc's
+ * shape rules are those of fq_quantize.
+ * target FQ_OSCI_GRID_VALUE: w = q (its quantized value); desc, codes,
+ * scales and outer are not read and may be NULL. */
+enum { FQ_OSCI_BIN_CENTRE = 0, FQ_OSCI_GRID_VALUE = 1 };
+fq_status fq_osci_reset(const fq_desc *desc, float *w, const void *q_bf16, const void *codes,
+                        const void *scales, const float *outer, int64_t rows, int64_t cols,
+                        float *w_prev, void *q_prev_bf16, float *dist_m, float *dist_q,
+                        float tau, int32_t target, void *stream);
 
 /* ---- TetraJet-v2 static outlier-channel retention (sec. 2.C) ----
  * Calibration: fq_channel_absmax folds max |x[:, c]| of a BF16 [rows, cols]

@@ -316,20 +316,101 @@ def osci_track(w: np.ndarray, q: np.ndarray, st: dict, first: bool) -> None:
     st["q_prev"][:] = q
 
 
-def osci_reset(w: np.ndarray, q: np.ndarray, st: dict, tau: float) -> np.ndarray:
+E2M1_GRID = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)
+
+
+def e2m1_bin_centres() -> list[float]:
+    """Centre of the quantization bin of each E2M1 magnitude code m = 0..7.
+
+    "Resumo Tecnico: TetraJet-v2", sec. 2.B (mechanism) resets an oscillating
+    master weight to the centre of its current quantization bin.  The bin of
+    grid value g_m is the interval of scaled magnitudes that round to it: from
+    the midpoint with the grid value below to the midpoint with the one above.
+    READINGS: the bin of 0 holds both signs ([-0.25, 0.25], centre 0); E2M1
+    stops at 6, so the top bin (from 5 up) is closed at 7, the midpoint with
+    8, the value that follows 4 and 6 in the format's exponent progression,
+    which puts its centre on 6 itself (also the largest magnitude the clipped
+    straight-through gradient still passes).
+    """
+    g = list(E2M1_GRID) + [8.0]
+    out = []
+    for m in range(8):
+        hi = (g[m] + g[m + 1]) / 2
+        lo = -hi if m == 0 else (g[m - 1] + g[m]) / 2
+        out.append((lo + hi) / 2)
+    return out
+
+
+def element_code_and_scale(codes: np.ndarray, scales: np.ndarray, outer, fmt: str,
+                           shape: tuple[int, int], axis: str = "row"):
+    """Per element of x [R, C]: its E2M1 code (uint8) and effective block scale
+    s_eff (float32), read from quantizer outputs in the layout of `axis`
+    (MXFP4: 2^(code - 127); NVFP4: RN32(e4m3(code) * s), s the per-tensor or
+    128-block outer scale)."""
+    R, C = shape
+    QR, QC = (R, C) if axis == "row" else (C, R)
+    B = BLOCK[fmt]
+    packed = np.asarray(codes, np.uint8).reshape(QR, QC // 2)
+    code = np.empty((QR, QC), np.uint8)
+    code[:, 0::2] = packed & 15
+    code[:, 1::2] = packed >> 4
+    sc = np.repeat(np.asarray(scales, np.uint8).reshape(QR, QC // B), B, axis=1)
+    if fmt == "mx":
+        table = np.array([e8m0_decode(c) for c in range(255)] + [np.nan], np.float32)
+        s_eff = table[sc]
+    else:
+        table = np.array([e4m3_decode(c) for c in range(256)], np.float64).astype(np.float32)
+        if fmt == "nv_tensor":
+            s = np.float32(np.asarray(outer, np.float32).reshape(-1)[0])
+        else:
+            s = np.repeat(np.asarray(outer, np.float32).reshape(QR, QC // 128), 128, axis=1)
+        s_eff = (table[sc] * s).astype(np.float32)        # one FP32 rounding
+    if axis == "col":
+        code, s_eff = code.T, s_eff.T
+    return np.ascontiguousarray(code), np.ascontiguousarray(s_eff)
+
+
+def bin_centre_values(codes: np.ndarray, scales: np.ndarray, outer, fmt: str,
+                      shape: tuple[int, int], axis: str = "row") -> np.ndarray:
+    """FP32 [R, C]: sign(code) * RN32(c_m * s_eff), the centre of each element's
+    current quantization bin in the units of x (c_m from e2m1_bin_centres,
+    exact in FP32; the sign of the code is kept, so code 8 gives -0.0)."""
+    code, s_eff = element_code_and_scale(codes, scales, outer, fmt, shape, axis)
+    c = np.array(e2m1_bin_centres(), np.float32)[code & 7]
+    mag = (c * s_eff).astype(np.float32)
+    return np.where(code >= 8, -mag, mag).astype(np.float32)
+
+
+def osci_reset(w: np.ndarray, q: np.ndarray, st: dict, tau: float, target: str = "centre",
+               quant: dict | None = None, fmt: str | None = None, axis: str = "row"):
     """The OsciReset check (sec. 2.B, mechanism), called by the training loop
     when the learning rate is low.  The oscillation risk is dist_q / dist_m;
     READING: an element oscillates when dist_q > RN32(tau * dist_m) (so a
     quantized value that moved while the master weight did not counts, and
-    one that never moved does not), and its master weight is reset to its
-    current quantized value, the representative of its quantization bin.  A
-    check starts a new window: the distances restart at 0 and the trajectory
-    continues from the (reset) weights.  Returns the new w and the boolean
-    mask of reset elements."""
+    one that never moved does not).
+
+    target "centre" (the page's mechanism): an oscillating master weight goes
+    to the centre of its current quantization bin (bin_centre_values), read
+    from `quant`, the codes / scales / outer of the quantization that gave q
+    (fake_quant's output for w's BF16 copy, format fmt, along `axis`); w is
+    then [R, C] shaped like that quantization's input.  target "grid": it
+    goes to its quantized value q itself (the grid point its bin maps to).
+
+    A check starts a new window: the distances restart at 0 and the
+    trajectory continues from the (reset) weights.  Returns the new w (flat)
+    and the boolean mask of reset elements."""
+    shape = np.shape(w)
     w = np.array(w, np.float32).reshape(-1)
     q = np.asarray(q, np.uint16).reshape(-1)
     osc = st["dist_q"] > (np.float32(tau) * st["dist_m"])
-    w[osc] = bf16_bits_to_f64(q[osc]).astype(np.float32)
+    if target == "grid":
+        w[osc] = bf16_bits_to_f64(q[osc]).astype(np.float32)
+    elif target == "centre":
+        cv = bin_centre_values(quant["codes"], quant["scales"], quant["outer"], fmt,
+                               shape, axis).reshape(-1)
+        w[osc] = cv[osc]
+    else:
+        raise ValueError(f"unknown reset target {target!r}")
     st["w_prev"][:] = w
     st["q_prev"][:] = q
     st["dist_m"][:] = 0

@@ -62,3 +62,22 @@ def assert_same(gpu: dict, ref: dict, keys=("codes", "scales", "outer", "y"), ta
         assert bad.size == 0, (f"{tag}: {k}: {bad.size} of {g.size} differ; first at flat "
                                f"{bad[:5].tolist()}: gpu {g.reshape(-1)[bad[:5]].tolist()} "
                                f"oracle {r.reshape(-1)[bad[:5]].tolist()}")
+
+
+def assert_product_bound(got: np.ndarray, ref: np.ndarray, absprod: np.ndarray, kdim: int,
+                         keep: np.ndarray | None = None, tag: str = ""):
+    """Element-wise check of a BF16 matrix product against the float64 product
+    `ref` of the same BF16 operands.  The products of BF16 values are exact in
+    FP32, so the device result differs from `ref` only by the FP32
+    accumulation (at most about kdim * 2^-24 * (|A| @ |B|), any order) and the
+    final BF16 rounding (2^-8 relative): |got - ref| <= 2^-8 |ref| +
+    2 kdim 2^-24 (|A| @ |B|).  Where keep is 0 the result must be +0 or -0."""
+    bound = 2.0 ** -8 * np.abs(ref) + 2.0 * kdim * 2.0 ** -24 * absprod
+    err = np.abs(got - ref)
+    if keep is not None:
+        assert np.all(got[keep == 0] == 0), (tag, "dropped entries must be 0")
+        err = np.where(keep == 0, 0.0, err)
+    bad = np.argwhere(err > bound)
+    assert bad.size == 0, (f"{tag}: {len(bad)} of {got.size} elements outside the bound; "
+                           f"first {bad[:3].tolist()}: got {got[tuple(bad[0])]} ref "
+                           f"{ref[tuple(bad[0])]} bound {bound[tuple(bad[0])]}")

@@ -123,7 +123,11 @@ def test_other_entry_points_validate(L):
                             fake(), fake(), ws, None) == fq.FQ_ERR_DESC
     assert L.fq_qlinear_fwd(ctypes.byref(col), ctypes.byref(col), fake(), fake(), 128, 128, 128,
                             fake(), fake(), ws, None) == fq.FQ_ERR_DESC
+    # documented shape rules: K a multiple of 64 (K = 96 is a whole number of
+    # NVFP4 blocks but not of the 64-element K step), N a multiple of 8
     assert L.fq_qlinear_fwd(ctypes.byref(nv), ctypes.byref(col), fake(), fake(), 128, 96, 128,
+                            fake(), fake(), ws, None) == fq.FQ_ERR_SHAPE
+    assert L.fq_qlinear_fwd(ctypes.byref(nv), ctypes.byref(col), fake(), fake(), 128, 128, 132,
                             fake(), fake(), ws, None) == fq.FQ_ERR_SHAPE
     assert L.fq_qlinear_fwd(ctypes.byref(nv), ctypes.byref(col), fake(), fake(), 128, 128, 128,
                             fake(), fake(), 1024, None) == fq.FQ_ERR_WORKSPACE
@@ -165,11 +169,30 @@ def test_outcontrol_entry_points_validate(L):
     assert L.fq_osci_track(f(), None, f(), f(), f(), f(), 64, 0, None) == fq.FQ_ERR_NULL
     assert L.fq_osci_track(f(0x10004), f(), f(), f(), f(), f(), 64, 0, None) == fq.FQ_ERR_ALIGN
     assert L.fq_osci_track(f(), f(0x10004), f(), f(), f(), f(), 64, 0, None) == fq.FQ_ERR_ALIGN
-    assert L.fq_osci_reset(f(), f(), f(), f(), f(), None, 64, ctypes.c_float(2.0),
-                           None) == fq.FQ_ERR_NULL
+    # fq_osci_reset(desc, w, q, codes, scales, outer, rows, cols, w_prev, q_prev,
+    #               dist_m, dist_q, tau, target, stream)
+    mx = fq.fq_desc_mxfp4()
+    nv = fq.fq_desc_nvfp4()
+    C, G = fq.FQ_OSCI_BIN_CENTRE, fq.FQ_OSCI_GRID_VALUE
+
+    def rst(desc=mx, w=f(), q=f(), codes=f(), scales=f(), outer=None, rows=2, cols=32,
+            tau=2.0, target=C):
+        d = None if desc is None else ctypes.byref(desc)
+        return L.fq_osci_reset(d, w, q, codes, scales, outer, rows, cols, f(), f(), f(), f(),
+                               ctypes.c_float(tau), target, None)
+
+    assert rst(q=None) == fq.FQ_ERR_NULL
     for bad in (-1.0, float("nan"), float("inf")):
-        assert L.fq_osci_reset(f(), f(), f(), f(), f(), f(), 64, ctypes.c_float(bad),
-                               None) == fq.FQ_ERR_DESC, bad
+        assert rst(tau=bad) == fq.FQ_ERR_DESC, bad
+    assert rst(target=2) == fq.FQ_ERR_DESC
+    assert rst(cols=30) == fq.FQ_ERR_SHAPE                  # cols % 4
+    assert rst(rows=0) == fq.FQ_ERR_SHAPE
+    assert rst(cols=36) == fq.FQ_ERR_SHAPE                  # MXFP4 row blocks of 32
+    assert rst(desc=None) == fq.FQ_ERR_NULL                 # the centre needs the format
+    assert rst(codes=None) == fq.FQ_ERR_NULL
+    assert rst(scales=None) == fq.FQ_ERR_NULL
+    assert rst(desc=nv, cols=48) == fq.FQ_ERR_NULL         # NVFP4 needs its outer scale
+    assert rst(codes=f(0x10008)) == fq.FQ_ERR_ALIGN
     # calibration and selection
     assert L.fq_channel_absmax(f(), 64, 12, f(), None) == fq.FQ_ERR_SHAPE
     assert L.fq_channel_absmax(f(), 0, 64, f(), None) == fq.FQ_ERR_SHAPE

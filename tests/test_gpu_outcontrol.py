@@ -17,30 +17,59 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 
 
-def test_osci_trajectory_matches_oracle():
+OSCI_CASES = [("mx", "row", (256, 512)), ("nv_tensor", "row", (128, 1024)),
+              ("nv_128", "row", (96, 1024)), ("mx", "col", (512, 264)),
+              ("nv_tensor", "col", (1024, 136)), ("nv_128", "col", (384, 200))]
+
+
+def _gpu_quant(wbits, fmt, axis):
+    """The GPU quantizer's fake quantization of the BF16 copy of w (checked
+    against the oracle's), as the forward would produce q and its codes."""
+    d = make_desc(fmt, "rne", axis)
+    R, C = wbits.shape
+    out = fq.alloc_outputs(d, R, C, DEV)
+    y = fq.fq_fake_quant(d, to_dev(wbits), out=out)
+    ref = oracle.fake_quant(wbits, fmt, "rne", axis)
+    torch.cuda.synchronize()
+    assert_same({"y": to_bits(y), "codes": to_np(out.codes), "scales": to_np(out.scales),
+                 "outer": None if out.outer is None else to_np(out.outer)}, ref)
+    return d, out, y, ref
+
+
+@pytest.mark.parametrize("fmt,axis,shape", OSCI_CASES)
+@pytest.mark.parametrize("target", ["centre", "grid"])
+def test_osci_trajectory_matches_oracle(fmt, axis, shape, target):
     rng = np.random.default_rng(21)
-    R, C = 256, 512                       # n = 131072 weights, MXFP4 groups along rows
+    R, C = shape
     n = R * C
-    w = (rng.standard_normal(n).astype(np.float32) * np.float32(0.02))
+    w = (rng.standard_normal(n).astype(np.float32) * np.float32(0.02)).reshape(R, C)
     st_o = oracle.osci_state(n)
     st_g = fq.osci_state(n, DEV)
     tw = torch.from_numpy(w.copy()).to(DEV)
     for t in range(6):
         if t:
-            w = (w + rng.standard_normal(n).astype(np.float32) * np.float32(2e-4)).astype(np.float32)
+            w = (w + rng.standard_normal((R, C)).astype(np.float32) * np.float32(2e-4)).astype(np.float32)
             tw.copy_(torch.from_numpy(w))
-        q = oracle.fake_quant(wl.f32_to_bf16_bits(w).reshape(R, C), "mx")["y"].reshape(-1)
-        oracle.osci_track(w, q, st_o, first=(t == 0))
-        fq.fq_osci_track(tw, to_dev(q), st_g, first=(t == 0))
+        d, out, yq, ref = _gpu_quant(wl.f32_to_bf16_bits(w), fmt, axis)
+        q = ref["y"].reshape(-1)
+        oracle.osci_track(w.reshape(-1), q, st_o, first=(t == 0))
+        fq.fq_osci_track(tw, yq, st_g, first=(t == 0))
         torch.cuda.synchronize()
         for k in ("w_prev", "dist_m", "dist_q"):
             assert np.array_equal(to_np(st_g[k]).view(np.uint32), st_o[k].view(np.uint32)), (t, k)
         assert np.array_equal(to_bits(st_g["q_prev"]), st_o["q_prev"]), t
-    w_new, osc = oracle.osci_reset(w, q, st_o, 4.0)
+    w_new, osc = oracle.osci_reset(w, q, st_o, 4.0, target, ref, fmt, axis)
     assert osc.any() and not osc.all()
-    fq.fq_osci_reset(tw, to_dev(q), st_g, 4.0)
+    if target == "centre":
+        fq.fq_osci_reset(tw, yq, st_g, 4.0, d, out, fq.FQ_OSCI_BIN_CENTRE)
+        # the two readings part where the current code sits in the lopsided
+        # bins of 2 and 4
+        qv = oracle.bf16_bits_to_f64(q).astype(np.float32)
+        assert (w_new[osc] != qv[osc]).any()
+    else:
+        fq.fq_osci_reset(tw, yq, st_g, 4.0, target=fq.FQ_OSCI_GRID_VALUE)
     torch.cuda.synchronize()
-    assert np.array_equal(to_np(tw).view(np.uint32), w_new.view(np.uint32))
+    assert np.array_equal(to_np(tw).reshape(-1).view(np.uint32), w_new.view(np.uint32))
     for k in ("w_prev", "dist_m", "dist_q"):
         assert np.array_equal(to_np(st_g[k]).view(np.uint32), st_o[k].view(np.uint32)), k
 
@@ -95,24 +124,39 @@ def test_fake_quant_retain_full_size():
     _retain_case(x, "nv_128", "sr", 410, seed=1234)
 
 
-@pytest.mark.parametrize("n", [4, 132, 4096 * 33 + 4])
-def test_osci_sizes(n):
-    # the smallest size, a size that leaves a partial wave, and one that
-    # leaves a partial workgroup: every element tracked and checked
+@pytest.mark.parametrize("shape,fmt", [((1, 4), None), ((1, 132), None),
+                                       ((33, 4096 + 4), None), ((33, 4128), "mx"),
+                                       ((3, 4096 * 11), "nv_128")])
+def test_osci_sizes(shape, fmt):
+    # the smallest size, a size that leaves a partial wave, and ones that
+    # leave a partial workgroup: every element tracked and checked (the
+    # grid-value target where the shape cannot be blocked)
+    R, C = shape
+    n = R * C
     rng = np.random.default_rng(n)
-    w0 = rng.standard_normal(n).astype(np.float32)
-    w1 = (w0 + rng.standard_normal(n).astype(np.float32) * np.float32(1e-3)).astype(np.float32)
-    q0 = wl.f32_to_bf16_bits(w0)
-    q1 = wl.f32_to_bf16_bits(np.where(rng.random(n) < 0.5, w1, w0 + np.float32(0.25)))
+    w0 = rng.standard_normal((R, C)).astype(np.float32)
+    w1 = (w0 + rng.standard_normal((R, C)).astype(np.float32) * np.float32(1e-3)).astype(np.float32)
+    if fmt is None:
+        q0 = wl.f32_to_bf16_bits(w0)
+        q1 = wl.f32_to_bf16_bits(np.where(rng.random((R, C)) < 0.5, w1, w0 + np.float32(0.25)))
+        tq0, tq1 = to_dev(q0), to_dev(q1)
+    else:
+        _, _, tq0, r0 = _gpu_quant(wl.f32_to_bf16_bits(w0), fmt, "row")
+        d, out, tq1, r1 = _gpu_quant(wl.f32_to_bf16_bits(w1), fmt, "row")
+        q0, q1 = r0["y"], r1["y"]
     st_o, st_g = oracle.osci_state(n), fq.osci_state(n, DEV)
     tw = torch.from_numpy(w0.copy()).to(DEV)
-    oracle.osci_track(w0, q0, st_o, first=True)
-    fq.fq_osci_track(tw, to_dev(q0), st_g, first=True)
+    oracle.osci_track(w0.reshape(-1), q0.reshape(-1), st_o, first=True)
+    fq.fq_osci_track(tw, tq0, st_g, first=True)
     tw.copy_(torch.from_numpy(w1))
-    oracle.osci_track(w1, q1, st_o, first=False)
-    fq.fq_osci_track(tw, to_dev(q1), st_g)
-    w_new, osc = oracle.osci_reset(w1, q1, st_o, 8.0)
-    fq.fq_osci_reset(tw, to_dev(q1), st_g, 8.0)
+    oracle.osci_track(w1.reshape(-1), q1.reshape(-1), st_o, first=False)
+    fq.fq_osci_track(tw, tq1, st_g)
+    if fmt is None:
+        w_new, osc = oracle.osci_reset(w1, q1, st_o, 8.0, "grid")
+        fq.fq_osci_reset(tw, tq1, st_g, 8.0, target=fq.FQ_OSCI_GRID_VALUE)
+    else:
+        w_new, osc = oracle.osci_reset(w1, q1, st_o, 0.5, "centre", r1, fmt, "row")
+        fq.fq_osci_reset(tw, tq1, st_g, 0.5, d, out)
     torch.cuda.synchronize()
-    assert np.array_equal(to_np(tw).view(np.uint32), w_new.view(np.uint32))
-    assert np.array_equal(to_bits(st_g["q_prev"]), st_o["q_prev"])
+    assert np.array_equal(to_np(tw).reshape(-1).view(np.uint32), w_new.view(np.uint32))
+    assert np.array_equal(to_bits(st_g["q_prev"]).reshape(-1), st_o["q_prev"])

@@ -12,7 +12,8 @@ import torch
 import fp4_block_quantization_fq_amd as fq
 import oracle
 import workloads as wl
-from gpu_util import (assert_same, gpu_fake_quant, make_desc, to_bits, to_dev, to_np)
+from gpu_util import (assert_product_bound, assert_same, gpu_fake_quant, make_desc, to_bits,
+                      to_dev, to_np)
 
 pytestmark = pytest.mark.gpu
 
@@ -173,6 +174,10 @@ def _qlinear_check(M, K, N, fmt_x="nv_tensor", fmt_w="nv_tensor", seeds=(6, 7), 
         assert np.array_equal(to_bits(xhat), ref["xhat"])
         assert np.array_equal(to_bits(what_t), np.ascontiguousarray(ref["what"].T))
     yg = oracle.bf16_bits_to_f64(to_bits(y))
+    # every element within the FP32-accumulation and BF16-rounding bound
+    absprod = np.abs(oracle.bf16_bits_to_f64(ref["xhat"])) @ np.abs(
+        oracle.bf16_bits_to_f64(ref["what"]))
+    assert_product_bound(yg, ref["y"], absprod, K, tag=f"qlinear {M}x{K}x{N} {fmt_x}/{fmt_w}")
     err = np.linalg.norm(yg - ref["y"]) / np.linalg.norm(ref["y"])
     assert err <= tol, err
     return err
@@ -247,6 +252,20 @@ def test_workload_qlinear_mxfp4():
     # the same shape with both operands MXFP4: codes and scales on the FP4 matrix cores
     err = _qlinear_check(8192, 2880, 5760, "mx", "mx")
     assert err < 4e-3
+
+
+@pytest.mark.parametrize("fmt", ["nv_tensor", "mx"])
+def test_qlinear_repeat_runs_identical(fmt):
+    """Two runs of the full-size linear give the same bits (the GEMMs' LDS
+    stages and epilogue have no race that could change a result)."""
+    x, w = wl.linear_inputs()
+    dx, dw = make_desc(fmt, "rne", "row"), make_desc(fmt, "rne", "col")
+    xd, wd = to_dev(x), to_dev(w)
+    ws = fq.qlinear_workspace(dx, dw, 8192, 2880, 5760, xd.device)
+    y1 = fq.fq_qlinear_fwd(dx, dw, xd, wd, ws=ws)
+    y2 = fq.fq_qlinear_fwd(dx, dw, xd, wd, ws=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
 
 
 def test_workload_column_ops_at_bench_size():

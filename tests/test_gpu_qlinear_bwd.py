@@ -9,7 +9,7 @@ import torch
 import fp4_block_quantization_fq_amd as fq
 import oracle
 import workloads as wl
-from gpu_util import make_desc, to_bits, to_dev
+from gpu_util import assert_product_bound, make_desc, to_bits, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -25,11 +25,18 @@ def _bwd_check(M, K, N, fmt_x, fmt_w, fmt_g, rounding_g="sr", seed_g=1234,
                                make_desc(fmt_g, rounding_g, "row", seed_g),
                                to_dev(x), to_dev(w), to_dev(dy))
     torch.cuda.synchronize()
+    f64 = oracle.bf16_bits_to_f64
     errs = {}
-    for name, got, keep in (("dx", dx, ref["keep_x"]), ("dw", dw, ref["keep_w"])):
-        g = oracle.bf16_bits_to_f64(to_bits(got))
+    for name, got, keep, a, b, kdim in (
+            ("dx", dx, ref["keep_x"], f64(ref["q_dy_n"]), f64(ref["q_w_n"]).T, N),
+            ("dw", dw, ref["keep_w"], f64(ref["q_x_m"]).T, f64(ref["q_dy_m"]), M)):
+        g = f64(to_bits(got))
         r = ref[name]
         assert np.all(g[keep == 0] == 0), name
+        # element-wise: the unmasked product within the accumulation bound
+        raw = a @ b
+        assert_product_bound(g, raw, np.abs(a) @ np.abs(b), kdim, keep=keep,
+                             tag=f"{name} {M}x{K}x{N}")
         errs[name] = np.linalg.norm(g - r) / np.linalg.norm(r)
         assert errs[name] <= tol, (name, errs[name])
     return errs
@@ -63,3 +70,18 @@ def test_workload_qlinear_bwd_mxfp4():
     # MXFP4 gradient operands: both products run on the scaled FP4 matrix cores
     errs = _bwd_check(8192, 2880, 5760, "mx", "mx", "mx")
     assert max(errs.values()) < 4e-3
+
+
+@pytest.mark.parametrize("fmts", [("nv_tensor", "nv_tensor", "nv_128"), ("mx", "mx", "mx")])
+def test_qlinear_bwd_repeat_runs_identical(fmts):
+    """Two runs of the full-size backward (grouped dX / dW launch, masked
+    epilogue) give the same bits."""
+    x, w = wl.linear_inputs()
+    dy = wl.normal_bf16((8192, 5760), 1e-3, 8)
+    args = (make_desc(fmts[0], "rne", "row"), make_desc(fmts[1], "rne", "col"),
+            make_desc(fmts[2], "sr", "row", 1234), to_dev(x), to_dev(w), to_dev(dy))
+    a = fq.fq_qlinear_bwd(*args)
+    b = fq.fq_qlinear_bwd(*args)
+    torch.cuda.synchronize()
+    for u, v in zip(a, b):
+        assert torch.equal(u.view(torch.int16), v.view(torch.int16))

@@ -17,11 +17,15 @@ def bf(vals):
 
 
 def run_traj(ws, qs, tau):
+    """Detection on hand trajectories; the reset goes to the quantized value
+    (the "grid" target), which equals the bin centre at the grid points these
+    trajectories use (0, 0.5, 1, 1.5 and 3 have symmetric bins)."""
     st = oracle.osci_state(len(ws[0]))
     for t, (w, q) in enumerate(zip(ws, qs)):
         oracle.osci_track(np.asarray(w, np.float32), bf(q), st, first=(t == 0))
     dm, dq = st["dist_m"].copy(), st["dist_q"].copy()
-    w_new, osc = oracle.osci_reset(np.asarray(ws[-1], np.float32), bf(qs[-1]), st, tau)
+    w_new, osc = oracle.osci_reset(np.asarray(ws[-1], np.float32), bf(qs[-1]), st, tau,
+                                   target="grid")
     return dm, dq, w_new, osc, st
 
 
@@ -57,6 +61,117 @@ def test_osci_degenerate_windows():
     assert dm.tolist() == [0.0, 0.0, 0.5] and dq.tolist() == [1.0, 0.0, 1.0]
     assert osc.tolist() == [True, False, False]
     assert w_new.tolist() == [3.0, 3.0, 1.5]
+
+
+def test_bin_centres_by_hand():
+    # E2M1 magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6; round-to-nearest bins
+    # [-.25, .25], [.25, .75], [.75, 1.25], [1.25, 1.75], [1.75, 2.5],
+    # [2.5, 3.5], [3.5, 5], [5, 7] (the last one by the reading)
+    assert oracle.e2m1_bin_centres() == [0.0, 0.5, 1.0, 1.5, 2.125, 3.0, 4.25, 6.0]
+
+
+def test_bin_centres_lie_in_their_rounding_bins():
+    # every centre rounds to its own code, and so does every point of the bin
+    # short of its two ends (the oracle's RNE is pinned on its own)
+    c = oracle.e2m1_bin_centres()
+    g = list(oracle.E2M1_GRID)
+    for m in range(8):
+        assert oracle.e2m1_rne(c[m]) == m
+        hi = (g[m] + g[m + 1]) / 2 if m < 7 else 7.0
+        lo = (g[m - 1] + g[m]) / 2 if m else 0.0
+        for t in np.linspace(lo, hi, 33)[1:-1]:
+            assert oracle.e2m1_rne(float(t)) == m, (m, t)
+        assert c[m] - lo == hi - c[m] or m == 0
+
+
+def _osci_case(rows_of_w, fmt, tau, axis="row"):
+    """Track a trajectory of [R, C] master weights quantized with fmt (RNE)
+    along axis, then reset with both targets.  Returns the two new weights."""
+    st_c = oracle.osci_state(rows_of_w[0].size)
+    st_g = oracle.osci_state(rows_of_w[0].size)
+    for t, w in enumerate(rows_of_w):
+        q = oracle.fake_quant(bf(w), fmt, "rne", axis)
+        for st in (st_c, st_g):
+            oracle.osci_track(np.asarray(w, np.float32).reshape(-1), q["y"].reshape(-1), st,
+                              first=(t == 0))
+    w = np.asarray(rows_of_w[-1], np.float32)
+    wc, osc_c = oracle.osci_reset(w, q["y"], st_c, tau, "centre", q, fmt, axis)
+    wg, osc_g = oracle.osci_reset(w, q["y"], st_g, tau, "grid")
+    assert np.array_equal(osc_c, osc_g)
+    return wc.reshape(w.shape), wg.reshape(w.shape), osc_c.reshape(w.shape)
+
+
+def test_osci_reset_to_bin_centre_mxfp4():
+    # one 32-block with amax 0.75 -> E8M0 scale 2^-3.  Element 1 hops across
+    # the 1.5 / 2 boundary (1.75 * 2^-3 = 0.21875): a = 1.8125, 1.6875, 1.8125
+    # -> q = 0.25, 0.1875, 0.25; element 2 across the 3 / 4 boundary
+    # (-0.4375): a = 3.5625, 3.4375, 3.5625 -> q = -0.5, -0.375, -0.5.
+    # dist_m = 1/32 for both; dist_q = 1/8 and 1/4: risks 4 and 8 > 2.
+    # Current codes 4 (2.0) and 0xE (-4.0): bin centres 2.125 * 2^-3 = 0.265625
+    # and -4.25 * 2^-3 = -0.53125; the grid target gives 0.25 and -0.5.
+    base = np.zeros((1, 32), np.float32)
+    base[0, 0] = 0.75
+    traj = []
+    for w1, w2 in ((0.2265625, -0.4453125), (0.2109375, -0.4296875), (0.2265625, -0.4453125)):
+        b = base.copy()
+        b[0, 1], b[0, 2] = w1, w2
+        traj.append(b)
+    wc, wg, osc = _osci_case(traj, "mx", 2.0)
+    assert np.flatnonzero(osc).tolist() == [1, 2]
+    assert wc[0, :3].tolist() == [0.75, 0.265625, -0.53125]
+    assert wg[0, :3].tolist() == [0.75, 0.25, -0.5]
+
+
+def test_osci_reset_to_bin_centre_nvfp4():
+    # NVFP4 per tensor, one 16-block with amax 2.625: s_t = 2^-10, block scale
+    # 448, s_eff = 0.4375.  Element 1: 0.78125, 0.75, 0.78125 -> a = 1.7857.. /
+    # 1.7142.. -> codes 4, 3, 4 (q = 0.875, 0.65625, 0.875); dist_m = 1/16,
+    # dist_q = 7/16 (risk 7).  Element 2: -1.65625, -1.5, -1.65625 -> a =
+    # 3.7857.. / 3.4285.. -> codes 0xE, 0xD (q = -1.75, -1.3125); dist_m =
+    # 5/16, dist_q = 7/8 (risk 2.8).  Centres: 2.125 * 0.4375 = 0.9296875 and
+    # -4.25 * 0.4375 = -1.859375; grid values 0.875 and -1.75.
+    base = np.zeros((1, 16), np.float32)
+    base[0, 0] = 2.625
+    traj = []
+    for w1, w2 in ((0.78125, -1.65625), (0.75, -1.5), (0.78125, -1.65625)):
+        b = base.copy()
+        b[0, 1], b[0, 2] = w1, w2
+        traj.append(b)
+    wc, wg, osc = _osci_case(traj, "nv_tensor", 2.0)
+    assert np.flatnonzero(osc).tolist() == [1, 2]
+    assert wc[0, :3].tolist() == [2.625, 0.9296875, -1.859375]
+    assert wg[0, :3].tolist() == [2.625, 0.875, -1.75]
+
+
+def test_osci_reset_centre_column_layout():
+    # W [32, 8] grouped down its columns (MXFP4): column 3 has amax 0.75
+    # (scale 2^-3), the others amax 48 (scale 2^3).  Element (5, 3) flips
+    # between codes 3 and 4 of its column's scale and is reset to
+    # 2.125 * 2^-3; read in the row layout its code and scale would differ.
+    base = np.zeros((32, 8), np.float32)
+    base[0, :] = 48.0
+    base[0, 3] = 0.75
+    traj = []
+    for v in (0.2265625, 0.2109375, 0.2265625):
+        b = base.copy()
+        b[5, 3] = v
+        traj.append(b)
+    wc, wg, osc = _osci_case(traj, "mx", 2.0, axis="col")
+    assert np.argwhere(osc).tolist() == [[5, 3]]
+    assert wc[5, 3] == 0.265625 and wg[5, 3] == 0.25
+    assert np.array_equal(np.delete(wc.reshape(-1), 5 * 8 + 3), np.delete(traj[-1].reshape(-1), 5 * 8 + 3))
+
+
+def test_bin_centre_values_signed_zero_and_top_bin():
+    # code 8 (-0) -> -0.0; code 7 (6) -> 6 * s; code 0xF -> -6 * s
+    x = np.zeros((1, 32), np.float32)
+    x[0, 0] = 6.5          # a = 6.5 -> clipped, code 7, scale 1 (amax 6.5 -> 2^0)
+    x[0, 1] = -0.125       # a = 0.125 -> code 8
+    x[0, 2] = -5.5         # code 0xF
+    q = oracle.fake_quant(bf(x), "mx")
+    v = oracle.bin_centre_values(q["codes"], q["scales"], q["outer"], "mx", (1, 32))
+    assert v[0, :3].tolist() == [6.0, 0.0, -6.0]
+    assert np.signbit(v[0, 1])
 
 
 def test_selection_finds_the_generated_outlier_channels():
