@@ -34,7 +34,7 @@ EXPORTED = (
     "fq_select_channels", "fq_fake_quant_retain", "fq_fake_quant_rht",
     "fq_qlinear_workspace_size", "fq_qlinear_fwd", "fq_hadamard",
     "fq_qlinear_bwd_workspace_size", "fq_qlinear_bwd", "fq_status_string",
-    "fq_last_error", "fq_version",
+    "fq_last_error", "fq_version", "fq_fake_quant_noalloc",
 )
 
 
@@ -87,6 +87,8 @@ def lib() -> ctypes.CDLL:
         L.fq_dequantize.restype = ctypes.c_int
         L.fq_fake_quant.argtypes = [dp, vp, i64, i64, vp, vp, vp, vp, vp, sz, vp]
         L.fq_fake_quant.restype = ctypes.c_int
+        L.fq_fake_quant_noalloc.argtypes = [dp, vp, i64, i64, vp, vp, vp, vp, vp]
+        L.fq_fake_quant_noalloc.restype = ctypes.c_int
         L.fq_ste_backward.argtypes = [dp, vp, vp, vp, vp, i64, i64, vp, vp]
         L.fq_fake_quant_mask.restype = ctypes.c_int
         L.fq_fake_quant_mask.argtypes = [dp, vp, i64, i64, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -289,6 +291,18 @@ def fq_fake_quant(desc: FqDesc, x, y=None, out: Quantized | None = None, ws=None
     _check(lib().fq_fake_quant(ctypes.byref(desc), _bf16(x, rows, cols, "x"), rows, cols,
                                _bf16(y, rows, cols, "y"), codes, scales, outer,
                                _ptr(ws, nbytes, "ws"), nbytes, _stream(stream)))
+    return y
+
+
+def fq_fake_quant_noalloc(desc: FqDesc, x, y, out: Quantized | None = None, stream=None):
+    """fq_fake_quant with the library's own per-GPU scratch instead of a
+    workspace (the C call allocates nothing; y and out are the caller's).
+    Returns y."""
+    rows, cols = x.shape
+    codes, scales, outer = _qptrs(desc, out, rows, cols)
+    _check(lib().fq_fake_quant_noalloc(ctypes.byref(desc), _bf16(x, rows, cols, "x"), rows, cols,
+                                       _bf16(y, rows, cols, "y"), codes, scales, outer,
+                                       _stream(stream)))
     return y
 
 

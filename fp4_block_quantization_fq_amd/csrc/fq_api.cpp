@@ -10,6 +10,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "fq.h"
 #include "fq_internal.h"
@@ -246,6 +247,69 @@ fq_status fq_fake_quant(const fq_desc *desc, const void *x_bf16, int64_t rows, i
         if (ws_bytes < need)
             return fail(FQ_ERR_WORKSPACE, "workspace %zu bytes < %zu required", ws_bytes, need);
     }
+    return run_quant(f, desc, x_bf16, rows, cols, y_bf16, codes, scales, outer, ws,
+                     (hipStream_t)stream);
+}
+
+}  // extern "C"
+
+// ---- the entry point that allocates nothing --------------------------------
+// The per-tensor maximum's partials live in this library-owned device array
+// instead of a caller workspace.  Each GPU holds its own copy (allocated with
+// the code object, kept until the process ends); its address on a device is
+// looked up once, with that device current, and only that address is ever
+// handed to kernels.  Nothing in it needs clearing: the maximum pass writes
+// every partial the quantizer then reads.  Calls that overlap on one GPU share
+// it and race.
+namespace {
+
+constexpr size_t kStaticScratchBytes = fqimpl::kAbsmaxPartials * sizeof(uint32_t);   // 4 KB
+static __device__ __align__(256) uint32_t scratch[fqimpl::kAbsmaxPartials];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];          // per device, null until looked up
+
+fq_status device_scratch(void **out)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return device_status(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(FQ_ERR_DEVICE, "device %d beyond the %d this library tracks", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) return device_status(e, "scratch symbol lookup");
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return FQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+fq_status fq_fake_quant_noalloc(const fq_desc *desc, const void *x_bf16, int64_t rows,
+                                int64_t cols, void *y_bf16, void *codes, void *scales,
+                                float *outer, void *stream)
+{
+    Fmt f;
+    FQ_TRY(check_desc(desc, &f, "desc"));
+    FQ_TRY(check_shape(f, desc->axis, rows, cols));
+    FQ_TRY(check_ptr(x_bf16, "x", true));
+    FQ_TRY(check_ptr(y_bf16, "y", true));
+    FQ_TRY(check_ptr(codes, "codes", false));
+    FQ_TRY(check_ptr(scales, "scales", false));
+    FQ_TRY(check_ptr(outer, "outer", false, 4));
+    const size_t need = quant_ws(f);
+    if (need > kStaticScratchBytes)
+        return fail(FQ_ERR_WORKSPACE, "needs %zu bytes of scratch, the static array holds %zu",
+                    need, kStaticScratchBytes);
+    void *ws = nullptr;
+    if (need) FQ_TRY(device_scratch(&ws));
     return run_quant(f, desc, x_bf16, rows, cols, y_bf16, codes, scales, outer, ws,
                      (hipStream_t)stream);
 }

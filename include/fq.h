@@ -170,6 +170,20 @@ fq_status fq_ste_backward(const fq_desc *desc, const void *x_bf16,
                           const void *dy_bf16, int64_t rows, int64_t cols,
                           void *dx_bf16, void *stream);
 
+/* fq_fake_quant for callers that cannot allocate or pass a workspace (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same computation and outputs, with the per-tensor
+ * maximum's partials (the only scratch any format needs, at most 4096 bytes
+ * whatever the shape) in a 4 KB device array the library owns, one per GPU,
+ * instead of ws.  The call allocates nothing.  Calls on one GPU share that
+ * array: calls that overlap on one GPU (different streams, or different
+ * threads) race and must be serialized by the caller.  Arguments and errors
+ * otherwise as fq_fake_quant; FQ_ERR_DEVICE if the array's address cannot be
+ * looked up on the current device. */
+fq_status fq_fake_quant_noalloc(const fq_desc *desc, const void *x_bf16, int64_t rows,
+                                int64_t cols, void *y_bf16, void *codes, void *scales,
+                                float *outer, void *stream);
+
 /* Fake quantization that also writes the STE keep mask: as fq_fake_quant,
  * plus keep [rows, cols / 8] uint8 in the layout of x (row-major, whatever
  * desc->axis is): bit (c mod 8) of byte (r, c / 8) is 1 where element (r, c)
