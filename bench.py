@@ -117,6 +117,179 @@ def warm(fn, torch, seconds=WARM_SECONDS):
         torch.cuda.synchronize()
 
 
+CONFIG_TARGET_US = {"cfg1_mx_rne_1024x4096": 3.39, "cfg2_nvt_rne_2880x2880": 6.76,
+                    "cfg4b_nvt_sr_col_4096x4096": 7.68, "cfg4c_mx_sr_col_4096x4096": 7.58}
+
+
+def time_configs(fq, wl, torch, np, dev, to_dev):
+    """The small configurations at their own shapes: one op per call, each call
+    on its own buffer set, with enough sets (over 512 MB in all) that no call
+    finds its operands in the 256 MB Infinity Cache.  One HIP graph holds one
+    call per set and is replayed; the time per call includes the gaps between
+    back-to-back kernels.  Bytes: input read once plus every output (and the
+    per-tensor maximum pass's second read of x charged, not counted)."""
+    cfgs = [
+        ("cfg1_mx_rne_1024x4096", wl.mx_activation(), fq.fq_desc_mxfp4(), "fake_quant"),
+        ("cfg2_nvt_rne_2880x2880", wl.nv_weight(), fq.fq_desc_nvfp4(), "fake_quant"),
+        ("cfg4b_nvt_sr_col_4096x4096", wl.backward_weight(),
+         fq.fq_desc_nvfp4(rounding=fq.FQ_ROUND_SR, axis=fq.FQ_AXIS_COL, seed=1234), "quantize"),
+        ("cfg4c_mx_sr_col_4096x4096", wl.backward_weight(),
+         fq.fq_desc_mxfp4(rounding=fq.FQ_ROUND_SR, axis=fq.FQ_AXIS_COL, seed=1235), "quantize"),
+    ]
+    res = {}
+    for name, xb, d, kind in cfgs:
+        R, C = xb.shape
+        n = R * C
+        nouter = 0 if d.outer == fq.FQ_OUTER_NONE else 4
+        by = (2 * n + n // 2 + n // d.block_size + nouter + (2 * n if kind == "fake_quant" else 0))
+        nsets = max(2, (512 << 20) // by + 2)
+        xs = [to_dev(xb) for _ in range(nsets)]
+        ys = [torch.empty_like(xs[0]) for _ in range(nsets)] if kind == "fake_quant" else None
+        outs = [fq.alloc_outputs(d, R, C, dev) for _ in range(nsets)]
+        ws = torch.empty((4096,), dtype=torch.uint8, device=dev)
+
+        def call(i):
+            if kind == "fake_quant":
+                fq.fq_fake_quant(d, xs[i], y=ys[i], out=outs[i], ws=ws)
+            else:
+                fq.fq_quantize(d, xs[i], out=outs[i], ws=ws)
+        for i in range(nsets):
+            call(i)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        with torch.cuda.graph(g, stream=cap):
+            for i in range(nsets):
+                call(i)
+        for _ in range(3):
+            g.replay()
+        torch.cuda.synchronize()
+        reps = 10
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / (reps * nsets)
+        gbs = by / (us * 1e-6) / 1e9
+        res[name] = {"us": round(us, 3), "bytes": by, "GBps": round(gbs, 1),
+                     "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
+                     "target_us": CONFIG_TARGET_US[name], "buffer_sets": nsets,
+                     "op": kind}
+        del xs, ys, outs, g
+    return res
+
+
+def kernel_split(torch, fn, calls):
+    """Average kernel durations (us per call) of `calls` calls made by fn,
+    grouped as 'gemm' (the matrix-core product) and the rest by kernel name,
+    from torch's profiler (device-side timestamps)."""
+    try:
+        from torch.profiler import ProfilerActivity, profile
+        with profile(activities=[ProfilerActivity.CUDA]) as prof:
+            fn()
+            torch.cuda.synchronize()
+        tot = {}
+        for ev in prof.key_averages():
+            dev_us = getattr(ev, "device_time_total", None)
+            if dev_us is None:
+                dev_us = getattr(ev, "cuda_time_total", 0.0)
+            if not dev_us:
+                continue
+            key = ev.key
+            if "k_gemm" in key:
+                name = "gemm"
+            elif "k_absmax" in key:
+                name = "absmax"
+            elif "k_quant_col" in key:
+                name = "quant_col_w"
+            elif "k_quant_row" in key:
+                name = "quant_row_x"
+            else:
+                continue
+            tot[name] = tot.get(name, 0.0) + dev_us / calls
+        return {k: round(v, 2) for k, v in tot.items()} or None
+    except Exception as e:  # the profiler is an optional diagnostic
+        log(f"bench: kernel split unavailable ({e})")
+        return None
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_configs(oracle, wl, np):
+    """The oracle on every configuration at its full size (wall clock), a
+    single-thread run of configuration 1, and configuration 5 as the oracle's
+    two fake quantizations plus numpy's FP32 matmul (BLAS threads recorded)."""
+    out = {}
+
+    def timed(fn):
+        t = time.perf_counter()
+        fn()
+        return time.perf_counter() - t
+
+    def entry(by, dt, threads):
+        return {"seconds": round(dt, 3), "GBps": round(by / dt / 1e9, 4), "threads": threads}
+
+    nt = oracle.default_threads()
+    x1 = wl.mx_activation()
+    n1 = x1.size
+    b1 = 2 * n1 + 2 * n1 + n1 // 2 + n1 // 32
+    out["cfg1"] = entry(b1, timed(lambda: oracle.fake_quant(x1, "mx", "rne")), nt)
+    out["cfg1_single_thread"] = entry(b1, timed(lambda: oracle.fake_quant(x1, "mx", "rne",
+                                                                          nthreads=1)), 1)
+    x2 = wl.nv_weight()
+    n2 = x2.size
+    out["cfg2"] = entry(4 * n2 + n2 // 2 + n2 // 16 + 4,
+                        timed(lambda: oracle.fake_quant(x2, "nv_tensor", "rne")), nt)
+    x3 = wl.nv_activation()
+    n3 = x3.size
+    b3 = 4 * n3 + n3 // 2 + n3 // 16 + 4 * (n3 // 128)
+    out["cfg3_rne"] = entry(b3, timed(lambda: oracle.fake_quant(x3, "nv_128", "rne")), nt)
+    out["cfg3_sr"] = entry(b3, timed(lambda: oracle.fake_quant(x3, "nv_128", "sr", seed=1234)), nt)
+    f3 = oracle.fake_quant(x3, "nv_128", "rne")
+    dy = wl.grad_output()
+    out["cfg4a_ste"] = entry(6 * n3 + n3 // 16 + 4 * (n3 // 128),
+                             timed(lambda: oracle.ste_backward(x3, f3["scales"], f3["outer"], dy,
+                                                               "nv_128")), nt)
+    del x3, f3, dy
+    w4 = wl.backward_weight()
+    n4 = w4.size
+    out["cfg4b"] = entry(2 * n4 + n4 // 2 + n4 // 16 + 4,
+                         timed(lambda: oracle.fake_quant(w4, "nv_tensor", "sr", "col", 1234)), nt)
+    out["cfg4c"] = entry(2 * n4 + n4 // 2 + n4 // 32,
+                         timed(lambda: oracle.fake_quant(w4, "mx", "sr", "col", 1235)), nt)
+    xm, wm = wl.linear_inputs()
+    t = time.perf_counter()
+    fx = oracle.fake_quant(xm, "nv_tensor", "rne", "row")
+    fw = oracle.fake_quant(wm, "nv_tensor", "rne", "col")
+    a = oracle.bf16_bits_to_f64(fx["y"]).astype(np.float32)
+    b = oracle.bf16_bits_to_f64(fw["y"]).astype(np.float32)
+    tq = time.perf_counter() - t
+    t = time.perf_counter()
+    a @ b
+    tm = time.perf_counter() - t
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [i.get("num_threads") for i in threadpool_info() if i.get("user_api") == "blas"]
+    except Exception:
+        blas = []
+    fl = 2.0 * xm.shape[0] * xm.shape[1] * wm.shape[1]
+    out["cfg5"] = {"seconds_fake_quant": round(tq, 3), "seconds_matmul_fp32": round(tm, 3),
+                   "TFLOPs": round(fl / (tq + tm) / 1e12, 4), "threads": nt,
+                   "blas_threads": blas[0] if blas else None}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -277,6 +450,12 @@ def main():
     copy = {"op": "torch copy_ of 16384x4096 bf16", "bytes": 4 * n, "ms": round(copy_ms, 5),
             "GBps": round(4 * n / (copy_ms * 1e-3) / 1e9, 1)}
 
+    # ---------------- the configurations at their own shapes ----------------
+    per_config = None
+    if not args.only:
+        log("bench: per-config timings")
+        per_config = time_configs(fq, wl, torch, np, dev, to_dev)
+
     # ---------------- QAT linear ----------------
     qlin = None
     if not args.only:
@@ -298,10 +477,34 @@ def main():
         qms = e0.elapsed_time(e1) / args.qlinear_iters
         flops = 2.0 * M * Kd * N
         tf = flops / (qms * 1e-3) / 1e12
+        # cold operands: three independent (X, W, workspace, Y) sets in turn,
+        # 0.76 GB in all, so no call finds its operands in the Infinity Cache
+        sets = [(to_dev(xm), to_dev(wm), fq.qlinear_workspace(dxd, dwd, M, Kd, N, dev),
+                 torch.empty((M, N), dtype=torch.bfloat16, device=dev)) for _ in range(3)]
+        run_cold = lambda i: fq.fq_qlinear_fwd(dxd, dwd, sets[i % 3][0], sets[i % 3][1],
+                                               y=sets[i % 3][3], ws=sets[i % 3][2])
+        warm(lambda: [run_cold(i) for i in range(3)], torch)
+        e0.record()
+        for i in range(args.qlinear_iters):
+            run_cold(i)
+        e1.record()
+        torch.cuda.synchronize()
+        cms = e0.elapsed_time(e1) / args.qlinear_iters
+        split = kernel_split(torch, lambda: [run_cold(i) for i in range(6)], 6)
         qlin = {"workload": "X 8192x2880 N(0,1) @ W 2880x5760 N(0,0.02^2), NVFP4 RNE both",
                 "ms": round(qms, 4), "TFLOPs": round(tf, 1),
+                "ms_cold": round(cms, 4),
+                "TFLOPs_cold": round(flops / (cms * 1e-3) / 1e12, 1),
+                "kernels_us": split,
                 "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": BF16_PEAK_TFLOPS,
-                             "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4)}}
+                             "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4),
+                             "frac_cold": round(flops / (cms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}}
+        if split and "gemm" in split:
+            gtf = flops / (split["gemm"] * 1e-6) / 1e12
+            qlin["gemm_only"] = {"us": split["gemm"], "TFLOPs": round(gtf, 1),
+                                 "frac": round(gtf / BF16_PEAK_TFLOPS, 4)}
+            qlin["prologue_us"] = round(sum(v for k, v in split.items() if k != "gemm"), 2)
+        del sets
 
     # ---------------- the same linear with MXFP4 operands (FP4 matrix cores) ----------------
     qmx = None
@@ -486,7 +689,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline and not args.only:
         import oracle
-        log(f"bench: cpu oracle on {args.cpu_rows} rows")
+        log(f"bench: cpu oracle on {args.cpu_rows} rows and on each configuration")
         r = args.cpu_rows
         xs_c = np.ascontiguousarray(x_bits[:r])
         dy_c = np.ascontiguousarray(dy_bits[:r])
@@ -506,7 +709,8 @@ def main():
         cpu = {"value": round(cbytes / dt / 1e9, 4), "unit": "GB/s", "cores": nthreads,
                "kind": "oracle", "seconds": round(dt, 2),
                "sample": f"the same 8-op step on the first {r} of {ROWS} rows "
-                         f"({nc} elements per op)"}
+                         f"({nc} elements per op)",
+               "cpu_model": cpu_model(), "per_config": cpu_configs(oracle, wl, np)}
 
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
@@ -522,6 +726,7 @@ def main():
         "copy_yardstick": copy,
         "cpu_baseline": cpu,
         "kernels": kernels,
+        "per_config": per_config,
         "qlinear": qlin,
         "qlinear_mxfp4": qmx,
         "qlinear_bwd": qbwd,

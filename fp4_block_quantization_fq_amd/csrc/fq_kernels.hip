@@ -233,7 +233,12 @@ __global__ __launch_bounds__(kThreads) void k_quant_row(
         ot = tensor_scale<kThreads>(partials, npart);
         if (outer && blockIdx.x == 0 && threadIdx.x == 0) outer[0] = ot.s;
     }
-    for (uint32_t u = blockIdx.x * kThreads + threadIdx.x; u < nunits;
+    // The per-tensor format reads x a second time right after the maximum
+    // pass: its workgroups walk the tensor from the end, so the first ones
+    // find the part of x the maximum pass read last still in the Infinity
+    // Cache, before this pass's own traffic displaces it.
+    const uint32_t wg = (FMT == FMT_NVT) ? gridDim.x - 1 - blockIdx.x : blockIdx.x;
+    for (uint32_t u = wg * kThreads + threadIdx.x; u < nunits;
          u += gridDim.x * kThreads) {
         if (MAP == 1) {
             const uint4 v = ld_stream<NT>(&x[u]);
@@ -313,8 +318,11 @@ __global__ __launch_bounds__(kQcThreads) void k_quant_col(
     }
     const uint32_t lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const uint32_t tiles_c = (C + kQcCols - 1) / kQcCols;
-    const uint32_t tc0 = (blockIdx.x % tiles_c) * kQcCols;
-    const uint32_t tr0 = (blockIdx.x / tiles_c) * kQcRows;
+    // per-tensor format: tiles in reverse order, as in k_quant_row (x was
+    // just read by the maximum pass)
+    const uint32_t tile = (FMT == FMT_NVT) ? gridDim.x - 1 - blockIdx.x : blockIdx.x;
+    const uint32_t tc0 = (tile % tiles_c) * kQcCols;
+    const uint32_t tr0 = (tile / tiles_c) * kQcRows;
     const uint32_t ldx = C >> 3;                     // 16-byte chunks per row
     // Waves issuing loads or stores run at a raised priority, so that on a CU
     // shared by several tiles the memory phases go ahead of the arithmetic
