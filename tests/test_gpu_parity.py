@@ -254,6 +254,32 @@ def test_workload_qlinear_mxfp4():
     assert err < 4e-3
 
 
+@pytest.mark.parametrize("fmts", [("nv_tensor", "nv_tensor"), ("nv_128", "nv_128"),
+                                  ("nv_tensor", "nv_128"), ("mx", "mx")])
+def test_qlinear_identity_operand_gives_the_other_operand(fmts):
+    """With W = I (K = N) the product is X_hat itself, and with X = I (M = K)
+    it is W_hat: the quantized identity is the identity (each column's single
+    1 is its block maximum and comes back as 1), every output element is one
+    exact product, and a BF16 value survives the FP32 accumulator and the
+    BF16 store unchanged.  So every element of the product equals the
+    oracle's X_hat / W_hat bit for bit (a -0 comes out as +0: the
+    accumulator starts at +0)."""
+    fx, fw = fmts
+    K = 384
+    eye = wl.f32_to_bf16_bits(np.eye(K, dtype=np.float32))
+    assert np.array_equal(oracle.fake_quant(eye, fw, "rne", "col")["y"], eye)
+    assert np.array_equal(oracle.fake_quant(eye, fx, "rne", "row")["y"], eye)
+    x = wl.activation_with_outlier_channels((640, K), 1.0, 4, 100.0, 71)
+    w = wl.weight_with_outlier_entries((K, 520), 0.02, 1e-3, 50.0, 72)
+    dx, dw = make_desc(fx, "rne", "row"), make_desc(fw, "rne", "col")
+    yx = fq.fq_qlinear_fwd(dx, dw, to_dev(x), to_dev(eye))
+    yw = fq.fq_qlinear_fwd(dx, dw, to_dev(eye), to_dev(w))
+    torch.cuda.synchronize()
+    plus0 = lambda b: np.where(b == 0x8000, np.uint16(0), b)
+    assert np.array_equal(plus0(to_bits(yx)), plus0(oracle.fake_quant(x, fx, "rne", "row")["y"]))
+    assert np.array_equal(plus0(to_bits(yw)), plus0(oracle.fake_quant(w, fw, "rne", "col")["y"]))
+
+
 @pytest.mark.parametrize("fmt", ["nv_tensor", "mx"])
 def test_qlinear_repeat_runs_identical(fmt):
     """Two runs of the full-size linear give the same bits (the GEMMs' LDS
