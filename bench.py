@@ -606,12 +606,12 @@ def main():
         retain, cscale = fq.fq_select_channels(amax, kret)
         ret_outs = [fq.alloc_outputs(d_nv128, ROWS, COLS, dev) for _ in range(NBUF)]
         for i in range(NBUF):
-            fq.fq_fake_quant_retain(d_nv128, xs[i], retain, cscale, y=ys[i], out=ret_outs[i])
+            fq.fq_fake_quant_retain(d_nv128, xs[i], retain, cscale, y=ys[i], out=ret_outs[i], ws=ws)
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for s in range(K):
-            fq.fq_fake_quant_retain(d_nv128, xs[s % NBUF], retain, cscale, y=ys[s % NBUF],
+            fq.fq_fake_quant_retain(d_nv128, xs[s % NBUF], retain, cscale, y=ys[s % NBUF], ws=ws,
                                     out=ret_outs[s % NBUF])
         e1.record()
         torch.cuda.synchronize()

@@ -34,7 +34,8 @@ EXPORTED = (
     "fq_select_channels", "fq_fake_quant_retain", "fq_fake_quant_rht",
     "fq_qlinear_workspace_size", "fq_qlinear_fwd", "fq_hadamard",
     "fq_qlinear_bwd_workspace_size", "fq_qlinear_bwd", "fq_status_string",
-    "fq_last_error", "fq_version", "fq_fake_quant_noalloc",
+    "fq_last_error", "fq_version", "fq_fake_quant_noalloc", "fq_qlinear_fwd_retain",
+    "fq_qlinear_bwd_retain",
 )
 
 
@@ -103,7 +104,7 @@ def lib() -> ctypes.CDLL:
         L.fq_channel_absmax.restype = ctypes.c_int
         L.fq_select_channels.argtypes = [vp, i64, i64, vp, vp, vp]
         L.fq_select_channels.restype = ctypes.c_int
-        L.fq_fake_quant_retain.argtypes = [dp, vp, i64, i64, vp, vp, vp, vp, vp, vp, vp]
+        L.fq_fake_quant_retain.argtypes = [dp, vp, i64, i64, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.fq_fake_quant_retain.restype = ctypes.c_int
         L.fq_fake_quant_rht.argtypes = [dp, vp, i64, i64, ctypes.c_int32, ctypes.c_uint64, vp, vp,
                                         vp, vp, vp]
@@ -122,6 +123,12 @@ def lib() -> ctypes.CDLL:
         L.fq_qlinear_bwd.argtypes = [dp, dp, dp, i32, u64, vp, vp, vp, i64, i64, i64, vp, vp, vp,
                                      sz, vp]
         L.fq_qlinear_bwd.restype = ctypes.c_int
+        L.fq_qlinear_fwd_retain.argtypes = [dp, dp, vp, vp, i64, i64, i64, vp, vp, vp, vp, sz,
+                                            vp]
+        L.fq_qlinear_fwd_retain.restype = ctypes.c_int
+        L.fq_qlinear_bwd_retain.argtypes = [dp, dp, dp, vp, vp, vp, i64, i64, i64, vp, vp, vp, vp,
+                                            vp, sz, vp]
+        L.fq_qlinear_bwd_retain.restype = ctypes.c_int
         L.fq_status_string.argtypes = [ctypes.c_int]
         L.fq_status_string.restype = ctypes.c_char_p
         L.fq_last_error.argtypes = []
@@ -407,18 +414,23 @@ def fq_select_channels(amax, k: int, stream=None):
 
 
 def fq_fake_quant_retain(desc: FqDesc, x, retain, chan_scale, y=None,
-                         out: Quantized | None = None, stream=None):
-    """Row fake quantization with FP8 retained channels.  Returns y."""
+                         out: Quantized | None = None, ws=None, stream=None):
+    """Fake quantization (either axis, any format) with the retained channels
+    (columns of x) in FP8.  Returns y."""
     torch = _torch()
     rows, cols = x.shape
     if y is None:
         y = torch.empty_like(x)
+    if ws is None:
+        ws, nbytes = workspace(desc, rows, cols, x.device)
+    else:
+        nbytes = ws.numel() * ws.element_size()
     codes, scales, outer = _qptrs(desc, out, rows, cols)
     _check(lib().fq_fake_quant_retain(ctypes.byref(desc), _bf16(x, rows, cols, "x"), rows, cols,
                                       _bf16(y, rows, cols, "y"), codes, scales, outer,
                                       _ptr(retain, cols // 8, "retain"),
                                       _ptr(chan_scale, 4 * cols, "chan_scale", elem=4),
-                                      _stream(stream)))
+                                      _ptr(ws, nbytes, "ws"), nbytes, _stream(stream)))
     return y
 
 
@@ -531,6 +543,53 @@ def fq_qlinear_bwd(desc_x: FqDesc, desc_w: FqDesc, desc_g: FqDesc, x, w, dy, dx=
                                 _bf16(dy, M, N, "dy"), M, K, N, _bf16(dx, M, K, "dx"),
                                 _bf16(dw, K, N, "dw"), _ptr(ws, None, "ws", elem=1), ws.numel(),
                                 _stream(stream)))
+    return dx, dw
+
+
+def fq_qlinear_fwd_retain(desc_x: FqDesc, desc_w: FqDesc, x, w, retain, chan_scale, y=None,
+                          ws=None, stream=None):
+    """Y = FQ(X) @ FQ(W) with X's retained channels (retain [K/8], chan_scale
+    [K]) in FP8."""
+    torch = _torch()
+    M, K = x.shape
+    K2, N = w.shape
+    if K2 != K:
+        raise ValueError(f"inner dimensions differ: {x.shape} @ {w.shape}")
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    if ws is None:
+        ws = qlinear_workspace(desc_x, desc_w, M, K, N, x.device)
+    _check(lib().fq_qlinear_fwd_retain(ctypes.byref(desc_x), ctypes.byref(desc_w),
+                                       _bf16(x, M, K, "x"), _bf16(w, K, N, "w"), M, K, N,
+                                       _ptr(retain, K // 8, "retain"),
+                                       _ptr(chan_scale, 4 * K, "chan_scale", elem=4),
+                                       _bf16(y, M, N, "y"), _ptr(ws, None, "ws", elem=1),
+                                       ws.numel(), _stream(stream)))
+    return y
+
+
+def fq_qlinear_bwd_retain(desc_x: FqDesc, desc_w: FqDesc, desc_g: FqDesc, x, w, dy, retain,
+                          chan_scale, dx=None, dw=None, ws=None, stream=None):
+    """(dX, dW) of the linear with X's retained channels in FP8 in the forward
+    and the backward."""
+    torch = _torch()
+    M, K = x.shape
+    K2, N = w.shape
+    if K2 != K or tuple(dy.shape) != (M, N):
+        raise ValueError(f"shapes differ: x {tuple(x.shape)}, w {tuple(w.shape)}, dy {tuple(dy.shape)}")
+    if dx is None:
+        dx = torch.empty((M, K), dtype=torch.bfloat16, device=x.device)
+    if dw is None:
+        dw = torch.empty((K, N), dtype=torch.bfloat16, device=x.device)
+    if ws is None:
+        ws = qlinear_bwd_workspace(desc_x, desc_w, desc_g, M, K, N, x.device, 0)
+    _check(lib().fq_qlinear_bwd_retain(ctypes.byref(desc_x), ctypes.byref(desc_w),
+                                       ctypes.byref(desc_g), _bf16(x, M, K, "x"),
+                                       _bf16(w, K, N, "w"), _bf16(dy, M, N, "dy"), M, K, N,
+                                       _ptr(retain, K // 8, "retain"),
+                                       _ptr(chan_scale, 4 * K, "chan_scale", elem=4),
+                                       _bf16(dx, M, K, "dx"), _bf16(dw, K, N, "dw"),
+                                       _ptr(ws, None, "ws", elem=1), ws.numel(), _stream(stream)))
     return dx, dw
 
 

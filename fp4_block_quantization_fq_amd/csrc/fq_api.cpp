@@ -429,9 +429,67 @@ size_t fq_qlinear_workspace_size(const fq_desc *desc_x, const fq_desc *desc_w, i
            2 * fqimpl::kAbsmaxPartials * sizeof(uint32_t);
 }
 
-fq_status fq_qlinear_fwd(const fq_desc *desc_x, const fq_desc *desc_w, const void *x_bf16,
-                         const void *w_bf16, int64_t M, int64_t K, int64_t N, void *y_bf16,
-                         void *ws, size_t ws_bytes, void *stream)
+// Retained-channel fake quantization along either axis (shared by
+// fq_fake_quant_retain and the linear's retained paths): the per-tensor
+// format's maximum pass leaves the retained columns out.
+static fq_status run_quant_retain(const Fmt &f, const fq_desc *d, uint64_t seed, const void *x,
+                                  int64_t R, int64_t C, void *y, void *yt, void *codes,
+                                  void *scales, float *outer, void *keep, const void *retain,
+                                  const float *chan_scale, uint32_t *parts, hipStream_t st,
+                                  bool cached)
+{
+    uint32_t npart = 0;
+    if (f.fmt == fqimpl::FMT_NVT) {
+        hipError_t e = fqimpl::launch_absmax(x, R * C, parts, &npart, st, retain, C);
+        if (e != hipSuccess) return device_status(e, "masked tensor absmax launch");
+    }
+    if (d->axis == FQ_AXIS_ROW) {
+        fqimpl::RetainArgs a;
+        a.fmt = f.fmt;
+        a.sr = d->rounding == FQ_ROUND_SR;
+        a.seed = seed;
+        a.x = x;
+        a.R = R;
+        a.C = C;
+        a.retain = retain;
+        a.chan_scale = chan_scale;
+        a.y = y;
+        a.codes = codes;
+        a.scales = scales;
+        a.outer = f.fmt == fqimpl::FMT_MX ? nullptr : outer;
+        a.keep = keep;
+        a.partials = parts;
+        a.npart = npart;
+        a.cached_outputs = cached;
+        return device_status(fqimpl::launch_quant_retain(a, st), "retain quantize launch");
+    }
+    fqimpl::QuantArgs a;
+    a.fmt = f.fmt;
+    a.sr = d->rounding == FQ_ROUND_SR;
+    a.col = 1;
+    a.seed = seed;
+    a.x = x;
+    a.R = R;
+    a.C = C;
+    a.y = y;
+    a.yt = yt;
+    a.codes = codes;
+    a.scales = scales;
+    a.outer = f.fmt == fqimpl::FMT_MX ? nullptr : outer;
+    a.keep = keep;
+    a.partials = parts;
+    a.cached_outputs = cached;
+    a.retain = retain;
+    a.chan_scale = chan_scale;
+    return device_status(fqimpl::launch_quant(a, npart, st), "retain quantize launch");
+}
+
+// The forward; retain / chan_scale (or null) keep the activation's retained
+// channels (columns of X) in FP8.
+static fq_status qlinear_fwd_impl(const fq_desc *desc_x, const fq_desc *desc_w,
+                                  const void *x_bf16, const void *w_bf16, int64_t M, int64_t K,
+                                  int64_t N, void *y_bf16, void *ws, size_t ws_bytes,
+                                  void *stream, const void *retain, const float *chan_scale)
 {
     Fmt fx, fw;
     FQ_TRY(check_desc(desc_x, &fx, "desc_x"));
@@ -461,7 +519,11 @@ fq_status fq_qlinear_fwd(const fq_desc *desc_x, const fq_desc *desc_w, const voi
     hipStream_t st = (hipStream_t)stream;
     uint32_t *parts = (uint32_t *)(base + round256((size_t)M * K * 2) + round256((size_t)N * K * 2));
 
-    if (fx.fmt == fqimpl::FMT_MX && fw.fmt == fqimpl::FMT_MX && K % 64 == 0) {
+    if (retain) {
+        FQ_TRY(check_ptr(retain, "retain", true, 1));
+        FQ_TRY(check_ptr(chan_scale, "chan_scale", true));
+    }
+    if (fx.fmt == fqimpl::FMT_MX && fw.fmt == fqimpl::FMT_MX && K % 64 == 0 && !retain) {
         // MXFP4 x MXFP4: the codes and E8M0 scales go straight to the scaled
         // FP4 matrix cores, nothing is dequantized
         const MxLinLayout L = mx_lin_layout(M, K, N);
@@ -499,9 +561,13 @@ fq_status fq_qlinear_fwd(const fq_desc *desc_x, const fq_desc *desc_w, const voi
     void *xhat = base;
     char *what_t = base + round256((size_t)M * K * 2);
 
-    // X_hat = FQ(X) along K (rows of X)
-    FQ_TRY(run_quant(fx, desc_x, x_bf16, M, K, xhat, nullptr, nullptr, nullptr, parts, st,
-                     /*cached=*/true));
+    // X_hat = FQ(X) along K (rows of X), the retained channels in FP8
+    if (retain)
+        FQ_TRY(run_quant_retain(fx, desc_x, desc_x->seed, x_bf16, M, K, xhat, nullptr, nullptr,
+                                nullptr, nullptr, nullptr, retain, chan_scale, parts, st, true));
+    else
+        FQ_TRY(run_quant(fx, desc_x, x_bf16, M, K, xhat, nullptr, nullptr, nullptr, parts, st,
+                         /*cached=*/true));
     // W_hat^T: FQ(W) along K (columns of W), written transposed [N, K]
     {
         fqimpl::QuantArgs a;
@@ -529,6 +595,26 @@ fq_status fq_qlinear_fwd(const fq_desc *desc_x, const fq_desc *desc_w, const voi
     }
     return device_status(fqimpl::launch_gemm_bf16_nt(xhat, what_t, y_bf16, M, N, K, st),
                          "gemm launch");
+}
+
+fq_status fq_qlinear_fwd(const fq_desc *desc_x, const fq_desc *desc_w, const void *x_bf16,
+                         const void *w_bf16, int64_t M, int64_t K, int64_t N, void *y_bf16,
+                         void *ws, size_t ws_bytes, void *stream)
+{
+    return qlinear_fwd_impl(desc_x, desc_w, x_bf16, w_bf16, M, K, N, y_bf16, ws, ws_bytes,
+                            stream, nullptr, nullptr);
+}
+
+fq_status fq_qlinear_fwd_retain(const fq_desc *desc_x, const fq_desc *desc_w, const void *x_bf16,
+                                const void *w_bf16, int64_t M, int64_t K, int64_t N,
+                                const void *retain, const float *chan_scale, void *y_bf16,
+                                void *ws, size_t ws_bytes, void *stream)
+{
+    if (!retain) return fail(FQ_ERR_NULL, "retain is NULL");
+    if (!chan_scale) return fail(FQ_ERR_NULL, "chan_scale is NULL");
+    if (K % 8 != 0) return fail(FQ_ERR_SHAPE, "K=%lld must be a multiple of 8", (long long)K);
+    return qlinear_fwd_impl(desc_x, desc_w, x_bf16, w_bf16, M, K, N, y_bf16, ws, ws_bytes,
+                            stream, retain, chan_scale);
 }
 
 // qlinear backward workspace regions, in order (each rounded up to 256 B).
@@ -648,10 +734,15 @@ static fq_status bwd_quant(const Fmt &f, const fq_desc *d, uint64_t seed, bool c
     return device_status(fqimpl::launch_quant(a, npart, st), "quantize launch");
 }
 
-fq_status fq_qlinear_bwd(const fq_desc *desc_x, const fq_desc *desc_w, const fq_desc *desc_g,
-                         int32_t rht_block, uint64_t rht_seed, const void *x_bf16,
-                         const void *w_bf16, const void *dy_bf16, int64_t M, int64_t K, int64_t N,
-                         void *dx_bf16, void *dw_bf16, void *ws, size_t ws_bytes, void *stream)
+// The backward; retain / chan_scale (or null): the activation's retained
+// channels stay FP8 in X_hat and in X_hat's quantization along M, and their
+// STE keep bits follow the FP8 test.
+static fq_status qlinear_bwd_impl(const fq_desc *desc_x, const fq_desc *desc_w,
+                                  const fq_desc *desc_g, int32_t rht_block, uint64_t rht_seed,
+                                  const void *x_bf16, const void *w_bf16, const void *dy_bf16,
+                                  int64_t M, int64_t K, int64_t N, void *dx_bf16, void *dw_bf16,
+                                  void *ws, size_t ws_bytes, void *stream, const void *retain,
+                                  const float *chan_scale)
 {
     Fmt fx, fw, fg;
     FQ_TRY(check_desc(desc_x, &fx, "desc_x"));
@@ -701,8 +792,13 @@ fq_status fq_qlinear_bwd(const fq_desc *desc_x, const fq_desc *desc_w, const fq_
     const uint64_t sg = desc_g->seed;
 
     // the forward's operands and their STE keep masks: X_hat [M, K], W_hat [K, N]
-    FQ_TRY(bwd_quant(fx, desc_x, desc_x->seed, false, x_bf16, M, K, b + L.xhat, nullptr,
-                     nullptr, nullptr, b + L.xkeep, parts, st));
+    if (retain)
+        FQ_TRY(run_quant_retain(fx, desc_x, desc_x->seed, x_bf16, M, K, b + L.xhat, nullptr,
+                                nullptr, nullptr, nullptr, b + L.xkeep, retain, chan_scale, parts,
+                                st, true));
+    else
+        FQ_TRY(bwd_quant(fx, desc_x, desc_x->seed, false, x_bf16, M, K, b + L.xhat, nullptr,
+                         nullptr, nullptr, b + L.xkeep, parts, st));
     FQ_TRY(bwd_quant(fw, desc_w, desc_w->seed, true, w_bf16, K, N, b + L.what, nullptr,
                      nullptr, nullptr, b + L.wkeep, parts, st));
     // the operands before quantization, rotated along each contraction axis
@@ -729,7 +825,7 @@ fq_status fq_qlinear_bwd(const fq_desc *desc_x, const fq_desc *desc_w, const fq_
     const Op ops[4] = {{op_dy_n, M, N, false, L.dyq_n}, {op_w_n, K, N, false, L.wq_n},
                        {op_x_m, M, K, true, L.xq_mt}, {op_dy_m, M, N, true, L.dyq_mt}};
     hipError_t e;
-    if (fg.fmt == fqimpl::FMT_MX) {
+    if (fg.fmt == fqimpl::FMT_MX && !retain) {
         // MXFP4 operands go to the scaled FP4 matrix cores as codes + scales
         // (quantized along the contraction axis, which is what the product
         // needs): [rows, red/2] codes then [rows, red/32] scales
@@ -749,8 +845,18 @@ fq_status fq_qlinear_bwd(const fq_desc *desc_x, const fq_desc *desc_w, const fq_
         e = fqimpl::launch_gemm_mxfp4_nt_pair(o[0], o[1], 2, st);
     } else {
         // BF16 operands: row passes write y, column passes write y transposed
+        // (with retained channels, X_hat along M keeps them in FP8 and the
+        // products run here whatever the gradient format)
         for (int i = 0; i < 4; ++i) {
             const Op &p = ops[i];
+            if (retain && i == 2) {
+                fq_desc dg = *desc_g;
+                dg.axis = FQ_AXIS_COL;
+                FQ_TRY(run_quant_retain(fg, &dg, sg + i, p.src, p.R, p.C, nullptr, b + p.at,
+                                        nullptr, nullptr, nullptr, nullptr, retain, chan_scale,
+                                        parts, st, true));
+                continue;
+            }
             FQ_TRY(bwd_quant(fg, desc_g, sg + i, p.col, p.src, p.R, p.C, p.col ? nullptr : b + p.at,
                              p.col ? b + p.at : nullptr, nullptr, nullptr, nullptr, parts, st,
                              rht_fused ? rht_block : 0, rht_seed));
@@ -760,6 +866,31 @@ fq_status fq_qlinear_bwd(const fq_desc *desc_x, const fq_desc *desc_w, const fq_
                                              b + L.xkeep, b + L.wkeep);
     }
     return device_status(e, "gemm launch");
+}
+
+fq_status fq_qlinear_bwd(const fq_desc *desc_x, const fq_desc *desc_w, const fq_desc *desc_g,
+                         int32_t rht_block, uint64_t rht_seed, const void *x_bf16,
+                         const void *w_bf16, const void *dy_bf16, int64_t M, int64_t K, int64_t N,
+                         void *dx_bf16, void *dw_bf16, void *ws, size_t ws_bytes, void *stream)
+{
+    return qlinear_bwd_impl(desc_x, desc_w, desc_g, rht_block, rht_seed, x_bf16, w_bf16,
+                            dy_bf16, M, K, N, dx_bf16, dw_bf16, ws, ws_bytes, stream, nullptr,
+                            nullptr);
+}
+
+fq_status fq_qlinear_bwd_retain(const fq_desc *desc_x, const fq_desc *desc_w,
+                                const fq_desc *desc_g, const void *x_bf16, const void *w_bf16,
+                                const void *dy_bf16, int64_t M, int64_t K, int64_t N,
+                                const void *retain, const float *chan_scale, void *dx_bf16,
+                                void *dw_bf16, void *ws, size_t ws_bytes, void *stream)
+{
+    if (!retain) return fail(FQ_ERR_NULL, "retain is NULL");
+    if (!chan_scale) return fail(FQ_ERR_NULL, "chan_scale is NULL");
+    FQ_TRY(check_ptr(retain, "retain", true, 1));
+    FQ_TRY(check_ptr(chan_scale, "chan_scale", true));
+    if (K % 8 != 0) return fail(FQ_ERR_SHAPE, "K=%lld must be a multiple of 8", (long long)K);
+    return qlinear_bwd_impl(desc_x, desc_w, desc_g, 0, 0, x_bf16, w_bf16, dy_bf16, M, K, N,
+                            dx_bf16, dw_bf16, ws, ws_bytes, stream, retain, chan_scale);
 }
 
 static fq_status check_osci(const float *w, const void *q, const float *w_prev,
@@ -871,15 +1002,14 @@ fq_status fq_select_channels(const uint32_t *amax, int64_t cols, int64_t k, void
 fq_status fq_fake_quant_retain(const fq_desc *desc, const void *x_bf16, int64_t rows,
                                int64_t cols, void *y_bf16, void *codes, void *scales,
                                float *outer, const void *retain, const float *chan_scale,
-                               void *stream)
+                               void *ws, size_t ws_bytes, void *stream)
 {
     Fmt f;
     FQ_TRY(check_desc(desc, &f, "desc"));
-    if (desc->axis != FQ_AXIS_ROW)
-        return fail(FQ_ERR_DESC, "retained channels need FQ_AXIS_ROW (groups along channels)");
-    if (f.fmt == fqimpl::FMT_NVT)
-        return fail(FQ_ERR_DESC, "retained channels: MXFP4 or NVFP4 with FQ_OUTER_BLOCK128 only");
-    FQ_TRY(check_shape(f, FQ_AXIS_ROW, rows, cols));
+    FQ_TRY(check_shape(f, desc->axis, rows, cols));
+    if (cols % 8 != 0)
+        return fail(FQ_ERR_SHAPE, "cols=%lld must be a multiple of 8 (channel mask bytes)",
+                    (long long)cols);
     FQ_TRY(check_ptr(x_bf16, "x", true));
     FQ_TRY(check_ptr(y_bf16, "y", true));
     FQ_TRY(check_ptr(codes, "codes", false));
@@ -887,21 +1017,15 @@ fq_status fq_fake_quant_retain(const fq_desc *desc, const void *x_bf16, int64_t 
     FQ_TRY(check_ptr(outer, "outer", false, 4));
     FQ_TRY(check_ptr(retain, "retain", true, 1));
     FQ_TRY(check_ptr(chan_scale, "chan_scale", true));
-    fqimpl::RetainArgs a;
-    a.fmt = f.fmt;
-    a.sr = desc->rounding == FQ_ROUND_SR;
-    a.seed = desc->seed;
-    a.x = x_bf16;
-    a.R = rows;
-    a.C = cols;
-    a.retain = retain;
-    a.chan_scale = chan_scale;
-    a.y = y_bf16;
-    a.codes = codes;
-    a.scales = scales;
-    a.outer = f.fmt == fqimpl::FMT_NV128 ? outer : nullptr;
-    return device_status(fqimpl::launch_quant_retain(a, (hipStream_t)stream),
-                         "retain quantize launch");
+    const size_t need = quant_ws(f);
+    if (need) {
+        FQ_TRY(check_ptr(ws, "ws", true));
+        if (ws_bytes < need)
+            return fail(FQ_ERR_WORKSPACE, "workspace %zu bytes < %zu required", ws_bytes, need);
+    }
+    return run_quant_retain(f, desc, desc->seed, x_bf16, rows, cols, y_bf16, nullptr, codes,
+                            scales, outer, nullptr, retain, chan_scale, (uint32_t *)ws,
+                            (hipStream_t)stream, false);
 }
 
 const char *fq_status_string(fq_status s)

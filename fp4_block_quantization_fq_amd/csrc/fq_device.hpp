@@ -545,4 +545,54 @@ __device__ __forceinline__ uint32_t keep_mask(const uint32_t (&xp)[NP], const Bl
     return k;
 }
 
+
+// ---- workgroup maximum and the per-tensor NVFP4 scale ----------------------
+template <int NT>
+__device__ __forceinline__ uint32_t block_reduce_max(uint32_t m, uint32_t *red)
+{
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1)
+        m = max(m, (uint32_t)__shfl_xor((int)m, off));
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+    __syncthreads();
+    m = red[0];
+#pragma unroll
+    for (int w = 1; w < NT / 64; ++w) m = max(m, red[w]);
+    return m;
+}
+
+// NVFP4 per-tensor outer scale from the partial maxima (every thread of a
+// workgroup of NT threads; NT must be the launching workgroup's size, which
+// sizes the per-wave slots of the reduction).
+template <int NT>
+__device__ __forceinline__ OuterScale tensor_scale(const uint32_t *__restrict__ partials,
+                                                   uint32_t npart)
+{
+    static_assert(NT % 64 == 0 && NT <= 1024, "whole waves, at most 16");
+    __shared__ uint32_t red[NT / 64];
+    uint32_t m = 0;
+    for (uint32_t i = threadIdx.x; i < npart; i += NT) m = max(m, partials[i]);
+    m = block_reduce_max<NT>(m, red);
+    return make_outer(as_f(m << 16));
+}
+
+// Halves of a packed BF16 pair word (elements 2w, 2w + 1 of a chunk) whose
+// bit is set in the 8-bit mask r (bit e for element e of the chunk).
+__device__ __forceinline__ uint32_t retained_halves(uint32_t r, int e0)
+{
+    return (((r >> e0) & 1u) ? 0xFFFFu : 0u) | (((r >> (e0 + 1)) & 1u) ? 0xFFFF0000u : 0u);
+}
+
+// FP8 E4M3 fake quantization of one value under its channel scale (held as
+// a BlockScale: s_eff, and the correctly rounded quotient's reciprocal):
+// a = RN(|x| / s), E4M3 nearest-even saturating at 448, value * s, sign kept;
+// a zero scale gives +-0.  *clipped is set when a > 448.
+__device__ __forceinline__ float fp8_fake(float x, const BlockScale &s, bool *clipped)
+{
+    const float a = div_corrected(__builtin_fabsf(x) * s.xs, s.sq, s.rcp);
+    *clipped = a > 448.0f;
+    const float mag = e4m3_value(e4m3_encode_sat(a)) * s.s_eff;
+    return as_f(as_u(mag) | (as_u(x) & 0x80000000u));
+}
+
 }  // namespace fqdev

@@ -31,10 +31,18 @@ struct QuantArgs {
     uint64_t rht_seed = 0; //  the quantization axis (not with the per-tensor format)
     uint32_t *partials;   // kAbsmaxPartials words (NV per-tensor only)
     bool cached_outputs;  // ordinary stores (outputs re-read right away) instead of streaming
+    // column axis only: retained FP8 channels (columns of x; bit mask [C/8])
+    // and their FP32 scales [C], or null
+    const void *retain = nullptr;
+    const float *chan_scale = nullptr;
 };
 
+// Partial maxima of |x| for the per-tensor NVFP4 scale; with retain (bit
+// c mod 8 of byte c / 8 for column c of a row of `cols` elements) the
+// retained columns are left out.
 hipError_t launch_absmax(const void *x, int64_t n_elems, uint32_t *partials,
-                         uint32_t *npart_out, hipStream_t stream);
+                         uint32_t *npart_out, hipStream_t stream,
+                         const void *retain = nullptr, int64_t cols = 0);
 hipError_t launch_quant(const QuantArgs &a, uint32_t npart, hipStream_t stream);
 hipError_t launch_dequant(int fmt, int col, const void *codes, const void *scales,
                           const float *outer, int64_t R, int64_t C, void *y,
@@ -95,8 +103,10 @@ hipError_t launch_channel_absmax(const void *x, int64_t R, int64_t C, uint32_t *
                                  hipStream_t stream);
 hipError_t launch_select_channels(const uint32_t *amax, int64_t C, int64_t k, void *retain,
                                   float *chan_scale, hipStream_t stream);
+// Row-axis fake quantization with retained FP8 channels (any format; the
+// per-tensor one takes `npart` partial maxima over the other channels).
 struct RetainArgs {
-    int fmt;                 // FMT_MX or FMT_NV128
+    int fmt;                 // FMT_*
     int sr;
     uint64_t seed;
     const void *x;           // BF16 [R, C]
@@ -105,6 +115,10 @@ struct RetainArgs {
     const float *chan_scale; // FP32 [C]
     void *y, *codes, *scales;
     float *outer;
+    void *keep = nullptr;          // STE keep mask [R, C/8] or null
+    const uint32_t *partials = nullptr;
+    uint32_t npart = 0;
+    bool cached_outputs = false;
 };
 hipError_t launch_quant_retain(const RetainArgs &a, hipStream_t stream);
 

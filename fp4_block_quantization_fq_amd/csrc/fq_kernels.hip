@@ -80,29 +80,20 @@ __device__ __forceinline__ uint4 ld_stream(const uint4 *p)
 // workgroup.  Consumers reduce the partials themselves, so no zero-filled
 // accumulator and no atomics are needed.
 // ---------------------------------------------------------------------------
-template <int NT>
-__device__ __forceinline__ uint32_t block_reduce_max(uint32_t m, uint32_t *red)
-{
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1)
-        m = max(m, (uint32_t)__shfl_xor((int)m, off));
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
-    __syncthreads();
-    m = red[0];
-#pragma unroll
-    for (int w = 1; w < NT / 64; ++w) m = max(m, red[w]);
-    return m;
-}
-
 // One workgroup of kAbsmaxThreads per partial; at most kAbsmaxGrid partials,
 // so that every quantizer workgroup reduces at most 1 KB of them.
 constexpr int kAbsmaxThreads = 1024;
 constexpr uint32_t kAbsmaxGrid = 256;
 static_assert(kAbsmaxGrid <= fqimpl::kAbsmaxPartials, "partials fit the workspace");
 
+// MASK: the columns whose bit is set in retain (bit c mod 8 of byte c / 8 of
+// a row of cpr chunks) take no part in the maximum (retained FP8 channels).
+template <bool MASK>
 __global__ __launch_bounds__(kAbsmaxThreads) void k_absmax(const uint4 *__restrict__ x,
                                                            uint32_t nchunks,
-                                                           uint32_t *__restrict__ partials)
+                                                           uint32_t *__restrict__ partials,
+                                                           const uint8_t *__restrict__ retain,
+                                                           uint32_t cpr)
 {
     __shared__ uint32_t red[kAbsmaxThreads / 64];
     uint32_t m = 0;
@@ -113,27 +104,19 @@ __global__ __launch_bounds__(kAbsmaxThreads) void k_absmax(const uint4 *__restri
         for (int u = 0; u < 4; ++u) {
             uint32_t c = base + u * kAbsmaxThreads + threadIdx.x;
             v[u] = c < nchunks ? x[c] : make_uint4(0, 0, 0, 0);
+            if (MASK && c < nchunks) {
+                const uint32_t r = retain[c % cpr];
+                v[u].x &= ~retained_halves(r, 0);
+                v[u].y &= ~retained_halves(r, 2);
+                v[u].z &= ~retained_halves(r, 4);
+                v[u].w &= ~retained_halves(r, 6);
+            }
         }
 #pragma unroll
         for (int u = 0; u < 4; ++u) m = max(m, absmax_bits_8(v[u]));
     }
     m = block_reduce_max<kAbsmaxThreads>(m, red);
     if (threadIdx.x == 0) partials[blockIdx.x] = m;
-}
-
-// NVFP4 per-tensor outer scale from the partial maxima (every thread of a
-// workgroup of NT threads; NT must be the launching workgroup's size, which
-// sizes the per-wave slots of the reduction).
-template <int NT>
-__device__ __forceinline__ OuterScale tensor_scale(const uint32_t *__restrict__ partials,
-                                                   uint32_t npart)
-{
-    static_assert(NT % 64 == 0 && NT <= 1024, "whole waves, at most 16");
-    __shared__ uint32_t red[NT / 64];
-    uint32_t m = 0;
-    for (uint32_t i = threadIdx.x; i < npart; i += NT) m = max(m, partials[i]);
-    m = block_reduce_max<NT>(m, red);
-    return make_outer(as_f(m << 16));
 }
 
 // Block scale of this lane's 16 elements (cross-lane for MXFP4 and the
@@ -290,13 +273,18 @@ __global__ __launch_bounds__(kThreads) void k_quant_row(
 //    and leave as full row pieces.
 // (tile constants and qc_offset: fq_device.hpp)
 
-template <int FMT, int RND, bool NT, int RHT = 0>
+// RET: retained FP8 channels (columns of x, bit mask retain [C/8], scales
+// chan_scale [C]): every block of a retained column is empty for the FP4
+// encoding (codes 0, scale of a zero block) and its values are the FP8 fake
+// quantization under the channel's scale.
+template <int FMT, int RND, bool NT, int RHT = 0, bool RET = false>
 __global__ __launch_bounds__(kQcThreads) void k_quant_col(
     const uint4 *__restrict__ x, uint32_t R, uint32_t C, uint4 *__restrict__ y,
     uint4 *__restrict__ yt, uint8_t *__restrict__ codes, uint8_t *__restrict__ scales,
     float *__restrict__ outer, uint8_t *__restrict__ keep,
     const uint32_t *__restrict__ partials, uint32_t npart, uint32_t seed_lo, uint32_t seed_hi,
-    uint32_t rs_lo, uint32_t rs_hi)
+    uint32_t rs_lo, uint32_t rs_hi, const uint8_t *__restrict__ retain,
+    const float *__restrict__ chan_scale)
 {
     constexpr uint32_t B = (FMT == FMT_MX) ? 32 : 16;
     constexpr uint32_t NS = kQcRows / B;                  // scales per column of the tile
@@ -370,6 +358,20 @@ __global__ __launch_bounds__(kQcThreads) void k_quant_col(
         }
         // the rotation along the column (a 128-block is the lane's 8-lane group)
         if (RHT) rht_segment<RHT>(xp, row0, rs_lo, rs_hi);
+        bool ret = false;
+        uint32_t xr[8];
+        BlockScale chs;
+        if (RET) {
+            ret = ((retain[col >> 3] >> (col & 7)) & 1u) != 0;
+            chs.s_eff = ret ? chan_scale[col] : 0.0f;
+            chs.code = 0;
+            finish_nv_scale(chs);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                xr[i] = xp[i];
+                if (ret) xp[i] = 0u;       // no part in any FP4 maximum, code 0
+            }
+        }
         float so = 0.0f;
         const BlockScale b = lane_block_scale<FMT>(absmax_bits_pairs8(xp), ot, so);
         if (FMT == FMT_NV128 && rb == 0) s_outer[lc * 2 + half] = so;
@@ -385,9 +387,20 @@ __global__ __launch_bounds__(kQcThreads) void k_quant_col(
         }
         uint32_t cw[2], yq[8];
         encode_pairs<FMT, RND, 8>(xp, b, rnd, cw, yq);
+        uint32_t clipped = keep ? ~keep_mask<FMT, 8>(xp, b) & 0xFFFFu : 0u;
+        if (RET && ret) {
+            clipped = 0;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                bool c0, c1;
+                yq[i] = bf16_pair_rne(fp8_fake(as_f(lo_bits(xr[i])), chs, &c0),
+                                      fp8_fake(as_f(hi_bits(xr[i])), chs, &c1));
+                clipped |= (c0 ? 1u : 0u) << (2 * i) | (c1 ? 1u : 0u) << (2 * i + 1);
+            }
+        }
         if (keep) {
             // element i of the segment is row rl0 + i of the tile
-            for (uint32_t clip = ~keep_mask<FMT, 8>(xp, b) & 0xFFFFu; clip; clip &= clip - 1) {
+            for (uint32_t clip = clipped; clip; clip &= clip - 1) {
                 const uint32_t i = __builtin_ctz(clip);
                 atomicOr(&s_clip[(rl0 + i) * (kQcCols / 32) + (lc >> 5)], 1u << (lc & 31));
             }
@@ -764,9 +777,11 @@ hipError_t quant_dispatch_nt(const fqimpl::QuantArgs &a, uint32_t npart, hipStre
 #define FQ_COL_ARGS                                                                          \
     (const uint4 *)a.x, (uint32_t)a.R, (uint32_t)a.C, (uint4 *)a.y, (uint4 *)a.yt,          \
         (uint8_t *)a.codes, (uint8_t *)a.scales, a.outer, (uint8_t *)a.keep, parts, npart, slo, \
-        shi, rlo, rhi
+        shi, rlo, rhi, (const uint8_t *)a.retain, a.chan_scale
         const dim3 g = quant_col_grid(a.R, a.C), b(kQcThreads);
-        if (a.rht_n == 16)
+        if (a.retain)
+            hipLaunchKernelGGL((k_quant_col<FMT, RND, NT, 0, true>), g, b, 0, st, FQ_COL_ARGS);
+        else if (a.rht_n == 16)
             hipLaunchKernelGGL((k_quant_col<FMT, RND, NT, 16>), g, b, 0, st, FQ_COL_ARGS);
         else if (a.rht_n == 128)
             hipLaunchKernelGGL((k_quant_col<FMT, RND, NT, 128>), g, b, 0, st, FQ_COL_ARGS);
@@ -789,14 +804,20 @@ hipError_t quant_dispatch(const fqimpl::QuantArgs &a, uint32_t npart, hipStream_
 namespace fqimpl {
 
 hipError_t launch_absmax(const void *x, int64_t n_elems, uint32_t *partials,
-                         uint32_t *npart_out, hipStream_t stream)
+                         uint32_t *npart_out, hipStream_t stream, const void *retain,
+                         int64_t cols)
 {
     const uint64_t nchunks = (uint64_t)n_elems / 8;
     uint64_t g = (nchunks + kAbsmaxThreads * 4 - 1) / (kAbsmaxThreads * 4);
     if (g > kAbsmaxGrid) g = kAbsmaxGrid;
     if (g == 0) g = 1;
-    hipLaunchKernelGGL(k_absmax, dim3((uint32_t)g), dim3(kAbsmaxThreads), 0, stream,
-                       (const uint4 *)x, (uint32_t)nchunks, partials);
+    if (retain)
+        hipLaunchKernelGGL(k_absmax<true>, dim3((uint32_t)g), dim3(kAbsmaxThreads), 0, stream,
+                           (const uint4 *)x, (uint32_t)nchunks, partials,
+                           (const uint8_t *)retain, (uint32_t)(cols / 8));
+    else
+        hipLaunchKernelGGL(k_absmax<false>, dim3((uint32_t)g), dim3(kAbsmaxThreads), 0, stream,
+                           (const uint4 *)x, (uint32_t)nchunks, partials, nullptr, 1u);
     *npart_out = (uint32_t)g;
     return hipGetLastError();
 }

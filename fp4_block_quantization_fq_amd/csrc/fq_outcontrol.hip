@@ -270,17 +270,6 @@ __global__ __launch_bounds__(kThreads) void k_select_channels(const uint32_t *__
 // ---------------------------------------------------------------------------
 // Row fake quantization with retained (FP8) channels
 // ---------------------------------------------------------------------------
-// FP8 E4M3 fake quantization under the channel scale s: a = |x| / s (IEEE
-// division), E4M3 nearest-even saturating at 448, value * s, sign kept; a
-// zero scale gives +-0.
-__device__ __forceinline__ float fp8_fake(float x, const BlockScale &s)
-{
-    // RN(|x| / s) by the corrected reciprocal, as for the FP4 block quotient
-    const float a = div_corrected(__builtin_fabsf(x) * s.xs, s.sq, s.rcp);
-    const float mag = e4m3_value(e4m3_encode_sat(a)) * s.s_eff;
-    return as_f(as_u(mag) | (as_u(x) & 0x80000000u));
-}
-
 // One 8-element chunk per lane, as the row quantizer's chunk mapping; a
 // workgroup covers 256 consecutive chunks of kRetainRows consecutive rows
 // (row group and part from the workgroup index, so no per-lane division),
@@ -292,17 +281,27 @@ __device__ __forceinline__ float fp8_fake(float x, const BlockScale &s)
 // rows of its group.
 constexpr uint32_t kRetainRows = 8;
 
+// The per-tensor format reduces the partial maxima of the masked maximum pass
+// (retained channels left out) at the start; keep, if given, receives the STE
+// keep bits of each chunk (the FP8 test a <= 448 for retained elements).
 template <int FMT, int RND, bool NT>
 __global__ __launch_bounds__(kThreads) void k_quant_row_retain(
     const uint4 *__restrict__ x, uint32_t R, uint32_t cpr, uint32_t wpr,
     const uint8_t *__restrict__ retain, const float4 *__restrict__ chan_scale,
     uint4 *__restrict__ y, uint32_t *__restrict__ codes, uint8_t *__restrict__ scales,
-    float *__restrict__ outer, uint32_t seed_lo, uint32_t seed_hi)
+    float *__restrict__ outer, uint8_t *__restrict__ keep, const uint32_t *__restrict__ partials,
+    uint32_t npart, uint32_t seed_lo, uint32_t seed_hi)
 {
+    OuterScale ot = {0.0f, 0.0f};
+    if (FMT == FMT_NVT) {
+        ot = tensor_scale<kThreads>(partials, npart);
+        if (outer && blockIdx.x == 0 && threadIdx.x == 0) outer[0] = ot.s;
+    }
     const uint32_t lane = threadIdx.x & 63;
     const uint32_t group = blockIdx.x / wpr, part = blockIdx.x % wpr;
     const uint32_t j = part * kThreads + threadIdx.x;       // chunk within the row
     if (j >= cpr) return;      // block groups never straddle this edge (C % B == 0)
+                               // (after the workgroup-wide per-tensor reduction)
     const uint32_t rbits = retain[j];                       // bit e: element e is an FP8 channel
     BlockScale ch[8];
     if (rbits) {
@@ -316,10 +315,10 @@ __global__ __launch_bounds__(kThreads) void k_quant_row_retain(
         }
     }
     // the FP4 maxima skip the retained elements
-    uint32_t keep[4];
+    uint32_t fp4m[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-        keep[i] = (((rbits >> (2 * i)) & 1u) ? 0u : 0x7FFFu) |
+        fp4m[i] = (((rbits >> (2 * i)) & 1u) ? 0u : 0x7FFFu) |
                   (((rbits >> (2 * i + 1)) & 1u) ? 0u : 0x7FFF0000u);
     // the retained elements' code nibbles and BF16 halves
     uint32_t nib = 0, sel[4];
@@ -339,9 +338,8 @@ __global__ __launch_bounds__(kThreads) void k_quant_row_retain(
         const uint32_t xp[4] = {v.x, v.y, v.z, v.w};
         uint32_t mp[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) mp[i] = xp[i] & keep[i];
+        for (int i = 0; i < 4; ++i) mp[i] = xp[i] & fp4m[i];
         const uint32_t m = pkmax_u16(pkmax_u16(mp[0], mp[1]), pkmax_u16(mp[2], mp[3]));
-        const OuterScale ot = {0.0f, 0.0f};
         float so = 0.0f;
         const BlockScale b = chunk_block_scale<FMT>(max(m & 0xFFFFu, m >> 16), ot, so);
         if (FMT == FMT_NV128 && outer && (lane & 15) == 0) outer[c >> 4] = so;
@@ -357,16 +355,22 @@ __global__ __launch_bounds__(kThreads) void k_quant_row_retain(
             rnd[0] = philox4x32_10((uint32_t)c, (uint32_t)(c >> 32), 0u, 0u, seed_lo, seed_hi);
         uint32_t cw[1], yp[4];
         encode_pairs<FMT, RND, 4>(xp, b, rnd, cw, yp);
+        uint32_t kb = keep ? keep_mask<FMT, 4>(xp, b) : 0u;
         if (rbits) {
             // every element's FP8 value, then a select per element
             cw[0] &= ~nib;
+            uint32_t kr = 0;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const uint32_t f = bf16_pair_rne(fp8_fake(bf16_lo(xp[i]), ch[2 * i]),
-                                                 fp8_fake(bf16_hi(xp[i]), ch[2 * i + 1]));
+                bool c0, c1;
+                const uint32_t f = bf16_pair_rne(fp8_fake(bf16_lo(xp[i]), ch[2 * i], &c0),
+                                                 fp8_fake(bf16_hi(xp[i]), ch[2 * i + 1], &c1));
                 yp[i] = (f & sel[i]) | (yp[i] & ~sel[i]);
+                kr |= (c0 ? 0u : 1u) << (2 * i) | (c1 ? 0u : 1u) << (2 * i + 1);
             }
+            kb = (kb & ~rbits) | (kr & rbits);
         }
+        if (keep) keep[c] = (uint8_t)kb;
         if (codes) {
             if (NT) __builtin_nontemporal_store(cw[0], &codes[c]);
             else codes[c] = cw[0];
@@ -388,10 +392,16 @@ hipError_t retain_dispatch(const fqimpl::RetainArgs &a, hipStream_t st)
     const uint64_t groups = ((uint64_t)a.R + kRetainRows - 1) / kRetainRows;
     const uint64_t grid = groups * wpr;
     const uint32_t slo = (uint32_t)a.seed, shi = (uint32_t)(a.seed >> 32);
-    hipLaunchKernelGGL((k_quant_row_retain<FMT, RND, true>), dim3((uint32_t)grid), dim3(kThreads),
-                       0, st, (const uint4 *)a.x, (uint32_t)a.R, cpr, wpr,
-                       (const uint8_t *)a.retain, (const float4 *)a.chan_scale, (uint4 *)a.y,
-                       (uint32_t *)a.codes, (uint8_t *)a.scales, a.outer, slo, shi);
+#define FQ_RETAIN_ARGS                                                                         \
+    dim3((uint32_t)grid), dim3(kThreads), 0, st, (const uint4 *)a.x, (uint32_t)a.R, cpr, wpr, \
+        (const uint8_t *)a.retain, (const float4 *)a.chan_scale, (uint4 *)a.y,               \
+        (uint32_t *)a.codes, (uint8_t *)a.scales, a.outer, (uint8_t *)a.keep, a.partials,      \
+        a.npart, slo, shi
+    if (a.cached_outputs)
+        hipLaunchKernelGGL((k_quant_row_retain<FMT, RND, false>), FQ_RETAIN_ARGS);
+    else
+        hipLaunchKernelGGL((k_quant_row_retain<FMT, RND, true>), FQ_RETAIN_ARGS);
+#undef FQ_RETAIN_ARGS
     return hipGetLastError();
 }
 
@@ -460,6 +470,8 @@ hipError_t launch_quant_retain(const RetainArgs &a, hipStream_t st)
     switch (a.fmt * 2 + a.sr) {
     case FMT_MX * 2 + 0: return retain_dispatch<FMT_MX, RND_RNE>(a, st);
     case FMT_MX * 2 + 1: return retain_dispatch<FMT_MX, RND_SR>(a, st);
+    case FMT_NVT * 2 + 0: return retain_dispatch<FMT_NVT, RND_RNE>(a, st);
+    case FMT_NVT * 2 + 1: return retain_dispatch<FMT_NVT, RND_SR>(a, st);
     case FMT_NV128 * 2 + 0: return retain_dispatch<FMT_NV128, RND_RNE>(a, st);
     case FMT_NV128 * 2 + 1: return retain_dispatch<FMT_NV128, RND_SR>(a, st);
     default: return hipErrorInvalidValue;

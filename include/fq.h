@@ -366,18 +366,51 @@ fq_status fq_channel_absmax(const void *x_bf16, int64_t rows, int64_t cols, uint
 fq_status fq_select_channels(const uint32_t *amax, int64_t cols, int64_t k, void *retain,
                              float *chan_scale, void *stream);
 
-/* Row-axis fake quantization with retained channels: columns whose retain
- * bit is set are FP8 E4M3 fake-quantized under chan_scale (|x| / s in FP32,
- * nearest-even, saturating at 448, times s, sign kept; s = 0 gives +-0) and
- * carry FP4 code 0; every FP4 block and 128-element outer maximum is taken
- * over the other elements only.  desc: MXFP4 or NVFP4 double block
- * (FQ_OUTER_BLOCK128), axis FQ_AXIS_ROW, RNE or SR; y required, codes,
- * scales, outer optional (as fq_fake_quant); retain and chan_scale as written
- * by fq_select_channels, chan_scale 16-byte aligned. */
+/* Fake quantization with retained channels, along either axis: the columns
+ * of x whose retain bit is set (the activation's channels) are FP8 E4M3
+ * fake-quantized under chan_scale (|x| / s in FP32, nearest-even, saturating
+ * at 448, times s, sign kept; s = 0 gives +-0) and carry FP4 code 0; every
+ * FP4 block, 128-element outer and per-tensor maximum is taken over the other
+ * elements only.  That is the plain fake quantization of x with the retained
+ * columns set to +0, the FP8 values in their place.  FQ_AXIS_ROW: the
+ * retained columns drop out of the 1xB groups they share; FQ_AXIS_COL: every
+ * group of a retained column is empty.  desc: any format, rounding and axis;
+ * cols a multiple of 8; y required, codes, scales, outer optional (as
+ * fq_fake_quant); retain and chan_scale as written by fq_select_channels,
+ * chan_scale 16-byte aligned; ws / ws_bytes as fq_fake_quant (per-tensor
+ * NVFP4: 4096 bytes).  Source: "Resumo Tecnico: TetraJet-v2", sec. 2.C
+ * (OutControl, "Retencao Estatica de Outliers": the top p % channels stay in
+ * FP8 in the forward and the backward pass, the rest in FP4). */
 fq_status fq_fake_quant_retain(const fq_desc *desc, const void *x_bf16, int64_t rows,
                                int64_t cols, void *y_bf16, void *codes, void *scales,
                                float *outer, const void *retain, const float *chan_scale,
-                               void *stream);
+                               void *ws, size_t ws_bytes, void *stream);
+
+/* fq_qlinear_fwd with the activation's retained channels (columns of X, as
+ * fq_fake_quant_retain along the row axis) kept in FP8: Y = FQ_retain(X) x
+ * FQ(W) on the BF16 matrix cores (whatever the formats).  Arguments and
+ * workspace as fq_qlinear_fwd, plus retain [K/8] and chan_scale [K]; K a
+ * multiple of 8.  Source: "Resumo Tecnico: TetraJet-v2", sec. 2.C (forward
+ * pass). */
+fq_status fq_qlinear_fwd_retain(const fq_desc *desc_x, const fq_desc *desc_w, const void *x_bf16,
+                                const void *w_bf16, int64_t M, int64_t K, int64_t N,
+                                const void *retain, const float *chan_scale, void *y_bf16,
+                                void *ws, size_t ws_bytes, void *stream);
+
+/* fq_qlinear_bwd (without the rotation) with the activation's retained
+ * channels kept in FP8: X_hat is fq_fake_quant_retain of X along the row
+ * axis, X_hat's quantization along M for dW keeps the same channels in FP8
+ * (fq_fake_quant_retain along the column axis with desc_g's format, rounding
+ * and key seed + 2), and STE_X passes a retained entry where |x| / s <= 448
+ * (the FP8 format's clip).  Both products run on the BF16 matrix cores.
+ * Arguments and workspace as fq_qlinear_bwd with rht_block = 0, plus retain
+ * [K/8] and chan_scale [K]; K a multiple of 8.  Source: "Resumo Tecnico:
+ * TetraJet-v2", sec. 2.C (forward and backward pass). */
+fq_status fq_qlinear_bwd_retain(const fq_desc *desc_x, const fq_desc *desc_w,
+                                const fq_desc *desc_g, const void *x_bf16, const void *w_bf16,
+                                const void *dy_bf16, int64_t M, int64_t K, int64_t N,
+                                const void *retain, const float *chan_scale, void *dx_bf16,
+                                void *dw_bf16, void *ws, size_t ws_bytes, void *stream);
 
 /* Static description of a status code. */
 const char *fq_status_string(fq_status s);

@@ -88,6 +88,8 @@ def lib() -> ctypes.CDLL:
                                                u16p, i64, i64, u8p, f32p, u8p, u8p, f32p,
                                                u16p, ctypes.c_int]
         L.fqo_quantize_rows_retain.restype = ctypes.c_int
+        L.fqo_fp8_fake.argtypes = [u16p, f32p, i64, u16p, u8p]
+        L.fqo_fp8_fake.restype = ctypes.c_int
         L.fqo_max_threads.argtypes = []
         L.fqo_max_threads.restype = ctypes.c_int
         _lib = L
@@ -444,6 +446,54 @@ def select_channels(amax_bits: np.ndarray, k: int):
     return retain, scale
 
 
+def fp8_fake(x: np.ndarray, scale: np.ndarray):
+    """Element-wise FP8 E4M3 fake quantization of BF16 values x under the
+    FP32 scales `scale` (same shape): y (BF16 bits) and the clip flag
+    (a = |x| / s > 448)."""
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    sc = np.ascontiguousarray(np.broadcast_to(scale, x.shape), dtype=np.float32)
+    y = np.empty_like(x)
+    clip = np.empty(x.shape, np.uint8)
+    lib().fqo_fp8_fake(_ptr(x, ctypes.c_uint16), _ptr(sc, ctypes.c_float), x.size,
+                       _ptr(y, ctypes.c_uint16), _ptr(clip, ctypes.c_uint8))
+    return y, clip
+
+
+def fake_quant_retained(x: np.ndarray, fmt: str, retain: np.ndarray, chan_scale: np.ndarray,
+                        rounding: str = "rne", axis: str = "row", seed: int = 0,
+                        nthreads: int | None = None) -> dict:
+    """Fake quantization with static outlier-channel retention ("Resumo
+    Tecnico: TetraJet-v2", sec. 2.C) along either axis and in every format.
+
+    The channels are the columns of x [R, C] (retain [C] bool, chan_scale [C]
+    FP32).  READING (the same as fqo_quantize_rows_retain's on the row axis):
+    a retained element takes no part in any FP4 maximum (block, 128-block or
+    tensor) and carries FP4 code 0; its value is its FP8 fake quantization.
+    That is exactly the plain quantizer applied to x with the retained columns
+    set to +0, with the FP8 values put in their place: along the row axis the
+    retained columns drop out of the blocks they share with other columns;
+    along the column axis every block of a retained column is empty.  Returns
+    codes / scales / outer of the FP4 part (layouts of fake_quant), y, and
+    clip (FP4 rule for the rest, FP8 rule, a > 448, for retained elements)."""
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    ret = np.asarray(retain, bool)
+    cs = np.asarray(chan_scale, np.float32)
+    xz = x.copy()
+    xz[:, ret] = 0
+    q = fake_quant(xz, fmt, rounding, axis, seed, nthreads)
+    y8, clip8 = fp8_fake(x[:, ret], np.broadcast_to(cs[ret], (x.shape[0], int(ret.sum()))))
+    y = q["y"].copy()
+    y[:, ret] = y8
+    # the FP4 straight-through test recomputed from x and the stored scales,
+    # as ste_backward does, then the FP8 test for the retained columns
+    ones = np.full(x.shape, 0x3F80, dtype=np.uint16)
+    clip = (ste_backward(x, q["scales"], q["outer"], ones, fmt, axis, nthreads) == 0)
+    clip = clip.astype(np.uint8)
+    clip[:, ret] = clip8
+    return {"codes": q["codes"], "scales": q["scales"], "outer": q["outer"], "y": y,
+            "clip": clip}
+
+
 def fake_quant_retain(x: np.ndarray, fmt: str, retain: np.ndarray, chan_scale: np.ndarray,
                       rounding: str = "rne", seed: int = 0,
                       nthreads: int | None = None) -> dict:
@@ -479,14 +529,21 @@ def bf16_bits_to_f64(a: np.ndarray) -> np.ndarray:
 def qlinear(x: np.ndarray, w: np.ndarray, fmt_x: str = "nv_tensor",
             fmt_w: str = "nv_tensor", rounding_x: str = "rne",
             rounding_w: str = "rne", seed_x: int = 0, seed_w: int = 0,
-            nthreads: int | None = None) -> dict:
+            nthreads: int | None = None, retain=None, chan_scale=None) -> dict:
     """QAT linear forward: Y = FQ(X) @ FQ(W).
 
     X [M, K] is quantized in groups along K (its rows), W [K, N] in groups
     along K (its columns, the transposed axis).  Y is the float64 product of
     the two dequantized BF16 tensors (numpy matmul as the contraction step).
+    With retain / chan_scale the activation's retained channels (columns of X)
+    are FP8 (fake_quant_retained), the rest FP4 ("Resumo Tecnico:
+    TetraJet-v2", sec. 2.C, forward pass).
     """
-    fx = fake_quant(x, fmt_x, rounding_x, "row", seed_x, nthreads)
+    if retain is None:
+        fx = fake_quant(x, fmt_x, rounding_x, "row", seed_x, nthreads)
+    else:
+        fx = fake_quant_retained(x, fmt_x, retain, chan_scale, rounding_x, "row", seed_x,
+                                 nthreads)
     fw = fake_quant(w, fmt_w, rounding_w, "col", seed_w, nthreads)
     Y = bf16_bits_to_f64(fx["y"]) @ bf16_bits_to_f64(fw["y"])
     return {"xhat": fx["y"], "what": fw["y"], "y": Y}
@@ -502,7 +559,7 @@ def qlinear_bwd(x: np.ndarray, w: np.ndarray, dy: np.ndarray, fmt_x: str = "nv_t
                 fmt_w: str = "nv_tensor", fmt_g: str = "nv_128", rounding_g: str = "sr",
                 seed_g: int = 0, rounding_x: str = "rne", rounding_w: str = "rne",
                 seed_x: int = 0, seed_w: int = 0, rht_block: int = 0, rht_seed: int = 0,
-                nthreads: int | None = None) -> dict:
+                nthreads: int | None = None, retain=None, chan_scale=None) -> dict:
     """QAT linear backward of Y = FQ(X) @ FQ(W) (TetraJet-v2 sec. 2.A).
 
     X_hat = FQ(X) along K and W_hat = FQ(W) along K are the forward operands.
@@ -513,10 +570,19 @@ def qlinear_bwd(x: np.ndarray, w: np.ndarray, dy: np.ndarray, fmt_x: str = "nv_t
     with Philox keys seed_g + 0, + 1, + 2, + 3 for the four Q in that order,
     and keep_* the STE masks of the forward (1 where a <= 6).  With rht_block
     16 or 128 each Q's input is first rotated along that Q's axis by the
-    random Hadamard transform (seed rht_seed; TetraJet-v2 sec. 2.C).  The
-    products are float64 (numpy matmul as the contraction step).
+    random Hadamard transform (seed rht_seed; TetraJet-v2 sec. 2.C).  With
+    retain / chan_scale the activation's retained channels are FP8 in X_hat
+    and in Q(X_hat, along M), and keep_X uses the FP8 clip test for them
+    (sec. 2.C: the channels stay in higher precision in the forward and the
+    backward pass).  The products are float64 (numpy matmul as the
+    contraction step).
     """
-    fx = fake_quant(x, fmt_x, rounding_x, "row", seed_x, nthreads)
+    if retain is None:
+        fx = fake_quant(x, fmt_x, rounding_x, "row", seed_x, nthreads)
+    else:
+        assert not rht_block, "retention with the rotated backward is not defined here"
+        fx = fake_quant_retained(x, fmt_x, retain, chan_scale, rounding_x, "row", seed_x,
+                                 nthreads)
     fw = fake_quant(w, fmt_w, rounding_w, "col", seed_w, nthreads)
     m64 = (1 << 64) - 1
     rot = (lambda t, ax: hadamard(t, rht_block, ax, rht_seed, nthreads)) if rht_block else \
@@ -524,12 +590,18 @@ def qlinear_bwd(x: np.ndarray, w: np.ndarray, dy: np.ndarray, fmt_x: str = "nv_t
     q_dy_n = fake_quant(rot(dy, "row"), fmt_g, rounding_g, "row", (seed_g + 0) & m64, nthreads)
     q_w_n = fake_quant(rot(fw["y"], "row"), fmt_g, rounding_g, "row", (seed_g + 1) & m64,
                        nthreads)
-    q_x_m = fake_quant(rot(fx["y"], "col"), fmt_g, rounding_g, "col", (seed_g + 2) & m64,
-                       nthreads)
+    if retain is None:
+        q_x_m = fake_quant(rot(fx["y"], "col"), fmt_g, rounding_g, "col", (seed_g + 2) & m64,
+                           nthreads)
+    else:
+        # the retained channels stay FP8 in the backward too (sec. 2.C)
+        q_x_m = fake_quant_retained(fx["y"], fmt_g, retain, chan_scale, rounding_g, "col",
+                                    (seed_g + 2) & m64, nthreads)
     q_dy_m = fake_quant(rot(dy, "col"), fmt_g, rounding_g, "col", (seed_g + 3) & m64, nthreads)
     dx_raw = bf16_bits_to_f64(q_dy_n["y"]) @ bf16_bits_to_f64(q_w_n["y"]).T
     dw_raw = bf16_bits_to_f64(q_x_m["y"]).T @ bf16_bits_to_f64(q_dy_m["y"])
-    keep_x = _clip_keep(x, fx, fmt_x, "row")
+    keep_x = _clip_keep(x, fx, fmt_x, "row") if retain is None else \
+        (1.0 - fx["clip"].astype(np.float64))
     keep_w = _clip_keep(w, fw, fmt_w, "col")
     return {"dx": keep_x * dx_raw, "dw": keep_w * dw_raw, "xhat": fx["y"], "what": fw["y"],
             "q_dy_n": q_dy_n["y"], "q_w_n": q_w_n["y"], "q_x_m": q_x_m["y"],

@@ -411,6 +411,20 @@ static uint16_t fp8_fake_quant(float xv, float s)
     return fqo_f32_to_bf16(signbit(xv) ? -mag : mag);
 }
 
+/* Element-wise FP8 fake quantization of n BF16 values, each under its own
+ * scale s[i] (the retained channel's), and the straight-through clip flag of
+ * each.  READING: an FP8 element is clipped when a = |x| / s (FP32) exceeds
+ * 448, the largest E4M3 value, as an FP4 element is when a exceeds 6. */
+int fqo_fp8_fake(const uint16_t *x, const float *s, int64_t n, uint16_t *y, uint8_t *clip)
+{
+    for (int64_t i = 0; i < n; ++i) {
+        float xv = fqo_bf16_to_f32(x[i]);
+        y[i] = fp8_fake_quant(xv, s[i]);
+        if (clip) clip[i] = (s[i] != 0.0f && fabsf(xv) / s[i] > 448.0f) ? 1 : 0;
+    }
+    return 0;
+}
+
 /* Row-axis fake quantization with retained channels.  retain[c] != 0 marks
  * column c as an FP8 channel with scale chan_scale[c].  READING: retained
  * elements take no part in the FP4 scales (block and 128-element outer

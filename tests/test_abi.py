@@ -201,20 +201,33 @@ def test_outcontrol_entry_points_validate(L):
     assert L.fq_select_channels(f(), 64, -1, f(), f(), None) == fq.FQ_ERR_SHAPE
     assert L.fq_select_channels(f(), 60, 4, f(), f(), None) == fq.FQ_ERR_SHAPE
     assert L.fq_select_channels(f(), 64, 4, None, f(), None) == fq.FQ_ERR_NULL
-    # retained-channel quantizer: row axis, MXFP4 or double-block NVFP4
+    # retained-channel quantizer: either axis, every format
     mx, nvt = fq.fq_desc_mxfp4(), fq.fq_desc_nvfp4()
     col = fq.fq_desc_mxfp4(axis=fq.FQ_AXIS_COL)
 
-    def fqr(d, retain=f(), scale=f(), rows=64, cols=64, y=f()):
+    def fqr(d, retain=f(), scale=f(), rows=64, cols=64, y=f(), ws=f(), ws_bytes=4096):
         return L.fq_fake_quant_retain(ctypes.byref(d), f(), rows, cols, y, None, None, None,
-                                      retain, scale, None)
-    assert fqr(nvt) == fq.FQ_ERR_DESC
-    assert fqr(col) == fq.FQ_ERR_DESC
+                                      retain, scale, ws, ws_bytes, None)
+    assert fqr(nvt, ws=None) == fq.FQ_ERR_NULL                  # per tensor: partial maxima
+    assert fqr(nvt, ws_bytes=16) == fq.FQ_ERR_WORKSPACE
+    assert fqr(col, rows=48) == fq.FQ_ERR_SHAPE                 # column groups of 32 rows
     assert fqr(mx, retain=None) == fq.FQ_ERR_NULL
     assert fqr(mx, scale=None) == fq.FQ_ERR_NULL
     assert fqr(mx, y=None) == fq.FQ_ERR_NULL
     assert fqr(mx, cols=48) == fq.FQ_ERR_SHAPE
     assert fqr(fq.fq_desc_nvfp4(outer=fq.FQ_OUTER_BLOCK128), cols=64) == fq.FQ_ERR_SHAPE
+    assert fqr(fq.fq_desc_nvfp4(axis=fq.FQ_AXIS_COL), rows=64, cols=12) == fq.FQ_ERR_SHAPE
+    # the retained linear: both masks required, K a multiple of 8
+    nv, wcol = fq.fq_desc_nvfp4(), fq.fq_desc_nvfp4(axis=fq.FQ_AXIS_COL)
+    big = 1 << 40
+    assert L.fq_qlinear_fwd_retain(ctypes.byref(nv), ctypes.byref(wcol), f(), f(), 128, 128, 128,
+                                   None, f(), f(), f(), big, None) == fq.FQ_ERR_NULL
+    assert L.fq_qlinear_fwd_retain(ctypes.byref(nv), ctypes.byref(wcol), f(), f(), 128, 128, 128,
+                                   f(), None, f(), f(), big, None) == fq.FQ_ERR_NULL
+    g = fq.fq_desc_nvfp4(outer=fq.FQ_OUTER_BLOCK128, rounding=fq.FQ_ROUND_SR)
+    assert L.fq_qlinear_bwd_retain(ctypes.byref(nv), ctypes.byref(wcol), ctypes.byref(g), f(),
+                                   f(), f(), 128, 128, 128, None, f(), f(), f(), f(), big,
+                                   None) == fq.FQ_ERR_NULL
 
 
 def test_qlinear_bwd_validates(L):

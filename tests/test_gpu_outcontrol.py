@@ -11,7 +11,7 @@ import torch
 import fp4_block_quantization_fq_amd as fq
 import oracle
 import workloads as wl
-from gpu_util import assert_same, make_desc, to_bits, to_dev, to_np
+from gpu_util import assert_product_bound, assert_same, make_desc, to_bits, to_dev, to_np
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -95,10 +95,10 @@ def test_channel_selection_matches_oracle(shape):
             assert np.flatnonzero(ret_o).tolist() == cols.tolist()
 
 
-def _retain_case(x, fmt, rnd, k, seed=31):
+def _retain_case(x, fmt, rnd, k, seed=31, axis="row"):
     ret_o, sc_o = oracle.select_channels(oracle.channel_absmax(x), k)
-    ref = oracle.fake_quant_retain(x, fmt, ret_o, sc_o, rnd, seed)
-    d = make_desc(fmt, rnd, "row", seed)
+    ref = oracle.fake_quant_retained(x, fmt, ret_o, sc_o, rnd, axis, seed)
+    d = make_desc(fmt, rnd, axis, seed)
     tx = to_dev(x)
     R, C = x.shape
     out = fq.alloc_outputs(d, R, C, tx.device)
@@ -107,21 +107,79 @@ def _retain_case(x, fmt, rnd, k, seed=31):
     torch.cuda.synchronize()
     got = {"y": to_bits(y), "codes": to_np(out.codes), "scales": to_np(out.scales),
            "outer": None if out.outer is None else to_np(out.outer)}
-    assert_same(got, ref, tag=f"retain {fmt}/{rnd}/{x.shape}/k={k}")
+    assert_same(got, ref, tag=f"retain {fmt}/{rnd}/{axis}/{x.shape}/k={k}")
 
 
-@pytest.mark.parametrize("shape", [(256, 384), (130, 1024)])
+@pytest.mark.parametrize("shape", [(256, 384), (384, 1024)])
 @pytest.mark.parametrize("rnd", ["rne", "sr"])
-@pytest.mark.parametrize("fmt", ["mx", "nv_128"])
-def test_fake_quant_retain_matches_oracle(fmt, rnd, shape):
+@pytest.mark.parametrize("fmt", ["mx", "nv_128", "nv_tensor"])
+@pytest.mark.parametrize("axis", ["row", "col"])
+def test_fake_quant_retain_matches_oracle(fmt, rnd, shape, axis):
     x = wl.activation_with_outlier_channels(shape, 1.0, 6, 100.0, seed=shape[0])
     for k in (0, 6, shape[1] // 10):
-        _retain_case(x, fmt, rnd, k)
+        _retain_case(x, fmt, rnd, k, axis=axis)
+
+
+def test_fake_quant_retain_ragged_rows():
+    # 130 rows: a partial row group (row axis); column tiles of 256 rows with
+    # a ragged end (column axis needs rows in whole blocks: 160)
+    x = wl.activation_with_outlier_channels((130, 1024), 1.0, 6, 100.0, seed=130)
+    for fmt in ("mx", "nv_128", "nv_tensor"):
+        _retain_case(x, fmt, "sr", 102)
+    x = wl.activation_with_outlier_channels((160, 1032), 1.0, 6, 100.0, seed=160)
+    for fmt in ("mx", "nv_tensor"):
+        _retain_case(x, fmt, "sr", 103, axis="col")
 
 
 def test_fake_quant_retain_full_size():
     x = wl.nv_activation(16384, 4096, seed=3)
     _retain_case(x, "nv_128", "sr", 410, seed=1234)
+    _retain_case(x, "nv_128", "sr", 410, seed=1234, axis="col")
+    _retain_case(x, "nv_tensor", "rne", 410, axis="row")
+
+
+def _linear_retained(M, K, N, fmts, frac=0.1, seed_g=1234):
+    """The retained linear forward and backward against the oracle's
+    composition: X_hat bit for bit, every product element within the
+    FP32-accumulation / BF16-rounding bound, dropped STE entries exactly 0."""
+    fx, fw, fg = fmts
+    x, _ = wl.activation_and_outlier_channels((M, K), 1.0, 8, 100.0, seed=61)
+    w = wl.normal_bf16((K, N), 0.02, 62)
+    dy = wl.normal_bf16((M, N), 1e-3, 63)
+    k = max(1, int(round(frac * K)))
+    ret_o, sc_o = oracle.select_channels(oracle.channel_absmax(x), k)
+    retain = torch.from_numpy(np.packbits(ret_o, bitorder="little")).to(DEV)
+    cs = torch.from_numpy(sc_o).to(DEV)
+    dx_, dw_, dg_ = make_desc(fx, "rne", "row"), make_desc(fw, "rne", "col"), \
+        make_desc(fg, "sr", "row", seed_g)
+    xd, wd, dyd = to_dev(x), to_dev(w), to_dev(dy)
+    ws = fq.qlinear_workspace(dx_, dw_, M, K, N, xd.device)
+    y = fq.fq_qlinear_fwd_retain(dx_, dw_, xd, wd, retain, cs, ws=ws)
+    gx, gw = fq.fq_qlinear_bwd_retain(dx_, dw_, dg_, xd, wd, dyd, retain, cs)
+    torch.cuda.synchronize()
+    ref = oracle.qlinear(x, w, fx, fw, retain=ret_o, chan_scale=sc_o)
+    xhat, _ = fq.qlinear_workspace_views(ws, M, K, N)
+    assert np.array_equal(to_bits(xhat), ref["xhat"]), "X_hat with retained channels"
+    f64 = oracle.bf16_bits_to_f64
+    absprod = np.abs(f64(ref["xhat"])) @ np.abs(f64(ref["what"]))
+    assert_product_bound(f64(to_bits(y)), ref["y"], absprod, K, tag="retained forward")
+    rb = oracle.qlinear_bwd(x, w, dy, fx, fw, fg, "sr", seed_g, retain=ret_o, chan_scale=sc_o)
+    for name, got, keep, a, b, kdim in (
+            ("dx", gx, rb["keep_x"], f64(rb["q_dy_n"]), f64(rb["q_w_n"]).T, N),
+            ("dw", gw, rb["keep_w"], f64(rb["q_x_m"]).T, f64(rb["q_dy_m"]), M)):
+        g = f64(to_bits(got))
+        assert_product_bound(g, a @ b, np.abs(a) @ np.abs(b), kdim, keep=keep,
+                             tag=f"retained backward {name}")
+
+
+@pytest.mark.parametrize("fmts", [("nv_tensor", "nv_tensor", "nv_128"), ("mx", "mx", "mx"),
+                                  ("nv_128", "nv_tensor", "nv_tensor")])
+def test_linear_retained_small(fmts):
+    _linear_retained(256, 384, 256, fmts)
+
+
+def test_linear_retained_full_size():
+    _linear_retained(8192, 2880, 5760, ("nv_tensor", "nv_tensor", "nv_128"))
 
 
 @pytest.mark.parametrize("shape,fmt", [((1, 4), None), ((1, 132), None),

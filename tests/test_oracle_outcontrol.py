@@ -237,3 +237,131 @@ def test_retained_columns_are_fp8_e4m3():
         mag = (e * scale[c]).astype(np.float32)
         want = f32_to_bf16_bits(np.where(np.signbit(xf[:, c]), -mag, mag))
         assert np.array_equal(r["y"][:, c], want), c
+
+
+# ---------------------------------------------------------------------------
+# retention on both axes, every format, and in the linear (sec. 2.C: the
+# retained channels stay FP8 in the forward and the backward pass)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("fmt", ["mx", "nv_128"])
+@pytest.mark.parametrize("rnd", ["rne", "sr"])
+def test_retained_composition_equals_the_loop_oracle_on_rows(fmt, rnd):
+    # the zero-and-overlay composition against the C loop that masks the
+    # retained columns out of each block (two formulations of one reading)
+    x, cols = activation_and_outlier_channels((64, 384), 1.0, 8, 100.0, seed=3)
+    retain = np.zeros(384, bool)
+    retain[cols] = True
+    retain[[5, 6, 200]] = True
+    scale = np.where(retain, np.float32(0.37), np.float32(0)).astype(np.float32)
+    a = oracle.fake_quant_retained(x, fmt, retain, scale, rnd, "row", 99)
+    b = oracle.fake_quant_retain(x, fmt, retain, scale, rnd, 99)
+    for k in ("codes", "scales", "outer", "y"):
+        if a[k] is None:
+            assert b[k] is None
+            continue
+        assert np.array_equal(a[k], b[k]), k
+
+
+def test_fp8_clip_rule_by_hand():
+    # scale 1: |x| = 448 is kept, 464 (rounds to 448) and 480 are clipped;
+    # scale 0.5: 224 -> a = 448 kept, 232 -> a = 464 clipped; scale 0: kept, +-0
+    x = bf([448.0, 464.0, -480.0, 224.0, 232.0, -3.0, 1.0])
+    s = np.array([1, 1, 1, 0.5, 0.5, 0, 1], np.float32)
+    y, clip = oracle.fp8_fake(x, s)
+    assert clip.tolist() == [0, 1, 1, 0, 1, 0, 0]
+    assert f32(y).tolist() == [448.0, 448.0, -448.0, 224.0, 224.0, -0.0, 1.0]
+    assert np.signbit(f32(y)[5])
+
+
+def f32(bits):
+    return oracle.bf16_bits_to_f64(bits).astype(np.float32)
+
+
+def test_column_axis_retention_by_hand():
+    # x [32, 8], MXFP4 along rows of each column (32-row blocks).  Column 3 is
+    # retained with scale 2^-6: its values are FP8 of x / 2^-6 (1.3 -> 83.2
+    # -> E4M3 80 -> 1.25; 0.1 -> 6.4 -> 6.5 -> 0.1015625), it has FP4 codes 0
+    # and the E8M0 code of an empty block (0).  Column 0 keeps its FP4 block:
+    # amax 6 -> scale 1, 1.3 -> 1.5 (RNE).
+    x = np.zeros((32, 8), np.float32)
+    x[0, 0], x[1, 0] = 6.0, 1.3
+    x[0, 3], x[1, 3] = 1.3, -0.1
+    xb = bf(x)
+    retain = np.zeros(8, bool)
+    retain[3] = True
+    scale = np.zeros(8, np.float32)
+    scale[3] = 2.0 ** -6
+    r = oracle.fake_quant_retained(xb, "mx", retain, scale, "rne", "col")
+    y = f32(r["y"])
+    assert y[0, 3] == 1.25 and y[1, 3] == -0.1015625
+    assert y[0, 0] == 6.0 and y[1, 0] == 1.5
+    assert r["scales"][3].tolist() == [0]                    # column 3's only block: empty
+    assert r["scales"][0].tolist() == [127]
+    assert np.all(r["codes"][3] == 0)
+    assert r["clip"].sum() == 0
+
+
+def test_per_tensor_retention_leaves_the_retained_maximum_out():
+    # NVFP4 per tensor: the retained channel holds the largest value (100);
+    # the tensor scale comes from the others' maximum 2.625 = 2688 * 2^-10
+    # (block scale 448 * 2^-10 = 0.4375 for the block of 2.625: a = 6 and 1;
+    # 0.4375 sits in that block along rows at (0, 2), along columns at (1, 1))
+    x = np.zeros((16, 16), np.float32)
+    x[:, 0] = 100.0
+    x[0, 1] = 2.625
+    x[0, 2] = 0.4375
+    x[1, 1] = 0.4375
+    xb = bf(x)
+    retain = np.zeros(16, bool)
+    retain[0] = True
+    scale = np.zeros(16, np.float32)
+    scale[0] = np.float32(100.0 / 448.0)
+    for axis, at in (("row", (0, 2)), ("col", (1, 1))):
+        r = oracle.fake_quant_retained(xb, "nv_tensor", retain, scale, "rne", axis)
+        assert r["outer"].tolist() == [2.0 ** -10], axis
+        y = f32(r["y"])
+        assert y[0, 1] == 2.625 and y[at] == 0.4375, axis
+        assert y[0, 0] == 100.0, axis                         # 448 * s, s = 100/448
+
+
+def _fp8_exact_operands(M, K, N, seed):
+    """MXFP4 grid operands (every 32-block along both axes has a 6, scale 1),
+    X's retained channels holding E4M3 multiples of their scale 2^-6 that the
+    E2M1 grid does not hold (1.25, 2.5, 3.5, ...), so FP8 keeps them exactly
+    and FP4 would not."""
+    GRID = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+    rng = np.random.default_rng(seed)
+
+    def grid(R, C):
+        v = rng.choice(GRID, size=(R, C)) * rng.choice([-1.0, 1.0], size=(R, C))
+        i, j = np.indices((R, C))
+        v[(i + j) % 32 == 0] = 6.0
+        return v
+    x, w, dy = grid(M, K), grid(K, N), grid(M, N)
+    retain = np.zeros(K, bool)
+    retain[rng.choice(K, size=K // 10, replace=False)] = True
+    FP8_ONLY = np.array([1.25, 2.5, 3.5, 5.0, 0.75, 1.75])
+    x[:, retain] = rng.choice(FP8_ONLY, size=(M, int(retain.sum()))) * \
+        rng.choice([-1.0, 1.0], size=(M, int(retain.sum())))
+    scale = np.where(retain, np.float32(2.0 ** -6), np.float32(0)).astype(np.float32)
+    return x, w, dy, retain, scale
+
+
+def test_linear_with_retained_channels_exact():
+    M, K, N = 64, 160, 96
+    x, w, dy, retain, scale = _fp8_exact_operands(M, K, N, 5)
+    xb, wb, gb = bf(x), bf(w), bf(dy)
+    r = oracle.qlinear(xb, wb, "mx", "mx", retain=retain, chan_scale=scale)
+    assert np.array_equal(oracle.bf16_bits_to_f64(r["xhat"]), x)       # FP8 kept them
+    assert np.array_equal(r["y"], x @ w)
+    # without retention the same channels would be rounded to the E2M1 grid
+    plain = oracle.qlinear(xb, wb, "mx", "mx")
+    assert not np.array_equal(oracle.bf16_bits_to_f64(plain["xhat"]), x)
+    b = oracle.qlinear_bwd(xb, wb, gb, "mx", "mx", "mx", "sr", 11, retain=retain,
+                           chan_scale=scale)
+    assert np.array_equal(b["keep_x"], np.ones_like(x))
+    assert np.array_equal(b["dx"], dy @ w.T)
+    assert np.array_equal(b["dw"], x.T @ dy)                           # X_hat along M: FP8 too
+    bp = oracle.qlinear_bwd(xb, wb, gb, "mx", "mx", "mx", "sr", 11)
+    assert not np.array_equal(bp["dw"], x.T @ dy)
