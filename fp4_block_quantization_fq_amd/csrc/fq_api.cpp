@@ -125,7 +125,7 @@ fq_status device_status(hipError_t e, const char *what)
 fq_status run_quant(const Fmt &f, const fq_desc *d, const void *x, int64_t R, int64_t C,
                     void *y, void *codes, void *scales, float *outer, void *ws,
                     hipStream_t st, bool cached = false, void *keep = nullptr, int rht_n = 0,
-                    uint64_t rht_seed = 0)
+                    uint64_t rht_seed = 0, int64_t npart_given = -1)
 {
     fqimpl::QuantArgs a;
     a.fmt = f.fmt;
@@ -145,8 +145,9 @@ fq_status run_quant(const Fmt &f, const fq_desc *d, const void *x, int64_t R, in
     a.rht_n = rht_n;
     a.rht_seed = rht_seed;
     a.cached_outputs = cached;
-    uint32_t npart = 0;
-    if (f.fmt == fqimpl::FMT_NVT) {
+    // npart_given >= 0: the per-tensor partial maxima are already in ws
+    uint32_t npart = npart_given >= 0 ? (uint32_t)npart_given : 0u;
+    if (f.fmt == fqimpl::FMT_NVT && npart_given < 0) {
         hipError_t e = fqimpl::launch_absmax(x, R * C, a.partials, &npart, st);
         if (e != hipSuccess) return device_status(e, "tensor absmax launch");
     }
@@ -560,14 +561,25 @@ static fq_status qlinear_fwd_impl(const fq_desc *desc_x, const fq_desc *desc_w,
 
     void *xhat = base;
     char *what_t = base + round256((size_t)M * K * 2);
+    uint32_t *parts_w = parts + fqimpl::kAbsmaxPartials;
 
+    // both per-tensor: the two maximum passes in one launch
+    int64_t npart_x = -1, npart_w = -1;
+    if (fx.fmt == fqimpl::FMT_NVT && fw.fmt == fqimpl::FMT_NVT && !retain) {
+        uint32_t nx = 0, nw = 0;
+        hipError_t e = fqimpl::launch_absmax_pair(x_bf16, M * K, parts, &nx, w_bf16, K * N,
+                                                  parts_w, &nw, st);
+        if (e != hipSuccess) return device_status(e, "tensor absmax launch");
+        npart_x = nx;
+        npart_w = nw;
+    }
     // X_hat = FQ(X) along K (rows of X), the retained channels in FP8
     if (retain)
         FQ_TRY(run_quant_retain(fx, desc_x, desc_x->seed, x_bf16, M, K, xhat, nullptr, nullptr,
                                 nullptr, nullptr, nullptr, retain, chan_scale, parts, st, true));
     else
         FQ_TRY(run_quant(fx, desc_x, x_bf16, M, K, xhat, nullptr, nullptr, nullptr, parts, st,
-                         /*cached=*/true));
+                         /*cached=*/true, nullptr, 0, 0, npart_x));
     // W_hat^T: FQ(W) along K (columns of W), written transposed [N, K]
     {
         fqimpl::QuantArgs a;
@@ -582,10 +594,10 @@ static fq_status qlinear_fwd_impl(const fq_desc *desc_x, const fq_desc *desc_w,
         a.codes = nullptr;
         a.scales = nullptr;
         a.outer = nullptr;
-        a.partials = parts + fqimpl::kAbsmaxPartials;
+        a.partials = parts_w;
         a.cached_outputs = true;
-        uint32_t npart = 0;
-        if (fw.fmt == fqimpl::FMT_NVT) {
+        uint32_t npart = npart_w >= 0 ? (uint32_t)npart_w : 0u;
+        if (fw.fmt == fqimpl::FMT_NVT && npart_w < 0) {
             hipError_t e = fqimpl::launch_absmax(w_bf16, K * N, a.partials, &npart, st);
             if (e != hipSuccess) return device_status(e, "tensor absmax launch");
         }
@@ -647,7 +659,7 @@ static BwdLayout bwd_layout(bool rht, int64_t M, int64_t K, int64_t N)
     L.wq_n = take(kn * 2);
     L.xq_mt = take(mk * 2);
     L.dyq_mt = take(mn * 2);
-    L.parts = take(fqimpl::kAbsmaxPartials * sizeof(uint32_t));
+    L.parts = take(2 * fqimpl::kAbsmaxPartials * sizeof(uint32_t));   // X, W
     // rotated operands (random Hadamard transform), only when requested
     L.rdy_n = take(rht ? mn * 2 : 0);
     L.rw_n = take(rht ? kn * 2 : 0);
@@ -706,7 +718,8 @@ fq_status fq_hadamard(const void *x_bf16, int64_t rows, int64_t cols, int32_t ax
 static fq_status bwd_quant(const Fmt &f, const fq_desc *d, uint64_t seed, bool col,
                            const void *src, int64_t R, int64_t C, void *y, void *yt,
                            void *codes, void *scales, void *keep, uint32_t *parts,
-                           hipStream_t st, int rht_n = 0, uint64_t rht_seed = 0)
+                           hipStream_t st, int rht_n = 0, uint64_t rht_seed = 0,
+                           int64_t npart_given = -1)
 {
     fqimpl::QuantArgs a;
     a.fmt = f.fmt;
@@ -726,8 +739,9 @@ static fq_status bwd_quant(const Fmt &f, const fq_desc *d, uint64_t seed, bool c
     a.rht_seed = rht_seed;
     a.partials = parts;
     a.cached_outputs = true;
-    uint32_t npart = 0;
-    if (f.fmt == fqimpl::FMT_NVT) {
+    // npart_given >= 0: the per-tensor partial maxima are already in parts
+    uint32_t npart = npart_given >= 0 ? (uint32_t)npart_given : 0u;
+    if (f.fmt == fqimpl::FMT_NVT && npart_given < 0) {
         hipError_t e = fqimpl::launch_absmax(src, R * C, parts, &npart, st);
         if (e != hipSuccess) return device_status(e, "tensor absmax launch");
     }
@@ -792,15 +806,27 @@ static fq_status qlinear_bwd_impl(const fq_desc *desc_x, const fq_desc *desc_w,
     const uint64_t sg = desc_g->seed;
 
     // the forward's operands and their STE keep masks: X_hat [M, K], W_hat [K, N]
+    // (both per-tensor: the two maximum passes in one launch)
+    uint32_t *parts_w = parts + fqimpl::kAbsmaxPartials;
+    int64_t npart_x = -1, npart_w = -1;
+    if (fx.fmt == fqimpl::FMT_NVT && fw.fmt == fqimpl::FMT_NVT && !retain) {
+        uint32_t nx = 0, nw = 0;
+        hipError_t e = fqimpl::launch_absmax_pair(x_bf16, M * K, parts, &nx, w_bf16, K * N,
+                                                  parts_w, &nw, st);
+        if (e != hipSuccess) return device_status(e, "tensor absmax launch");
+        npart_x = nx;
+        npart_w = nw;
+    }
     if (retain)
         FQ_TRY(run_quant_retain(fx, desc_x, desc_x->seed, x_bf16, M, K, b + L.xhat, nullptr,
                                 nullptr, nullptr, nullptr, b + L.xkeep, retain, chan_scale, parts,
                                 st, true));
     else
         FQ_TRY(bwd_quant(fx, desc_x, desc_x->seed, false, x_bf16, M, K, b + L.xhat, nullptr,
-                         nullptr, nullptr, b + L.xkeep, parts, st));
+                         nullptr, nullptr, b + L.xkeep, parts, st, 0, 0, npart_x));
     FQ_TRY(bwd_quant(fw, desc_w, desc_w->seed, true, w_bf16, K, N, b + L.what, nullptr,
-                     nullptr, nullptr, b + L.wkeep, parts, st));
+                     nullptr, nullptr, b + L.wkeep, npart_w >= 0 ? parts_w : parts, st, 0, 0,
+                     npart_w));
     // the operands before quantization, rotated along each contraction axis
     const void *op_dy_n = dy_bf16, *op_w_n = b + L.what, *op_x_m = b + L.xhat, *op_dy_m = dy_bf16;
     if (rht && !rht_fused) {

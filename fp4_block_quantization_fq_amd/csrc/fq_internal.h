@@ -43,6 +43,10 @@ struct QuantArgs {
 hipError_t launch_absmax(const void *x, int64_t n_elems, uint32_t *partials,
                          uint32_t *npart_out, hipStream_t stream,
                          const void *retain = nullptr, int64_t cols = 0);
+// The partial maxima of two tensors in one launch (no retained columns).
+hipError_t launch_absmax_pair(const void *x0, int64_t n0, uint32_t *partials0, uint32_t *npart0,
+                              const void *x1, int64_t n1, uint32_t *partials1, uint32_t *npart1,
+                              hipStream_t stream);
 hipError_t launch_quant(const QuantArgs &a, uint32_t npart, hipStream_t stream);
 hipError_t launch_dequant(int fmt, int col, const void *codes, const void *scales,
                           const float *outer, int64_t R, int64_t C, void *y,

@@ -81,31 +81,47 @@ __device__ __forceinline__ uint4 ld_stream(const uint4 *p)
 // accumulator and no atomics are needed.
 // ---------------------------------------------------------------------------
 // One workgroup of kAbsmaxThreads per partial; at most kAbsmaxGrid partials,
-// so that every quantizer workgroup reduces at most 1 KB of them.
+// so that every quantizer workgroup reduces at most 1 KB of them.  A thread
+// keeps kAbsmaxUnroll 16-byte loads in flight per pass, and the workgroups of
+// a tensor are sized so that all of them make the same number of passes.
+// One launch serves up to two tensors (the QAT linear's X and W): workgroups
+// 0 .. j0.groups - 1 reduce the first, the rest the second.
 constexpr int kAbsmaxThreads = 1024;
+constexpr uint32_t kAbsmaxUnroll = 8;
 constexpr uint32_t kAbsmaxGrid = 256;
 static_assert(kAbsmaxGrid <= fqimpl::kAbsmaxPartials, "partials fit the workspace");
 
-// MASK: the columns whose bit is set in retain (bit c mod 8 of byte c / 8 of
-// a row of cpr chunks) take no part in the maximum (retained FP8 channels).
+struct AbsmaxJob {
+    const uint4 *x;
+    uint32_t nchunks;         // 16-byte chunks of x
+    uint32_t *partials;       // one word per workgroup
+    uint32_t groups;          // workgroups of this tensor
+    const uint8_t *retain;    // MASK: retained columns (bit c mod 8 of byte c / 8)
+    uint32_t cpr;             // MASK: chunks per row
+};
+
+// MASK: the columns whose bit is set in retain take no part in the maximum
+// (retained FP8 channels).
 template <bool MASK>
-__global__ __launch_bounds__(kAbsmaxThreads) void k_absmax(const uint4 *__restrict__ x,
-                                                           uint32_t nchunks,
-                                                           uint32_t *__restrict__ partials,
-                                                           const uint8_t *__restrict__ retain,
-                                                           uint32_t cpr)
+__global__ __launch_bounds__(kAbsmaxThreads) void k_absmax(AbsmaxJob j0, AbsmaxJob j1)
 {
     __shared__ uint32_t red[kAbsmaxThreads / 64];
+    const bool second = blockIdx.x >= j0.groups;
+    const AbsmaxJob j = second ? j1 : j0;
+    const uint32_t wg = second ? blockIdx.x - j0.groups : blockIdx.x;
+    constexpr uint32_t per = kAbsmaxThreads * kAbsmaxUnroll;
     uint32_t m = 0;
-    const uint32_t stride = gridDim.x * kAbsmaxThreads * 4;
-    for (uint32_t base = blockIdx.x * kAbsmaxThreads * 4; base < nchunks; base += stride) {
-        uint4 v[4];
+    for (uint32_t base = wg * per; base < j.nchunks; base += j.groups * per) {
+        // indexes past the end re-read the last chunk (the maximum is
+        // idempotent), so that no load sits behind a branch and all
+        // kAbsmaxUnroll of them are in flight together
+        uint4 v[kAbsmaxUnroll];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            uint32_t c = base + u * kAbsmaxThreads + threadIdx.x;
-            v[u] = c < nchunks ? x[c] : make_uint4(0, 0, 0, 0);
-            if (MASK && c < nchunks) {
-                const uint32_t r = retain[c % cpr];
+        for (uint32_t u = 0; u < kAbsmaxUnroll; ++u) {
+            const uint32_t c = min(base + u * kAbsmaxThreads + threadIdx.x, j.nchunks - 1);
+            v[u] = j.x[c];
+            if (MASK) {
+                const uint32_t r = j.retain[c % j.cpr];
                 v[u].x &= ~retained_halves(r, 0);
                 v[u].y &= ~retained_halves(r, 2);
                 v[u].z &= ~retained_halves(r, 4);
@@ -113,10 +129,10 @@ __global__ __launch_bounds__(kAbsmaxThreads) void k_absmax(const uint4 *__restri
             }
         }
 #pragma unroll
-        for (int u = 0; u < 4; ++u) m = max(m, absmax_bits_8(v[u]));
+        for (uint32_t u = 0; u < kAbsmaxUnroll; ++u) m = max(m, absmax_bits_8(v[u]));
     }
     m = block_reduce_max<kAbsmaxThreads>(m, red);
-    if (threadIdx.x == 0) partials[blockIdx.x] = m;
+    if (threadIdx.x == 0) j.partials[wg] = m;
 }
 
 // Block scale of this lane's 16 elements (cross-lane for MXFP4 and the
@@ -803,22 +819,51 @@ hipError_t quant_dispatch(const fqimpl::QuantArgs &a, uint32_t npart, hipStream_
 
 namespace fqimpl {
 
+namespace {
+AbsmaxJob absmax_job(const void *x, int64_t n_elems, uint32_t *partials, const void *retain,
+                     int64_t cols)
+{
+    AbsmaxJob j;
+    j.x = (const uint4 *)x;
+    j.nchunks = (uint32_t)((uint64_t)n_elems / 8);
+    j.partials = partials;
+    const uint64_t per = (uint64_t)kAbsmaxThreads * kAbsmaxUnroll;
+    const uint64_t passes = (j.nchunks + kAbsmaxGrid * per - 1) / (kAbsmaxGrid * per);
+    uint64_t g = passes ? (j.nchunks + passes * per - 1) / (passes * per) : 1;
+    j.groups = (uint32_t)(g ? g : 1);
+    j.retain = (const uint8_t *)retain;
+    j.cpr = retain ? (uint32_t)(cols / 8) : 1u;
+    return j;
+}
+}  // namespace
+
 hipError_t launch_absmax(const void *x, int64_t n_elems, uint32_t *partials,
                          uint32_t *npart_out, hipStream_t stream, const void *retain,
                          int64_t cols)
 {
-    const uint64_t nchunks = (uint64_t)n_elems / 8;
-    uint64_t g = (nchunks + kAbsmaxThreads * 4 - 1) / (kAbsmaxThreads * 4);
-    if (g > kAbsmaxGrid) g = kAbsmaxGrid;
-    if (g == 0) g = 1;
+    const AbsmaxJob j = absmax_job(x, n_elems, partials, retain, cols);
+    AbsmaxJob none = j;
+    none.groups = 0;
     if (retain)
-        hipLaunchKernelGGL(k_absmax<true>, dim3((uint32_t)g), dim3(kAbsmaxThreads), 0, stream,
-                           (const uint4 *)x, (uint32_t)nchunks, partials,
-                           (const uint8_t *)retain, (uint32_t)(cols / 8));
+        hipLaunchKernelGGL(k_absmax<true>, dim3(j.groups), dim3(kAbsmaxThreads), 0, stream, j,
+                           none);
     else
-        hipLaunchKernelGGL(k_absmax<false>, dim3((uint32_t)g), dim3(kAbsmaxThreads), 0, stream,
-                           (const uint4 *)x, (uint32_t)nchunks, partials, nullptr, 1u);
-    *npart_out = (uint32_t)g;
+        hipLaunchKernelGGL(k_absmax<false>, dim3(j.groups), dim3(kAbsmaxThreads), 0, stream, j,
+                           none);
+    *npart_out = j.groups;
+    return hipGetLastError();
+}
+
+hipError_t launch_absmax_pair(const void *x0, int64_t n0, uint32_t *partials0, uint32_t *npart0,
+                              const void *x1, int64_t n1, uint32_t *partials1, uint32_t *npart1,
+                              hipStream_t stream)
+{
+    const AbsmaxJob j0 = absmax_job(x0, n0, partials0, nullptr, 0);
+    const AbsmaxJob j1 = absmax_job(x1, n1, partials1, nullptr, 0);
+    hipLaunchKernelGGL(k_absmax<false>, dim3(j0.groups + j1.groups), dim3(kAbsmaxThreads), 0,
+                       stream, j0, j1);
+    *npart0 = j0.groups;
+    *npart1 = j1.groups;
     return hipGetLastError();
 }
 
