@@ -73,6 +73,10 @@ def lib() -> ctypes.CDLL:
                                         u16p, i64, i64, u8p, u8p, f32p, u16p, u8p,
                                         ctypes.c_int]
         L.fqo_quantize_rows.restype = ctypes.c_int
+        L.fqo_quantize_rows_at.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_uint64,
+                                           ctypes.c_uint64, u16p, i64, i64, u8p, u8p, f32p,
+                                           u16p, u8p, ctypes.c_int]
+        L.fqo_quantize_rows_at.restype = ctypes.c_int
         L.fqo_dequantize_rows.argtypes = [ctypes.c_int, u8p, u8p, f32p, i64, i64,
                                           u16p, ctypes.c_int]
         L.fqo_dequantize_rows.restype = ctypes.c_int
@@ -171,7 +175,7 @@ def r16(seed: int, n: int) -> int:
 # --------------------------------------------------------------------------
 
 def _rows_quantize(fmt: str, rounding: str, seed: int, x: np.ndarray,
-                   nthreads: int):
+                   nthreads: int, index_base: int = 0):
     R, C = x.shape
     B = BLOCK[fmt]
     codes = np.zeros((R, C // 2), np.uint8)
@@ -184,7 +188,7 @@ def _rows_quantize(fmt: str, rounding: str, seed: int, x: np.ndarray,
         outer = None
     y = np.zeros((R, C), np.uint16)
     clip = np.zeros((R, C), np.uint8)
-    rc = lib().fqo_quantize_rows(FORMATS[fmt], ROUNDINGS[rounding], seed,
+    rc = lib().fqo_quantize_rows_at(FORMATS[fmt], ROUNDINGS[rounding], seed, index_base,
                                  _ptr(x, ctypes.c_uint16), R, C,
                                  _ptr(codes, ctypes.c_uint8),
                                  _ptr(scales, ctypes.c_uint8),
@@ -197,7 +201,7 @@ def _rows_quantize(fmt: str, rounding: str, seed: int, x: np.ndarray,
 
 
 def fake_quant(x: np.ndarray, fmt: str, rounding: str = "rne", axis: str = "row",
-               seed: int = 0, nthreads: int | None = None) -> dict:
+               seed: int = 0, nthreads: int | None = None, index_base: int = 0) -> dict:
     """Quantize and dequantize a [R, C] BF16 tensor (uint16 bit patterns).
 
     axis="row": 1xB groups along each row.  codes [R, C/2], scales [R, C/B],
@@ -207,12 +211,17 @@ def fake_quant(x: np.ndarray, fmt: str, rounding: str = "rne", axis: str = "row"
     transposed layout); y [R, C] in the layout of x; the stochastic-rounding
     index of element (i, j) is j * R + i.
     Also returns clip (1 where the element was clipped), in the layout of y.
+    index_base is added to every stochastic-rounding index: for a sample of
+    whole rows (row axis) or of one whole column (column axis) cut from a
+    larger tensor, the flat index of the sample's first element in that
+    tensor (r0 * C_full, resp. c * R).  A per-tensor scale is then the
+    sample's own.
     """
     x = np.ascontiguousarray(x, dtype=np.uint16)
     assert x.ndim == 2
     n = default_threads() if nthreads is None else nthreads
     src = x if axis == "row" else np.ascontiguousarray(x.T)
-    codes, scales, outer, y, clip = _rows_quantize(fmt, rounding, seed, src, n)
+    codes, scales, outer, y, clip = _rows_quantize(fmt, rounding, seed, src, n, index_base)
     if axis == "col":
         y = np.ascontiguousarray(y.T)
         clip = np.ascontiguousarray(clip.T)

@@ -316,13 +316,16 @@ float fqo_absmax(const uint16_t *x, int64_t n)
  *   y      [R, C]     dequantized BF16
  *   clip   [R, C]     1 where the scaled magnitude exceeds 6 (the element was
  *                     clipped), else 0
- * Stochastic rounding draws fqo_r16(seed, r * C + c) for element (r, c).
+ * Stochastic rounding draws fqo_r16(seed, index_base + r * C + c) for element
+ * (r, c): index_base = 0 for a whole tensor, or the flat index of the first
+ * element when x is a run of whole rows cut from a larger tensor (a sample;
+ * the per-tensor format then takes its maximum over the sample only).
  * Returns 0, or -1 for a shape the format cannot block.
  */
-int fqo_quantize_rows(int fmt, int rounding, uint64_t seed,
-                      const uint16_t *x, int64_t R, int64_t C,
-                      uint8_t *codes, uint8_t *scales, float *outer,
-                      uint16_t *y, uint8_t *clip, int nthreads)
+int fqo_quantize_rows_at(int fmt, int rounding, uint64_t seed, uint64_t index_base,
+                         const uint16_t *x, int64_t R, int64_t C,
+                         uint8_t *codes, uint8_t *scales, float *outer,
+                         uint16_t *y, uint8_t *clip, int nthreads)
 {
     const int B = block_size_of(fmt);
     if (R <= 0 || C <= 0 || C % B != 0) return -1;
@@ -374,7 +377,7 @@ int fqo_quantize_rows(int fmt, int rounding, uint64_t seed,
                 float a = scaled_magnitude(xv, s_eff);
                 int m;
                 if (rounding == FQO_SR)
-                    m = fqo_e2m1_sr(a, fqo_r16(seed, (uint64_t)(r * C + c)));
+                    m = fqo_e2m1_sr(a, fqo_r16(seed, index_base + (uint64_t)(r * C + c)));
                 else
                     m = fqo_e2m1_rne(a);
                 int code = (signbit(xv) ? 8 : 0) | m;
@@ -389,6 +392,15 @@ int fqo_quantize_rows(int fmt, int rounding, uint64_t seed,
         }
     }
     return 0;
+}
+
+int fqo_quantize_rows(int fmt, int rounding, uint64_t seed,
+                      const uint16_t *x, int64_t R, int64_t C,
+                      uint8_t *codes, uint8_t *scales, float *outer,
+                      uint16_t *y, uint8_t *clip, int nthreads)
+{
+    return fqo_quantize_rows_at(fmt, rounding, seed, 0, x, R, C, codes, scales, outer, y, clip,
+                                nthreads);
 }
 
 /* ------------------------------------------------------------------ */
