@@ -106,3 +106,23 @@ def uniform_bits_bf16(shape, seed: int) -> np.ndarray:
     u = rng.integers(0, 1 << 16, size=shape, dtype=np.uint32).astype(np.uint16)
     finite = (u & 0x7F80) != 0x7F80
     return np.where(finite, u, u & 0x807F).astype(np.uint16)
+
+
+def device_normal_bf16(rows: int, cols: int, sigma: float, seed: int, device,
+                       block_elems: int = 1 << 28):
+    """A [rows, cols] BF16 tensor on `device`, N(0, sigma^2) drawn by torch's
+    seeded device generator in blocks of whole rows and rounded by torch's
+    BF16 cast: for tensors too large to draw on the host (beyond 2^32
+    elements).  Whoever uses it copies sampled rows or columns to the host
+    for the oracle."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    x = torch.empty((rows, cols), dtype=torch.bfloat16, device=device)
+    step = max(1, block_elems // cols)
+    for r0 in range(0, rows, step):
+        r1 = min(rows, r0 + step)
+        blk = torch.randn((r1 - r0, cols), generator=g, device=device, dtype=torch.float32)
+        x[r0:r1] = (blk * sigma).to(torch.bfloat16)
+        del blk
+    return x
