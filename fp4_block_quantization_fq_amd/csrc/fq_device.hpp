@@ -325,20 +325,42 @@ __device__ __forceinline__ void fwht16(float (&v)[16])
             }
 }
 
+// The value of lane ^ D (D = 1, 2, 4) by DPP inside the lane's 16-lane row,
+// with no LDS traffic: quad permutes for 1 and 2; for 4 a rotation of the row
+// by 12 (lane + 4, lanes with bit 2 clear) or by 4 (lane - 4, bit 2 set).
+template <int D>
+__device__ __forceinline__ float lane_xor(float v, bool bit2)
+{
+    const int iv = __float_as_int(v);
+    if (D == 1) return __int_as_float(__builtin_amdgcn_update_dpp(0, iv, 0xB1, 0xF, 0xF, false));
+    if (D == 2) return __int_as_float(__builtin_amdgcn_update_dpp(0, iv, 0x4E, 0xF, 0xF, false));
+    const int up = __builtin_amdgcn_update_dpp(0, iv, 0x12C, 0xF, 0xF, false);    // row_ror:12
+    const int dn = __builtin_amdgcn_update_dpp(0, iv, 0x124, 0xF, 0xF, false);    // row_ror:4
+    return __int_as_float(bit2 ? dn : up);
+}
+
+template <int D>
+__device__ __forceinline__ void fwht_lane_stage(float (&v)[16], uint32_t lane_in_block)
+{
+    // lower lane of a pair: a + b; upper: b - a = b + (-a), with b the
+    // partner's value (the same sums, exactly rounded, in either order)
+    const uint32_t neg = (lane_in_block & D) ? 0x80000000u : 0u;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const float p = lane_xor<D>(v[i], (lane_in_block & 4) != 0);
+        v[i] = p + as_f(as_u(v[i]) ^ neg);
+    }
+}
+
 // Cross-lane stages for n = 128: lane offsets 1, 2, 4 (element half-widths
 // 16, 32, 64).  The lower lane of a pair keeps a + b, the upper a - b, with a
-// the lower lane's value.
+// the lower lane's value.  The 8 lanes of a 128-block are 8 aligned lanes of
+// the wave (lane_in_block = lane mod 8).
 __device__ __forceinline__ void fwht_lanes(float (&v)[16], uint32_t lane_in_block)
 {
-#pragma unroll
-    for (int d = 1; d < 8; d *= 2) {
-        const bool upper = (lane_in_block & d) != 0;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const float p = __shfl_xor(v[i], d);
-            v[i] = upper ? (p - v[i]) : (v[i] + p);
-        }
-    }
+    fwht_lane_stage<1>(v, lane_in_block);
+    fwht_lane_stage<2>(v, lane_in_block);
+    fwht_lane_stage<4>(v, lane_in_block);
 }
 
 __device__ __forceinline__ float flip(float e, uint32_t bits, int i)
