@@ -409,8 +409,7 @@ __global__ __launch_bounds__(kQcThreads) void k_quant_col(
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 bool c0, c1;
-                yq[i] = bf16_pair_rne(fp8_fake(as_f(lo_bits(xr[i])), chs, &c0),
-                                      fp8_fake(as_f(hi_bits(xr[i])), chs, &c1));
+                yq[i] = fp8_fake_pair(xr[i], chs, chs, &c0, &c1);
                 clipped |= (c0 ? 1u : 0u) << (2 * i) | (c1 ? 1u : 0u) << (2 * i + 1);
             }
         }

@@ -363,8 +363,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_row_retain(
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 bool c0, c1;
-                const uint32_t f = bf16_pair_rne(fp8_fake(bf16_lo(xp[i]), ch[2 * i], &c0),
-                                                 fp8_fake(bf16_hi(xp[i]), ch[2 * i + 1], &c1));
+                const uint32_t f = fp8_fake_pair(xp[i], ch[2 * i], ch[2 * i + 1], &c0, &c1);
                 yp[i] = (f & sel[i]) | (yp[i] & ~sel[i]);
                 kr |= (c0 ? 0u : 1u) << (2 * i) | (c1 ? 0u : 1u) << (2 * i + 1);
             }

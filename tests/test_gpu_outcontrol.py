@@ -131,6 +131,36 @@ def test_fake_quant_retain_ragged_rows():
         _retain_case(x, fmt, "sr", 103, axis="col")
 
 
+@pytest.mark.parametrize("fmt,axis", [("mx", "row"), ("nv_tensor", "row"), ("nv_128", "col"),
+                                      ("mx", "col")])
+def test_fake_quant_retain_every_bf16_value(fmt, axis):
+    """Every finite BF16 value through the FP8 channel path: all 64 columns
+    retained, each column holding the values whose pattern is its index mod
+    64 (every exponent), under 64 channel scales from 2^-40 to 2^30 (plus 1,
+    1/3 and 0), rotated over three calls so that every value meets three
+    scales; bit for bit against the oracle (y, and the empty FP4 part)."""
+    pats = np.arange(65536, dtype=np.uint32)
+    finite = pats[(pats & 0x7F80) != 0x7F80].astype(np.uint16)
+    x = np.zeros(1024 * 64, np.uint16)
+    x[:finite.size] = finite
+    x = x.reshape(1024, 64)
+    base = (2.0 ** np.linspace(-40, 30, 64)).astype(np.float32) * np.float32(1.37)
+    base[0], base[1], base[2] = 1.0, np.float32(1.0 / 3.0), 0.0
+    ret = np.ones(64, np.uint8)
+    retain = torch.from_numpy(np.packbits(ret, bitorder="little")).to(DEV)
+    d = make_desc(fmt, "rne", axis)
+    tx = to_dev(x)
+    for shift in (0, 21, 42):
+        sc = np.roll(base, shift).astype(np.float32)
+        ref = oracle.fake_quant_retained(x, fmt, ret, sc, "rne", axis, 0)
+        out = fq.alloc_outputs(d, 1024, 64, tx.device)
+        y = fq.fq_fake_quant_retain(d, tx, retain, torch.from_numpy(sc).to(DEV), out=out)
+        torch.cuda.synchronize()
+        got = {"y": to_bits(y), "codes": to_np(out.codes), "scales": to_np(out.scales),
+               "outer": None if out.outer is None else to_np(out.outer)}
+        assert_same(got, ref, tag=f"every BF16 value, {fmt}/{axis}, scale shift {shift}")
+
+
 def test_fake_quant_retain_full_size():
     x = wl.nv_activation(16384, 4096, seed=3)
     _retain_case(x, "nv_128", "sr", 410, seed=1234)
