@@ -77,6 +77,18 @@ def op_bytes(op: str, n: int) -> int:
 
 OPS = ["mx_rne_row", "nvt_rne_row", "nv128_rne_row", "nv128_sr_row", "nv128_sr_col",
        "mx_sr_col", "ste_nv128", "dequant_nv128"]
+# the kernels each op launches (names as the rocprofv3 summaries list them;
+# template arguments: format, rounding, row mapping or non-temporal stores, ...)
+OP_KERNELS = {
+    "mx_rne_row": ["k_quant_row<0, 0, 1, true, 0>"],
+    "nvt_rne_row": ["k_absmax<false>", "k_quant_row<1, 0, 2, true, 0>"],
+    "nv128_rne_row": ["k_quant_row<2, 0, 1, true, 0>"],
+    "nv128_sr_row": ["k_quant_row<2, 1, 0, true, 0>"],
+    "nv128_sr_col": ["k_quant_col<2, 1, true, 0, false>"],
+    "mx_sr_col": ["k_quant_col<0, 1, true, 0, false>"],
+    "ste_nv128": ["k_ste_row<2>"],
+    "dequant_nv128": ["k_dequant_row<2>"],
+}
 
 
 def kernel_source_hash() -> str:
@@ -424,13 +436,18 @@ def main():
                        "GBps": round(by / (avg * 1e-3) / 1e9, 1),
                        "frac_hbm": round(by / (avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
-    # dominant single-kernel op: the largest share of the step time
+    # dominant single-kernel op: the largest share of the step time (the
+    # per-tensor op is two kernels, so it is reported beside it instead)
     single = [o for o in ops if o != "nvt_rne_row"]
     dom = max(single or ops, key=lambda o: kernels[o]["ms"])
     achieved = kernels[dom]["GBps"]
-    roofline = {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS,
+    roofline = {"bound": "hbm", "kernel": dom, "kernels": OP_KERNELS.get(dom),
+                "achieved": achieved, "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": load_traffic(dom)}
+    low = min(ops, key=lambda o: kernels[o]["frac_hbm"])
+    roofline["lowest_op"] = {"op": low, "frac": kernels[low]["frac_hbm"],
+                             "kernels": OP_KERNELS.get(low), "traffic": load_traffic(low)}
 
     # ---------------- copy yardstick (achievable bandwidth) ----------------
     # torch's device copy of one 16384x4096 BF16 tensor: 2 B read + 2 B written
