@@ -23,7 +23,9 @@ streams its operands from HBM, not from the 256 MB Infinity Cache.  The step
 is captured once per starting set as a HIP graph and the graphs are replayed
 (`ms_per_step`); the same ops launched one by one with events around each
 (`ms_per_step_eager`) give the per-kernel times under "kernels" and the
-roofline figures.
+roofline figures: each op's rate as a fraction of the 8 TB/s HBM peak
+(`frac_hbm`, the target) and of the device copy measured in the same run
+(`frac_copy`, context).
 
 The QAT linear forward (X 8192x2880 @ W 2880x5760, both NVFP4 RNE) and its
 backward (dY 8192x5760, gradient operands NVFP4 double block with stochastic
@@ -466,6 +468,9 @@ def main():
     copy_ms = c0.elapsed_time(c1) / 10
     copy = {"op": "torch copy_ of 16384x4096 bf16", "bytes": 4 * n, "ms": round(copy_ms, 5),
             "GBps": round(4 * n / (copy_ms * 1e-3) / 1e9, 1)}
+    # second fraction, as context: each op's rate against the measured copy
+    for op in ops:
+        kernels[op]["frac_copy"] = round(kernels[op]["GBps"] / copy["GBps"], 4)
 
     # ---------------- the configurations at their own shapes ----------------
     per_config = None
