@@ -434,7 +434,9 @@ def main():
         avg = float(np.mean(times))
         by = op_bytes(op, n)
         step_bytes += by
-        kernels[op] = {"ms": round(avg, 5), "bytes": by,
+        # mean (what a profiler's per-kernel average compares with) and median
+        kernels[op] = {"ms": round(avg, 5), "ms_median": round(float(np.median(times)), 5),
+                       "bytes": by,
                        "GBps": round(by / (avg * 1e-3) / 1e9, 1),
                        "frac_hbm": round(by / (avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
