@@ -35,6 +35,9 @@ fq_status ok()
 }
 
 constexpr int64_t kMaxElems = int64_t(1) << 34;
+// every dimension fits the kernels' 32-bit row/column arguments and the
+// products' int tile arithmetic
+constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
 
 struct Fmt {
     int fmt;   // fqimpl::FMT_*
@@ -73,8 +76,8 @@ fq_status check_shape(const Fmt &f, int axis, int64_t R, int64_t C)
 {
     if (R < 1 || C < 1) return fail(FQ_ERR_SHAPE, "rows=%lld cols=%lld must be >= 1",
                                     (long long)R, (long long)C);
-    if (R > kMaxElems || C > kMaxElems || R * C > kMaxElems)
-        return fail(FQ_ERR_SHAPE, "rows*cols=%lld*%lld exceeds 2^34 elements", (long long)R,
+    if (R > kMaxDim || C > kMaxDim || R * C > kMaxElems)
+        return fail(FQ_ERR_SHAPE, "rows=%lld cols=%lld: each must be below 2^31 and rows*cols at most 2^34", (long long)R,
                     (long long)C);
     const int64_t q = (axis == FQ_AXIS_ROW) ? C : R;    // quantized axis length
     const char *qn = (axis == FQ_AXIS_ROW) ? "cols" : "rows";
@@ -371,8 +374,8 @@ fq_status fq_ste_backward_mask(const void *keep, const void *dy_bf16, int64_t ro
     if (rows < 1 || cols < 8 || cols % 8 != 0)
         return fail(FQ_ERR_SHAPE, "rows=%lld must be >= 1 and cols=%lld a positive multiple of 8",
                     (long long)rows, (long long)cols);
-    if (rows > kMaxElems || cols > kMaxElems || rows * cols > kMaxElems)
-        return fail(FQ_ERR_SHAPE, "rows*cols=%lld*%lld exceeds 2^34 elements", (long long)rows,
+    if (rows > kMaxDim || cols > kMaxDim || rows * cols > kMaxElems)
+        return fail(FQ_ERR_SHAPE, "rows=%lld cols=%lld: each must be below 2^31 and rows*cols at most 2^34", (long long)rows,
                     (long long)cols);
     FQ_TRY(check_ptr(keep, "keep", true));
     FQ_TRY(check_ptr(dy_bf16, "dy", true));
@@ -425,7 +428,8 @@ size_t fq_qlinear_workspace_size(const fq_desc *desc_x, const fq_desc *desc_w, i
 {
     (void)desc_x;
     (void)desc_w;
-    if (M < 1 || K < 1 || N < 1) return 0;
+    if (M < 1 || K < 1 || N < 1 || M > kMaxDim || K > kMaxDim || N > kMaxDim) return 0;
+    if (M * K > kMaxElems || K * N > kMaxElems) return 0;
     return round256((size_t)M * K * 2) + round256((size_t)N * K * 2) +
            2 * fqimpl::kAbsmaxPartials * sizeof(uint32_t);
 }
@@ -678,7 +682,7 @@ size_t fq_qlinear_bwd_workspace_size(const fq_desc *desc_x, const fq_desc *desc_
         check_desc(desc_g, &fg, "desc_g") != FQ_OK)
         return 0;
     if (rht_block != 0 && rht_block != 16 && rht_block != 128) return 0;
-    if (M < 1 || K < 1 || N < 1 || M > kMaxElems || K > kMaxElems || N > kMaxElems) return 0;
+    if (M < 1 || K < 1 || N < 1 || M > kMaxDim || K > kMaxDim || N > kMaxDim) return 0;
     // rotated operand buffers only where the rotation cannot be fused into
     // the quantizer (per-tensor gradient format: its maximum needs a pass)
     return bwd_layout(rht_block != 0 && fg.fmt == fqimpl::FMT_NVT, M, K, N).total;
@@ -692,8 +696,8 @@ fq_status fq_hadamard(const void *x_bf16, int64_t rows, int64_t cols, int32_t ax
     if (block != 16 && block != 128) return fail(FQ_ERR_DESC, "block=%d is not 16 or 128", block);
     if (rows < 1 || cols < 1) return fail(FQ_ERR_SHAPE, "rows=%lld cols=%lld must be >= 1",
                                           (long long)rows, (long long)cols);
-    if (rows > kMaxElems || cols > kMaxElems || rows * cols > kMaxElems)
-        return fail(FQ_ERR_SHAPE, "rows*cols exceeds 2^34 elements");
+    if (rows > kMaxDim || cols > kMaxDim || rows * cols > kMaxElems)
+        return fail(FQ_ERR_SHAPE, "rows, cols must be below 2^31 and rows*cols at most 2^34");
     const int64_t q = axis == FQ_AXIS_ROW ? cols : rows;
     if (q % block != 0)
         return fail(FQ_ERR_SHAPE, "%s=%lld must be a multiple of the block %d",
@@ -951,7 +955,7 @@ fq_status fq_osci_reset(const fq_desc *desc, float *w, const void *q_bf16, const
 {
     if (target != FQ_OSCI_BIN_CENTRE && target != FQ_OSCI_GRID_VALUE)
         return fail(FQ_ERR_DESC, "target=%d is not FQ_OSCI_BIN_CENTRE/GRID_VALUE", target);
-    if (rows < 1 || cols < 1 || rows > kMaxElems || cols > kMaxElems ||
+    if (rows < 1 || cols < 1 || rows > kMaxDim || cols > kMaxDim ||
         rows * cols > kMaxElems)
         return fail(FQ_ERR_SHAPE, "rows=%lld cols=%lld out of range", (long long)rows,
                     (long long)cols);
@@ -999,8 +1003,8 @@ fq_status fq_channel_absmax(const void *x_bf16, int64_t rows, int64_t cols, uint
     if (rows < 1 || cols < 8 || cols % 8 != 0)
         return fail(FQ_ERR_SHAPE, "rows=%lld must be >= 1 and cols=%lld a positive multiple of 8",
                     (long long)rows, (long long)cols);
-    if (rows > kMaxElems || cols > kMaxElems || rows * cols > kMaxElems)
-        return fail(FQ_ERR_SHAPE, "rows*cols exceeds 2^34 elements");
+    if (rows > kMaxDim || cols > kMaxDim || rows * cols > kMaxElems)
+        return fail(FQ_ERR_SHAPE, "rows, cols must be below 2^31 and rows*cols at most 2^34");
     FQ_TRY(check_ptr(x_bf16, "x", true));
     FQ_TRY(check_ptr(amax, "amax", true, 4));
     return device_status(fqimpl::launch_channel_absmax(x_bf16, rows, cols, amax,

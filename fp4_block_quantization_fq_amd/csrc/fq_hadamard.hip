@@ -52,7 +52,8 @@ __global__ __launch_bounds__(kThreads) void k_hadamard_row(const uint4 *__restri
     for (uint32_t u = blockIdx.x * kThreads + threadIdx.x; u < nseg; u += gridDim.x * kThreads) {
         const uint4 a = x[2 * u], b = x[2 * u + 1];
         const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-        const uint64_t col0 = ((uint64_t)u * 16) % C;
+        // position along the row (C / 16 < 2^30, so 32-bit arithmetic)
+        const uint64_t col0 = (uint64_t)(u % (C >> 4)) * 16;
         const uint32_t bits = sign_bits16(col0, seed_lo, seed_hi);
         float v[16];
 #pragma unroll

@@ -74,7 +74,7 @@
  * A call that returns an error other than FQ_ERR_DEVICE has enqueued nothing
  * and written nothing.
  *
- * Limits: rows, cols >= 1 and rows * cols <= 2^34 elements.
+ * Limits: 1 <= rows, cols < 2^31 and rows * cols <= 2^34 elements.
  */
 #ifndef FQ_H
 #define FQ_H
@@ -229,7 +229,8 @@ fq_status fq_ste_backward_mask(const void *keep, const void *dy_bf16, int64_t ro
  * descriptors are MXFP4, the operands stay encoded instead: X's codes [M, K/2] at 0, X's E8M0 scales [M, K/32] at
  * c1 = round_up(M * K / 2, 256), W's codes in the transposed layout [N, K/2]
  * at c2 = c1 + round_up(M * K / 32, 256), W's scales [N, K/32] at
- * c2 + round_up(N * K / 2, 256) (same total size). */
+ * c2 + round_up(N * K / 2, 256) (same total size).  0 for dimensions outside
+ * the limits of fq_qlinear_fwd. */
 size_t fq_qlinear_workspace_size(const fq_desc *desc_x, const fq_desc *desc_w,
                                  int64_t M, int64_t K, int64_t N);
 
@@ -241,7 +242,8 @@ size_t fq_qlinear_workspace_size(const fq_desc *desc_x, const fq_desc *desc_w,
  * matrix-core kernels step through K 64 elements at a time and have no
  * partial step; this also covers both block sizes), and of 128 for
  * FQ_OUTER_BLOCK128; N a multiple of 8 (W is quantized along its columns,
- * whose kernels move 8 columns at a time); M * K, K * N and M * N <= 2^34.
+ * whose kernels move 8 columns at a time); M, K, N < 2^31 and M * K, K * N
+ * and M * N <= 2^34.
  * Otherwise FQ_ERR_SHAPE.
  * Source: gpt-oss QAT tutorial, "NVFP4: The Next Generation"
  * (weight-activation quantization of the MLP); TetraJet-v2 sec. 2 (NVFP4

@@ -100,6 +100,25 @@ def test_quantize_validation(L):
     assert "reserved" in msg
 
 
+def test_dimension_limits(L):
+    """Each dimension below 2^31 (the kernels take 32-bit rows and columns and
+    the products int tile indexes), and no overflow of rows * cols for huge
+    dimensions whose product would wrap."""
+    mx = fq.fq_desc_mxfp4()
+    big = 1 << 31                                  # rows * cols = 2^31 <= 2^34
+    assert call_quant(L, mx, rows=1, cols=big) == fq.FQ_ERR_SHAPE
+    assert call_quant(L, fq.fq_desc_mxfp4(axis=fq.FQ_AXIS_COL), rows=big, cols=8) == fq.FQ_ERR_SHAPE
+    assert call_quant(L, mx, rows=1 << 34, cols=1 << 34) == fq.FQ_ERR_SHAPE   # product wraps int64
+    assert L.fq_hadamard(fake(), 1, big, fq.FQ_AXIS_ROW, 128, 0, fake(0x20000), None) == fq.FQ_ERR_SHAPE
+    assert "2^31" in L.fq_last_error().decode()
+    assert L.fq_ste_backward_mask(fake(), fake(), 1, big, fake(), None) == fq.FQ_ERR_SHAPE
+    assert L.fq_channel_absmax(fake(), 1, big, fake(), None) == fq.FQ_ERR_SHAPE
+    nv, col = fq.fq_desc_nvfp4(), fq.fq_desc_nvfp4(axis=fq.FQ_AXIS_COL)
+    assert L.fq_qlinear_fwd(ctypes.byref(nv), ctypes.byref(col), fake(), fake(), 1, big, 8,
+                            fake(), fake(), 1 << 40, None) == fq.FQ_ERR_SHAPE
+    assert L.fq_qlinear_workspace_size(ctypes.byref(nv), ctypes.byref(col), 1, big, 8) == 0
+
+
 def test_other_entry_points_validate(L):
     mx = fq.fq_desc_mxfp4()
     nv = fq.fq_desc_nvfp4()
