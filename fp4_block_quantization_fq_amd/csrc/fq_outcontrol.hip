@@ -281,6 +281,14 @@ __global__ __launch_bounds__(kThreads) void k_select_channels(const uint32_t *__
 // rows of its group.
 constexpr uint32_t kRetainRows = 8;
 
+typedef uint32_t u32v4 __attribute__((ext_vector_type(4)));
+// non-temporal load of an input read exactly once
+__device__ __forceinline__ uint4 ld_stream(const uint4 *p)
+{
+    const u32v4 v = __builtin_nontemporal_load(reinterpret_cast<const u32v4 *>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // The per-tensor format reduces the partial maxima of the masked maximum pass
 // (retained channels left out) at the start; keep, if given, receives the STE
 // keep bits of each chunk (the FP8 test a <= 448 for retained elements).
@@ -329,12 +337,20 @@ __global__ __launch_bounds__(kThreads) void k_quant_row_retain(
         sel[i] = (((rbits >> (2 * i)) & 1u) ? 0xFFFFu : 0u) |
                  (((rbits >> (2 * i + 1)) & 1u) ? 0xFFFF0000u : 0u);
 
+    // every row's load first, so that all of them are in flight together
+    // (streaming: x is read once; rows past the end re-read the last row and
+    // are not encoded): 89 -> 79 us for SR, 71 -> 70 us for RNE on 16384x4096
+    uint4 xv[kRetainRows];
+#pragma unroll
+    for (uint32_t r = 0; r < kRetainRows; ++r)
+        xv[r] = ld_stream(&x[(size_t)min(group * kRetainRows + r, R - 1) * cpr + j]);
     // every lane of a workgroup has the same row group: the exit is uniform
+#pragma unroll
     for (uint32_t r = 0; r < kRetainRows; ++r) {
         const uint32_t row = group * kRetainRows + r;
         if (row >= R) break;
         const size_t c = (size_t)row * cpr + j;
-        const uint4 v = x[c];
+        const uint4 v = xv[r];
         const uint32_t xp[4] = {v.x, v.y, v.z, v.w};
         uint32_t mp[4];
 #pragma unroll
@@ -375,7 +391,6 @@ __global__ __launch_bounds__(kThreads) void k_quant_row_retain(
             else codes[c] = cw[0];
         }
         if (y) {
-            typedef uint32_t u32v4 __attribute__((ext_vector_type(4)));
             const u32v4 o = {yp[0], yp[1], yp[2], yp[3]};
             if (NT) __builtin_nontemporal_store(o, reinterpret_cast<u32v4 *>(&y[c]));
             else *reinterpret_cast<u32v4 *>(&y[c]) = o;
